@@ -1,0 +1,263 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Closed forms, invariants, special cases that reduce to a library routine,
+and a float64 brute-force (non-cached, causal-mask) forward of whole tiny
+decoders.  All CPU; none of these touches the GPU path.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pyoracle as po
+from persistent_decode_megakernel_02_amd import synth
+from persistent_decode_megakernel_02_amd.configs import TINY, ModelShape
+from tests.refmodel import bf16_bits_to_f64, forward_logits
+
+U = 2.0 ** -24
+
+
+def bits(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- bf16
+def test_bf16_round_to_nearest_even_closed_forms():
+    assert po.f32_to_bf16(1.0) == 0x3F80
+    assert po.f32_to_bf16(1.0 + 2 ** -8) == 0x3F80          # tie -> even (down)
+    assert po.f32_to_bf16(1.0 + 3 * 2 ** -8) == 0x3F82      # tie -> even (up)
+    assert po.f32_to_bf16(1.0 + 2 ** -8 + 2 ** -20) == 0x3F81
+    assert po.f32_to_bf16(-2.0) == 0xC000
+    assert po.bf16_to_f32(0x3FC0) == 1.5
+
+
+def test_bf16_matches_torch_cast():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ours = np.array([po.f32_to_bf16(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(ours, bits(x))
+
+
+# ---------------------------------------------------------------- matvec
+@pytest.mark.parametrize("rows,cols", [(7, 256), (37, 688), (64, 1000)])
+def test_matvec_brute_force_within_higham_bound(rows, cols):
+    rng = np.random.default_rng(rows * cols)
+    W16 = bits(rng.standard_normal((rows, cols)) * 0.02)
+    x = rng.standard_normal(cols).astype(np.float32)
+    y = po.matvec(W16, x)
+    W = bf16_bits_to_f64(W16)
+    exact = W @ x.astype(np.float64)
+    bound = (cols + 1) * U / (1 - (cols + 1) * U) * (np.abs(W) @ np.abs(x.astype(np.float64)))
+    assert np.all(np.abs(y - exact) <= bound * 1.0001)
+    # row r of the output depends on row r of W only (no transposition)
+    W16b = W16.copy()
+    W16b[3] = bits(np.zeros(cols))
+    y2 = po.matvec(W16b, x)
+    assert y2[3] == 0.0 and np.array_equal(np.delete(y2, 3), np.delete(y, 3))
+
+
+def test_matvec_threads_bit_identical():
+    rng = np.random.default_rng(5)
+    W16 = bits(rng.standard_normal((300, 512)) * 0.02)
+    x = rng.standard_normal(512).astype(np.float32)
+    assert np.array_equal(po.matvec(W16, x, 1), po.matvec(W16, x, 4))
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_constant_vector_is_gamma():
+    n, eps = 256, 1e-5
+    ones = bits(np.ones(n))
+    y = po.rmsnorm(np.ones(n, np.float32), ones, eps)
+    assert np.allclose(y, 1.0 / math.sqrt(1.0 + eps), rtol=0, atol=2e-7)
+    assert np.all(np.abs(y - 1.0) <= 5.1e-6)
+    c = 3.0
+    y = po.rmsnorm(np.full(n, c, np.float32), ones, eps)
+    assert np.allclose(y, c / math.sqrt(c * c + eps), rtol=1e-6)
+
+
+def test_rmsnorm_random_gamma_against_float64():
+    rng = np.random.default_rng(2)
+    n, eps = 4096, 1e-5
+    x = rng.standard_normal(n).astype(np.float32)
+    g16 = bits(rng.uniform(0.5, 1.5, n))
+    y = po.rmsnorm(x, g16, eps)
+    xd = x.astype(np.float64)
+    ref = xd / np.sqrt(np.mean(xd * xd) + eps) * bf16_bits_to_f64(g16)
+    assert np.allclose(y, ref, rtol=2e-6, atol=1e-7)
+    # scale invariance (|alpha x| >> eps)
+    y2 = po.rmsnorm((x * 8.0).astype(np.float32), g16, eps)
+    assert np.allclose(y, y2, rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_identity_at_position_zero():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(128).astype(np.float32)
+    assert np.array_equal(po.rope(x, 0, 500000.0), x)
+
+
+def test_rope_pairing_and_frequency_closed_form():
+    # d=4, theta=100: pair 1 is (1, 3) with frequency 100^(-1/2) = 0.1; at position 10 the angle is 1 rad
+    y = po.rope(np.array([0, 1, 0, 0], np.float32), 10, 100.0)
+    assert np.allclose(y, [0, math.cos(1.0), 0, math.sin(1.0)], atol=1e-7)
+    # pair 0 is (0, 2) with frequency 1; at position 1 the angle is 1 rad
+    y = po.rope(np.array([1, 0, 0, 0], np.float32), 1, 100.0)
+    assert np.allclose(y, [math.cos(1.0), 0, math.sin(1.0), 0], atol=1e-7)
+    y = po.rope(np.array([0, 0, 1, 0], np.float32), 1, 100.0)
+    assert np.allclose(y, [-math.sin(1.0), 0, math.cos(1.0), 0], atol=1e-7)
+
+
+def test_rope_preserves_pair_norms_and_relative_positions():
+    rng = np.random.default_rng(4)
+    d, theta = 128, 500000.0
+    q = rng.standard_normal(d).astype(np.float32)
+    k = rng.standard_normal(d).astype(np.float32)
+    for p in (1, 17, 4095):
+        r = po.rope(q, p, theta)
+        half = d // 2
+        assert np.allclose(r[:half] ** 2 + r[half:] ** 2, q[:half] ** 2 + q[half:] ** 2, rtol=1e-5)
+    a = float(np.dot(po.rope(q, 100, theta).astype(np.float64), po.rope(k, 37, theta)))
+    b = float(np.dot(po.rope(q, 1100, theta).astype(np.float64), po.rope(k, 1037, theta)))
+    assert abs(a - b) <= 2e-4 * (np.abs(q) @ np.abs(k))
+
+
+# ---------------------------------------------------------------- attention
+def test_attention_single_key_returns_its_value():
+    rng = np.random.default_rng(6)
+    d = 64
+    K = bits(rng.standard_normal((1, d)))
+    V = bits(rng.standard_normal((1, d)))
+    o = po.attend(rng.standard_normal(d).astype(np.float32), K, V)
+    assert np.array_equal(o, bf16_bits_to_f64(V[0]).astype(np.float32))
+
+
+def test_attention_weights_are_softmax_of_scaled_scores_and_sum_to_one():
+    rng = np.random.default_rng(7)
+    n, d = 40, 64
+    K16 = bits(rng.standard_normal((n, d)))
+    V16 = bits(np.eye(n, d))        # one-hot values expose the softmax weights
+    q = (rng.standard_normal(d) * 0.5).astype(np.float32)
+    w = po.attend(q, K16, V16)[:n]
+    assert abs(float(np.sum(w.astype(np.float64))) - 1.0) < 1e-5
+    s = bf16_bits_to_f64(K16) @ q.astype(np.float64) / math.sqrt(d)
+    ref = torch.softmax(torch.from_numpy(s), dim=0).numpy()
+    assert np.allclose(w, ref, rtol=1e-5, atol=1e-7)
+
+
+def test_attention_zero_query_is_mean_of_values():
+    rng = np.random.default_rng(8)
+    n, d = 33, 128
+    K16 = bits(rng.standard_normal((n, d)))
+    V16 = bits(rng.standard_normal((n, d)))
+    o = po.attend(np.zeros(d, np.float32), K16, V16)
+    assert np.allclose(o, bf16_bits_to_f64(V16).mean(axis=0), rtol=1e-5, atol=1e-6)
+
+
+def test_attention_shift_invariance():
+    rng = np.random.default_rng(9)
+    n, d = 20, 64
+    K16 = bits(rng.standard_normal((n, d)))
+    V16 = bits(rng.standard_normal((n, d)))
+    q = rng.standard_normal(d).astype(np.float32)
+    # adding the same key component to every key shifts every score equally
+    K2 = bits(bf16_bits_to_f64(K16) + 0.0)  # identical
+    assert np.array_equal(po.attend(q, K16, V16), po.attend(q, K2, V16))
+
+
+# ---------------------------------------------------------------- SiLU / argmax
+def test_silu_closed_forms():
+    assert po.silu(0.0) == 0.0
+    assert abs(po.silu(30.0) - 30.0) < 1e-6
+    assert abs(po.silu(-30.0)) < 1e-9
+    for z in np.linspace(-8, 8, 33):
+        assert abs(po.silu(float(z)) - z / (1 + math.exp(-z))) <= 1e-6 * max(1.0, abs(z))
+
+
+def test_argmax_lowest_index_on_ties():
+    assert po.argmax(np.array([1, 3, 2, 3], np.float32)) == 1
+    assert po.argmax(np.array([-5, -5], np.float32)) == 0
+    assert po.argmax(np.array([0, 0, 7], np.float32)) == 2
+
+
+# ---------------------------------------------------------------- whole decoder
+def _weights(shape, seed, gamma_random=True):
+    ws = synth.make_weights(shape, seed=seed, device="cpu")
+    rng = np.random.default_rng(seed + 100)
+    out16, out64 = [], {}
+    for name, t in ws:
+        a = synth.bf16_bits(t)
+        if name.endswith("norm") and gamma_random:
+            a = bits(rng.uniform(0.6, 1.4, a.shape))   # non-unit gammas so a dropped gamma shows
+        out16.append(a)
+        out64[name] = bf16_bits_to_f64(a)
+    return out16, out64
+
+
+SHAPES = {
+    "tiny_gqa": TINY,
+    "tiny_mha_qknorm": ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=4, head_dim=64, ffn=688,
+                                  vocab=512, qk_norm=True),
+    "tiny_g4": ModelShape(n_layers=1, hidden=128, n_q_heads=8, n_kv_heads=2, head_dim=32, ffn=200, vocab=300,
+                          rope_theta=500000.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_cached_decode_equals_float64_causal_forward(name):
+    shape = SHAPES[name]
+    w16, w64 = _weights(shape, seed=11)
+    # scale up weights so that attention is far from uniform and errors would show
+    rng = np.random.default_rng(12)
+    tokens = rng.integers(0, shape.vocab, 12)
+    orc = po.Oracle(shape, w16, max_seq=16)
+    got = np.stack([orc.step(0, int(t)) for t in tokens])
+    ref = forward_logits(shape, w64, tokens)
+    err = np.abs(got - ref)
+    assert err.max() <= 1e-4 * max(1.0, np.abs(ref).max()), err.max()
+    assert orc.pos() == len(tokens)
+
+
+def test_cached_decode_with_prefilled_kv_equals_float64_forward():
+    shape = SHAPES["tiny_gqa"]
+    w16, w64 = _weights(shape, seed=13)
+    rng = np.random.default_rng(14)
+    P, KD = 9, shape.n_kv_heads * shape.head_dim
+    k16 = bits(rng.standard_normal((shape.n_layers, P, KD)))
+    v16 = bits(rng.standard_normal((shape.n_layers, P, KD)))
+    tokens = rng.integers(0, shape.vocab, 5)
+    orc = po.Oracle(shape, w16, max_seq=P + 5)
+    orc.set_kv(0, k16, v16)
+    got = np.stack([orc.step(0, int(t)) for t in tokens])
+    ref = forward_logits(shape, w64, tokens, kv_prefix=(bf16_bits_to_f64(k16), bf16_bits_to_f64(v16)))
+    assert np.abs(got - ref).max() <= 1e-4 * max(1.0, np.abs(ref).max())
+
+
+def test_zero_residual_branches_reduce_to_embedding_readout():
+    # Wo = Wd = 0: every layer leaves x unchanged, so logits = W_lm . rmsnorm(E[tok]) . gamma_f
+    shape = SHAPES["tiny_gqa"]
+    w16, w64 = _weights(shape, seed=15)
+    names = synth.canonical_names(shape)
+    for i, n in enumerate(names):
+        if n.endswith(".wo") or n.endswith(".w_down"):
+            w16[i] = np.zeros_like(w16[i])
+    orc = po.Oracle(shape, w16, max_seq=4)
+    for tok in (3, 700, 1023):
+        logits = orc.step(0, tok)
+        e = w64["embed"][tok]
+        h = e / np.sqrt(np.mean(e * e) + shape.rms_eps) * w64["final_norm"]
+        ref = w64["lm_head"] @ h
+        assert np.abs(logits - ref).max() < 1e-5
+        assert po.argmax(logits) == int(np.argmax(ref))
+
+
+def test_cache_capacity_and_token_range_errors():
+    shape = SHAPES["tiny_g4"]
+    w16, _ = _weights(shape, seed=16, gamma_random=False)
+    orc = po.Oracle(shape, w16, max_seq=2)
+    orc.step(0, 1, want_logits=False)
+    with pytest.raises(ValueError):
+        orc.step(0, shape.vocab)
+    orc.step(0, 2, want_logits=False)
+    with pytest.raises(ValueError):
+        orc.step(0, 3)
