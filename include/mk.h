@@ -1,0 +1,162 @@
+/*
+ * mk.h -- C ABI of the persistent decode megakernel library (libmk.so).
+ *
+ * The library runs greedy autoregressive decode of a Llama-style decoder on
+ * one MI355X (gfx950) GPU.  Each decode step is lowered, once, by a host-side
+ * builder to a fine-grained task graph: every operator becomes row tiles
+ * ("tasks"), and tasks are joined by events that fire when a counter of
+ * completed producers reaches a threshold.  This is the compiler / runtime
+ * split described in the MPK digest (fr.news.hada.io, "Part 1. Compilateur"
+ * and "Part 2. Runtime", "Exécution pilotée par événements").  The runtime
+ * is one persistent kernel whose workgroups (one per compute unit) each walk
+ * a static, pre-planned task list, the schedule being fixed ahead of time as
+ * in Ada-MK (gist.science, "L'Itinéraire Pré-planifié").  A second mode
+ * launches the same tasks as one kernel per operator, to measure what the
+ * single persistent kernel removes.
+ *
+ * Conventions for every call:
+ *  - Return value: MK_OK (0) or a negative MK_ERR_* code; no call throws.
+ *    After a failure, mk_last_error(ctx) describes it.
+ *  - A context is used by one host thread at a time.
+ *  - Device pointers are HIP device addresses on the context's device;
+ *    host pointers are ordinary host memory.  Ownership never transfers:
+ *    the library copies what it needs and never frees caller memory.
+ *  - Work is ordered on the context's stream (cfg.stream, or the null
+ *    stream); calls that produce results synchronise that stream before
+ *    returning.
+ *  - Layouts are row-major; bf16 values are raw 16-bit patterns.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes ------------------------------------------------------ */
+#define MK_OK 0
+#define MK_ERR_INVALID_ARG (-1) /* bad pointer, size, name, shape or value */
+#define MK_ERR_UNSUPPORTED (-2) /* shape or batch this build cannot tile  */
+#define MK_ERR_OOM (-3)         /* device or host allocation failed       */
+#define MK_ERR_HIP (-4)         /* a HIP runtime call failed              */
+#define MK_ERR_CAPACITY (-5)    /* a position would exceed max_seq        */
+#define MK_ERR_TIMEOUT (-6)     /* an event wait exceeded its poll budget */
+#define MK_ERR_STATE (-7)       /* call out of order (e.g. no weights)    */
+
+/* ---- execution modes ---------------------------------------------------- */
+#define MK_MODE_MEGAKERNEL 0 /* one persistent cooperative launch per mk_decode */
+#define MK_MODE_PER_OP 1     /* ablation: one kernel launch per operator        */
+
+/* ---- model / runtime configuration (plain data, copied by mk_create) ---- */
+typedef struct mk_model_cfg {
+  int32_t n_layers;   /* decoder layers L                                   */
+  int32_t hidden;     /* model width H                                      */
+  int32_t n_q_heads;  /* query heads Hq                                     */
+  int32_t n_kv_heads; /* key/value heads Hkv (Hq % Hkv == 0)                */
+  int32_t head_dim;   /* D, even, multiple of 8, <= 256                     */
+  int32_t ffn;        /* SwiGLU width F                                     */
+  int32_t vocab;      /* V                                                  */
+  float rms_eps;      /* RMSNorm epsilon                                    */
+  double rope_theta;  /* RoPE base                                          */
+  int32_t qk_norm;    /* 1: per-head RMSNorm of q and k before RoPE         */
+  int32_t batch;      /* B independent sequences decoded together           */
+  int32_t max_seq;    /* KV capacity in positions per sequence              */
+  int32_t mode;       /* MK_MODE_*                                          */
+  int32_t split;      /* KV positions per attention task; 0 = default (64)  */
+  int32_t n_workers;  /* persistent workgroups; 0 = one per compute unit    */
+  uint32_t watchdog_polls; /* max polls of one event wait; 0 = default     */
+  void* stream;       /* hipStream_t the library launches on, or NULL       */
+} mk_model_cfg;
+
+typedef struct mk_ctx mk_ctx;
+
+/* One weight tensor in canonical form.  Names and shapes (all bf16):
+ *   "embed" [V,H]; per layer l, prefix "layers.<l>.":
+ *   "attn_norm" [H], "wq" [Hq*D,H], "wk" [Hkv*D,H], "wv" [Hkv*D,H],
+ *   "wo" [H,Hq*D], ("q_norm" [D], "k_norm" [D] when qk_norm),
+ *   "ffn_norm" [H], "w_gate" [F,H], "w_up" [F,H], "w_down" [H,F];
+ *   "final_norm" [H], "lm_head" [V,H].
+ * Matrices are [out, in] row-major.  data is a host pointer, or a device
+ * pointer when on_device != 0. */
+typedef struct mk_tensor {
+  const char* name;
+  const void* data;
+  int64_t numel;
+  int32_t on_device;
+} mk_tensor;
+
+/* Validate cfg, build the task graph (host only) and allocate every device
+ * buffer: packed weights, KV cache [L][B][Hkv][max_seq][D] bf16 (K and V),
+ * activations, event flags.  *out receives the context.  Errors:
+ * INVALID_ARG, UNSUPPORTED (shape cannot be tiled), OOM, HIP. */
+int mk_create(const mk_model_cfg* cfg, mk_ctx** out);
+
+/* Copy and repack all weights.  Exactly the canonical set must be given,
+ * each with its canonical numel, in any order.  Synchronous.  Errors:
+ * INVALID_ARG (missing, duplicate, unknown or misshaped tensor), HIP. */
+int mk_load_weights(mk_ctx* ctx, const mk_tensor* tensors, int n);
+
+/* Prefill every sequence with its prompt: prompts is host int32 [B][len],
+ * ids in [0, V).  Positions 0..len-2 are written to the KV cache (decode
+ * steps run per operator, without the LM head) and prompts[b][len-1]
+ * becomes the token decode step 0 consumes at position len-1.  Resets any
+ * previous state.  Synchronous.  Errors: INVALID_ARG, CAPACITY
+ * (len > max_seq), STATE (no weights), HIP. */
+int mk_prefill(mk_ctx* ctx, const int32_t* prompts, int len);
+
+/* Install a pre-filled KV cache for sequence seq: k and v are bf16
+ * [L][n_pos][Hkv*D] (keys already rotated), host memory or device memory
+ * (on_device != 0).  pending is the token decode step 0 consumes at
+ * position n_pos.  All sequences must hold the same n_pos before
+ * mk_decode.  Synchronous.  Errors: INVALID_ARG, CAPACITY, HIP. */
+int mk_load_kv(mk_ctx* ctx, int seq, int n_pos, const void* k, const void* v, int32_t pending,
+               int on_device);
+
+/* Run n_steps greedy decode steps for all B sequences.  out_tokens is a
+ * device int32 [n_steps][B] buffer; out_logits a device fp32
+ * [n_steps][B][V] buffer or NULL.  Step i consumes the pending token at
+ * position pos+i, appends its K/V, and writes logits and the argmax
+ * (lowest index on ties), which becomes the next pending token.  In
+ * megakernel mode this is ONE kernel launch.  Synchronous.  Errors:
+ * INVALID_ARG, CAPACITY (pos + n_steps > max_seq), STATE, TIMEOUT
+ * (watchdog; state is then undefined until mk_reset), HIP. */
+int mk_decode(mk_ctx* ctx, int n_steps, int32_t* out_tokens, float* out_logits);
+
+/* Switch between MK_MODE_MEGAKERNEL and MK_MODE_PER_OP; state is kept. */
+int mk_set_mode(mk_ctx* ctx, int mode);
+
+/* Current position (shared by all sequences) and, if pending != NULL,
+ * host int32 [B] pending tokens. */
+int mk_get_state(mk_ctx* ctx, int32_t* pos, int32_t* pending);
+
+/* Canonical little-endian serialisation of the task graph (header, event
+ * table, task table in topological order).  If buf is NULL or *len is too
+ * small, *len receives the size needed and MK_ERR_INVALID_ARG is returned
+ * when buf is non-NULL. */
+int mk_get_graph(mk_ctx* ctx, void* buf, size_t* len);
+
+/* Build the canonical graph bytes for cfg with n_workers workgroups without
+ * touching any GPU (same rules as mk_create). */
+int mk_build_graph(const mk_model_cfg* cfg, int n_workers, void* buf, size_t* len);
+
+/* Zero positions, pending tokens, event flags and tickets (weights kept). */
+int mk_reset(mk_ctx* ctx);
+
+/* Duration in milliseconds of the last mk_decode's kernel work, measured
+ * with HIP events on the context's stream around the launch(es). */
+int mk_last_decode_ms(mk_ctx* ctx, float* ms);
+
+/* Text of the last error on ctx (or of the last failed mk_create when ctx
+ * is NULL).  Owned by the library; valid until the next call on ctx. */
+const char* mk_last_error(mk_ctx* ctx);
+
+/* Free everything; NULL is a no-op. */
+void mk_destroy(mk_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,582 @@
+// api.cpp -- the C ABI of libmk.so: context lifecycle, weight packing, KV
+// installation, prefill (per operator, as in Ada-MK's split between a
+// conventional prefill engine and the megakernel for decode -- gist.science,
+// "La « Flotte Hybride »"), decode in either execution mode, and the graph
+// export used to check the builder bit for bit.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "graph.h"
+#include "mk_internal.h"
+
+namespace mk {
+hipError_t prepare_kernels(int B);
+hipError_t launch(int kind, const KParams& P, hipStream_t st);
+size_t lds_bytes(const KParams& P);
+int max_coresident_workers(int B, size_t lds);
+constexpr int kXsFloats = 28672;
+constexpr int kRedFloats = 8192;
+constexpr uint32_t kDefaultWatchdog = 1u << 22;  // ~1-2 us per poll: several seconds, far above any healthy wait
+}  // namespace mk
+
+using namespace mk;
+
+struct mk_ctx {
+  mk_model_cfg cfg{};
+  Graph g;
+  hipStream_t stream = nullptr;
+  int device = 0;
+  std::string err;
+  // device memory
+  std::vector<void*> allocs;
+  uint16_t* warena = nullptr;
+  size_t wbytes = 0;
+  std::map<std::string, std::pair<size_t, int64_t>> wslots;  // canonical name -> (offset in elems, numel) for plain tensors
+  LayerW* d_layers = nullptr;
+  std::vector<LayerW> h_layers;
+  uint16_t *embed = nullptr, *final_norm = nullptr, *lm_head = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  uint16_t *kc = nullptr, *vc = nullptr;
+  size_t kv_elems = 0;
+  float *x = nullptr, *qkv = nullptr, *o = nullptr, *a = nullptr, *part_ml = nullptr, *part_acc = nullptr;
+  uint32_t* tickets = nullptr;
+  size_t n_tickets = 0;
+  LmPart* lm_part = nullptr;
+  int32_t* pending = nullptr;
+  int32_t* force = nullptr;
+  size_t force_cap = 0;
+  uint32_t* flags = nullptr;
+  uint32_t* status = nullptr;
+  EventRec* d_events = nullptr;
+  TaskRec* d_tasks = nullptr;
+  uint32_t *d_task_cu = nullptr, *d_list_off = nullptr, *d_list_len = nullptr, *d_cu_tasks = nullptr;
+  // state
+  bool have_weights = false;
+  int pos = 0;
+  std::vector<int> seq_pos;
+  uint32_t epoch = 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  float last_ms = 0.f;
+};
+
+static std::string g_create_err;
+
+static int fail(mk_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  else g_create_err = msg;
+  return code;
+}
+
+#define HIPCHK(ctx, call)                                                                           \
+  do {                                                                                              \
+    hipError_t e_ = (call);                                                                         \
+    if (e_ != hipSuccess) return fail(ctx, MK_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+static int dalloc(mk_ctx* c, void** p, size_t bytes) {
+  bytes = (bytes + 255) & ~(size_t)255;
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) return fail(c, MK_ERR_OOM, std::string("hipMalloc(") + std::to_string(bytes) + "): " + hipGetErrorString(e));
+  c->allocs.push_back(*p);
+  return MK_OK;
+}
+
+static std::string validate(const mk_model_cfg& cfg) {
+  if (cfg.batch != 1 && cfg.batch != 2 && cfg.batch != 4 && cfg.batch != 8 && cfg.batch != 16)
+    return "batch must be 1, 2, 4, 8 or 16";
+  if (cfg.n_q_heads <= 0 || cfg.n_kv_heads <= 0 || cfg.n_q_heads % cfg.n_kv_heads) return "bad head counts";
+  const int G = cfg.n_q_heads / cfg.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return "query heads per KV head must be 1, 2 or 4";
+  if (cfg.mode != MK_MODE_MEGAKERNEL && cfg.mode != MK_MODE_PER_OP) return "unknown mode";
+  if (!(cfg.rms_eps > 0.f) || !(cfg.rope_theta > 0.0)) return "rms_eps and rope_theta must be positive";
+  return "";
+}
+
+static int check_capacity(const mk_model_cfg& cfg, const Graph& g, std::string* why) {
+  const int D = cfg.head_dim, G = cfg.n_q_heads / cfg.n_kv_heads;
+  const int S = g.split;
+  const int lpp = D / 8, ppb = 512 / lpp;
+  if (S > 4 * ppb) {
+    *why = "split too large for head_dim (at most 16384 / head_dim)";
+    return MK_ERR_UNSUPPORTED;
+  }
+  const int att_floats = (G + 2) * D + G * D + D + G * S + 8 * G * D;
+  if (att_floats > kXsFloats) {
+    *why = "attention working set exceeds LDS";
+    return MK_ERR_UNSUPPORTED;
+  }
+  auto maxrows = [](int R, int T) { return (R + T - 1) / T; };
+  int worst = std::max({maxrows(cfg.hidden, g.n_wo) * 1, maxrows(cfg.ffn, g.n_gu) * 2, maxrows(cfg.vocab, g.n_lm),
+                        (G + 2) * D / g.qkv_tiles_per_group + 1});
+  if ((int64_t)worst * cfg.batch > kRedFloats) {
+    *why = "a GEMV tile has too many rows for the reduction buffer (use more workers or a smaller batch)";
+    return MK_ERR_UNSUPPORTED;
+  }
+  return MK_OK;
+}
+
+extern "C" {
+
+int mk_build_graph(const mk_model_cfg* cfg, int n_workers, void* buf, size_t* len) {
+  if (!cfg || !len) return fail(nullptr, MK_ERR_INVALID_ARG, "null argument");
+  std::string why = validate(*cfg);
+  if (!why.empty()) return fail(nullptr, MK_ERR_INVALID_ARG, why);
+  Graph g;
+  why = build_graph(*cfg, n_workers, &g);
+  if (!why.empty()) return fail(nullptr, MK_ERR_UNSUPPORTED, why);
+  std::vector<uint8_t> bytes = serialize_graph(*cfg, g);
+  const size_t need = bytes.size();
+  if (!buf || *len < need) {
+    *len = need;
+    return buf ? fail(nullptr, MK_ERR_INVALID_ARG, "buffer too small") : MK_OK;
+  }
+  std::memcpy(buf, bytes.data(), need);
+  *len = need;
+  return MK_OK;
+}
+
+int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
+  if (!cfg_in || !out) return fail(nullptr, MK_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  std::string why = validate(*cfg_in);
+  if (!why.empty()) return fail(nullptr, MK_ERR_INVALID_ARG, why);
+  mk_ctx* c = new mk_ctx();
+  c->cfg = *cfg_in;
+  const mk_model_cfg& cfg = c->cfg;
+  auto bail = [&](int code) {
+    g_create_err = c->err;
+    mk_destroy(c);
+    return code;
+  };
+  c->stream = (hipStream_t)cfg.stream;
+  if (hipGetDevice(&c->device) != hipSuccess) return bail(fail(c, MK_ERR_HIP, "hipGetDevice failed"));
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) return bail(fail(c, MK_ERR_HIP, "hipGetDeviceProperties"));
+  int nw = cfg.n_workers > 0 ? cfg.n_workers : prop.multiProcessorCount;
+  why = build_graph(cfg, nw, &c->g);
+  if (!why.empty()) return bail(fail(c, MK_ERR_UNSUPPORTED, why));
+  int rc = check_capacity(cfg, c->g, &why);
+  if (rc) return bail(fail(c, rc, why));
+  if (prepare_kernels(cfg.batch) != hipSuccess) return bail(fail(c, MK_ERR_HIP, "hipFuncSetAttribute failed"));
+  {
+    KParams tmp{};
+    tmp.xs_floats = kXsFloats;
+    const int per_cu = max_coresident_workers(cfg.batch, lds_bytes(tmp));
+    if (per_cu < 1 || (int64_t)per_cu * prop.multiProcessorCount < nw)
+      return bail(fail(c, MK_ERR_UNSUPPORTED, "workers cannot all be resident at once (cooperative launch)"));
+  }
+  const int L = cfg.n_layers, H = cfg.hidden, D = cfg.head_dim, Hq = cfg.n_q_heads, Hkv = cfg.n_kv_heads;
+  const int F = cfg.ffn, V = cfg.vocab, B = cfg.batch, G = Hq / Hkv;
+  const size_t QD = (size_t)Hq * D, KD = (size_t)Hkv * D, QKVR = QD + 2 * KD;
+
+  // ---- weight arena (256-byte aligned tensors)
+  size_t off = 0;
+  auto take = [&](size_t elems) {
+    size_t o = off;
+    off += (elems * 2 + 255) / 256 * 128;  // elems of bf16, rounded to 256 bytes
+    return o;
+  };
+  std::vector<size_t> lo(L * 9);
+  const size_t o_embed = take((size_t)V * H);
+  for (int l = 0; l < L; ++l) {
+    lo[l * 9 + 0] = take(QKVR * H);
+    lo[l * 9 + 1] = take((size_t)H * QD);
+    lo[l * 9 + 2] = take((size_t)F * H);
+    lo[l * 9 + 3] = take((size_t)F * H);
+    lo[l * 9 + 4] = take((size_t)H * F);
+    lo[l * 9 + 5] = take(H);
+    lo[l * 9 + 6] = take(H);
+    lo[l * 9 + 7] = take(D);
+    lo[l * 9 + 8] = take(D);
+  }
+  const size_t o_fn = take(H), o_lm = take((size_t)V * H);
+  c->wbytes = off * 2;
+  if ((rc = dalloc(c, (void**)&c->warena, c->wbytes))) return bail(rc);
+  c->embed = c->warena + o_embed;
+  c->final_norm = c->warena + o_fn;
+  c->lm_head = c->warena + o_lm;
+  c->h_layers.resize(L);
+  for (int l = 0; l < L; ++l) {
+    LayerW& w = c->h_layers[l];
+    w.wqkv = c->warena + lo[l * 9 + 0];
+    w.wo = c->warena + lo[l * 9 + 1];
+    w.wg = c->warena + lo[l * 9 + 2];
+    w.wu = c->warena + lo[l * 9 + 3];
+    w.wd = c->warena + lo[l * 9 + 4];
+    w.attn_norm = c->warena + lo[l * 9 + 5];
+    w.ffn_norm = c->warena + lo[l * 9 + 6];
+    w.q_norm = cfg.qk_norm ? c->warena + lo[l * 9 + 7] : nullptr;
+    w.k_norm = cfg.qk_norm ? c->warena + lo[l * 9 + 8] : nullptr;
+    const std::string p = "layers." + std::to_string(l) + ".";
+    c->wslots[p + "wo"] = {lo[l * 9 + 1], (int64_t)H * QD};
+    c->wslots[p + "w_gate"] = {lo[l * 9 + 2], (int64_t)F * H};
+    c->wslots[p + "w_up"] = {lo[l * 9 + 3], (int64_t)F * H};
+    c->wslots[p + "w_down"] = {lo[l * 9 + 4], (int64_t)H * F};
+    c->wslots[p + "attn_norm"] = {lo[l * 9 + 5], H};
+    c->wslots[p + "ffn_norm"] = {lo[l * 9 + 6], H};
+    if (cfg.qk_norm) {
+      c->wslots[p + "q_norm"] = {lo[l * 9 + 7], D};
+      c->wslots[p + "k_norm"] = {lo[l * 9 + 8], D};
+    }
+  }
+  c->wslots["embed"] = {o_embed, (int64_t)V * H};
+  c->wslots["final_norm"] = {o_fn, H};
+  c->wslots["lm_head"] = {o_lm, (int64_t)V * H};
+  if ((rc = dalloc(c, (void**)&c->d_layers, sizeof(LayerW) * L))) return bail(rc);
+  if (hipMemcpy(c->d_layers, c->h_layers.data(), sizeof(LayerW) * L, hipMemcpyHostToDevice) != hipSuccess)
+    return bail(fail(c, MK_ERR_HIP, "layer table upload"));
+  (void)G;
+
+  // ---- RoPE tables: angle pos * theta^(-2i/D) in fp64, rounded to fp32
+  {
+    const int half = D / 2;
+    std::vector<float> hc((size_t)cfg.max_seq * half), hs(hc.size());
+    for (int p = 0; p < cfg.max_seq; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * std::pow(cfg.rope_theta, -2.0 * (double)i / (double)D);
+        hc[(size_t)p * half + i] = (float)std::cos(ang);
+        hs[(size_t)p * half + i] = (float)std::sin(ang);
+      }
+    if ((rc = dalloc(c, (void**)&c->rope_cos, hc.size() * 4))) return bail(rc);
+    if ((rc = dalloc(c, (void**)&c->rope_sin, hs.size() * 4))) return bail(rc);
+    if (hipMemcpy(c->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(c->rope_sin, hs.data(), hs.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return bail(fail(c, MK_ERR_HIP, "rope upload"));
+  }
+
+  // ---- KV cache and activations
+  c->kv_elems = (size_t)L * B * Hkv * cfg.max_seq * D;
+  if ((rc = dalloc(c, (void**)&c->kc, c->kv_elems * 2))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->vc, c->kv_elems * 2))) return bail(rc);
+  const int NS = c->g.n_splits;
+  if ((rc = dalloc(c, (void**)&c->x, (size_t)B * H * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->qkv, (size_t)B * QKVR * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->o, (size_t)B * QD * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->a, (size_t)B * F * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->part_ml, (size_t)B * Hkv * NS * G * 2 * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->part_acc, (size_t)B * Hkv * NS * G * D * 4))) return bail(rc);
+  c->n_tickets = (size_t)L * B * Hkv;
+  if ((rc = dalloc(c, (void**)&c->tickets, c->n_tickets * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->lm_part, (size_t)B * c->g.n_lm * sizeof(LmPart)))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->pending, (size_t)B * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->flags, (size_t)c->g.n_slots * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->status, 64))) return bail(rc);
+  // ---- graph tables
+  const Graph& g = c->g;
+  if ((rc = dalloc(c, (void**)&c->d_events, g.events.size() * sizeof(EventRec)))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->d_tasks, g.tasks.size() * sizeof(TaskRec)))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->d_task_cu, g.task_cu.size() * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->d_list_off, g.list_off.size() * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->d_list_len, g.list_len.size() * 4))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->d_cu_tasks, g.cu_tasks.size() * 4))) return bail(rc);
+  if (hipMemcpy(c->d_events, g.events.data(), g.events.size() * sizeof(EventRec), hipMemcpyHostToDevice) ||
+      hipMemcpy(c->d_tasks, g.tasks.data(), g.tasks.size() * sizeof(TaskRec), hipMemcpyHostToDevice) ||
+      hipMemcpy(c->d_task_cu, g.task_cu.data(), g.task_cu.size() * 4, hipMemcpyHostToDevice) ||
+      hipMemcpy(c->d_list_off, g.list_off.data(), g.list_off.size() * 4, hipMemcpyHostToDevice) ||
+      hipMemcpy(c->d_list_len, g.list_len.data(), g.list_len.size() * 4, hipMemcpyHostToDevice) ||
+      hipMemcpy(c->d_cu_tasks, g.cu_tasks.data(), g.cu_tasks.size() * 4, hipMemcpyHostToDevice))
+    return bail(fail(c, MK_ERR_HIP, "graph upload"));
+  if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess)
+    return bail(fail(c, MK_ERR_HIP, "hipEventCreate"));
+  c->seq_pos.assign(B, 0);
+  if ((rc = mk_reset(c))) return bail(rc);
+  HIPCHK(c, hipMemset(c->kc, 0, c->kv_elems * 2));
+  HIPCHK(c, hipMemset(c->vc, 0, c->kv_elems * 2));
+  HIPCHK(c, hipDeviceSynchronize());
+  *out = c;
+  return MK_OK;
+}
+
+void mk_destroy(mk_ctx* c) {
+  if (!c) return;
+  if (c->stream) (void)hipStreamSynchronize(c->stream);
+  else (void)hipDeviceSynchronize();
+  for (void* p : c->allocs) (void)hipFree(p);
+  if (c->ev0) (void)hipEventDestroy(c->ev0);
+  if (c->ev1) (void)hipEventDestroy(c->ev1);
+  delete c;
+}
+
+const char* mk_last_error(mk_ctx* c) { return c ? c->err.c_str() : g_create_err.c_str(); }
+
+int mk_reset(mk_ctx* c) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
+  HIPCHK(c, hipMemsetAsync(c->flags, 0, (size_t)c->g.n_slots * 4, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->tickets, 0, c->n_tickets * 4, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->status, 0, 64, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->pending, 0, (size_t)c->cfg.batch * 4, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->pos = 0;
+  std::fill(c->seq_pos.begin(), c->seq_pos.end(), 0);
+  c->epoch = 0;
+  return MK_OK;
+}
+
+int mk_load_weights(mk_ctx* c, const mk_tensor* t, int n) {
+  if (!c || (!t && n > 0) || n < 0) return fail(c, MK_ERR_INVALID_ARG, "null argument");
+  const mk_model_cfg& cfg = c->cfg;
+  const int L = cfg.n_layers, H = cfg.hidden, D = cfg.head_dim, Hq = cfg.n_q_heads, Hkv = cfg.n_kv_heads;
+  const int G = Hq / Hkv;
+  const size_t RG = (size_t)(G + 2) * D;
+  std::map<std::string, int> seen;
+  const int expected = 1 + L * (9 + (cfg.qk_norm ? 2 : 0)) + 2;
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].name || !t[i].data) return fail(c, MK_ERR_INVALID_ARG, "tensor with null name or data");
+    if (seen.count(t[i].name)) return fail(c, MK_ERR_INVALID_ARG, std::string("duplicate tensor ") + t[i].name);
+    seen[t[i].name] = i;
+  }
+  if (n != expected) return fail(c, MK_ERR_INVALID_ARG, "expected " + std::to_string(expected) + " tensors, got " + std::to_string(n));
+  for (int i = 0; i < n; ++i) {
+    const std::string name = t[i].name;
+    const hipMemcpyKind kind = t[i].on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+    const uint16_t* src = (const uint16_t*)t[i].data;
+    auto it = c->wslots.find(name);
+    if (it != c->wslots.end()) {
+      if (t[i].numel != it->second.second) return fail(c, MK_ERR_INVALID_ARG, "wrong numel for " + name);
+      HIPCHK(c, hipMemcpyAsync(c->warena + it->second.first, src, (size_t)t[i].numel * 2, kind, c->stream));
+      continue;
+    }
+    // q/k/v: pack per KV-head group [G q heads | k | v]
+    int l = -1;
+    char which[16] = {0};
+    if (std::sscanf(name.c_str(), "layers.%d.%15s", &l, which) == 2 && l >= 0 && l < L &&
+        (!std::strcmp(which, "wq") || !std::strcmp(which, "wk") || !std::strcmp(which, "wv"))) {
+      const bool isq = which[1] == 'q';
+      const int nh = isq ? Hq : Hkv;
+      if (t[i].numel != (int64_t)nh * D * H) return fail(c, MK_ERR_INVALID_ARG, "wrong numel for " + name);
+      uint16_t* dst0 = const_cast<uint16_t*>(c->h_layers[l].wqkv);
+      for (int h = 0; h < nh; ++h) {
+        const int grp = isq ? h / G : h;
+        const size_t row = grp * RG + (isq ? (size_t)(h % G) * D : (which[1] == 'k' ? (size_t)G * D : (size_t)(G + 1) * D));
+        HIPCHK(c, hipMemcpyAsync(dst0 + row * H, src + (size_t)h * D * H, (size_t)D * H * 2, kind, c->stream));
+      }
+      continue;
+    }
+    return fail(c, MK_ERR_INVALID_ARG, "unknown tensor " + name);
+  }
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->have_weights = true;
+  return MK_OK;
+}
+
+static KParams make_params(mk_ctx* c) {
+  const mk_model_cfg& cfg = c->cfg;
+  KParams P{};
+  P.L = cfg.n_layers;
+  P.H = cfg.hidden;
+  P.Hq = cfg.n_q_heads;
+  P.Hkv = cfg.n_kv_heads;
+  P.D = cfg.head_dim;
+  P.F = cfg.ffn;
+  P.V = cfg.vocab;
+  P.G = P.Hq / P.Hkv;
+  P.RG = (P.G + 2) * P.D;
+  P.QKVR = P.Hkv * P.RG;
+  P.QD = P.Hq * P.D;
+  P.B = cfg.batch;
+  P.max_seq = cfg.max_seq;
+  P.S = c->g.split;
+  P.NS = c->g.n_splits;
+  P.qk_norm = cfg.qk_norm;
+  P.eps = cfg.rms_eps;
+  P.attn_scale = (float)(1.0 / std::sqrt((double)cfg.head_dim));
+  P.n_workers = c->g.n_workers;
+  P.n_qkv = c->g.n_qkv;
+  P.n_wo = c->g.n_wo;
+  P.n_gu = c->g.n_gu;
+  P.n_down = c->g.n_down;
+  P.n_lm = c->g.n_lm;
+  P.xs_floats = kXsFloats;
+  P.layers = c->d_layers;
+  P.embed = c->embed;
+  P.final_norm = c->final_norm;
+  P.lm_head = c->lm_head;
+  P.rope_cos = c->rope_cos;
+  P.rope_sin = c->rope_sin;
+  P.kc = c->kc;
+  P.vc = c->vc;
+  P.x = c->x;
+  P.qkv = c->qkv;
+  P.o = c->o;
+  P.a = c->a;
+  P.part_ml = c->part_ml;
+  P.part_acc = c->part_acc;
+  P.tickets = c->tickets;
+  P.lm_part = c->lm_part;
+  P.pending = c->pending;
+  P.flags = c->flags;
+  P.events = c->d_events;
+  P.tasks = c->d_tasks;
+  P.task_cu = c->d_task_cu;
+  P.list_off = c->d_list_off;
+  P.list_len = c->d_list_len;
+  P.cu_tasks = c->d_cu_tasks;
+  P.status = c->status;
+  P.watchdog = cfg.watchdog_polls ? cfg.watchdog_polls : kDefaultWatchdog;
+  P.with_lm = 1;
+  return P;
+}
+
+// one decode step per operator launch (ablation mode and prefill)
+static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
+  const Graph& g = c->g;
+  const size_t n_ranges = g.op_ranges.size() - (with_lm ? 0 : 1);
+  for (int s = 0; s < n_steps; ++s) {
+    P.step = s;
+    for (size_t r = 0; r < n_ranges; ++r) {
+      P.op_first = (int)g.op_ranges[r].first;
+      P.op_count = (int)g.op_ranges[r].count;
+      HIPCHK(c, launch(1, P, c->stream));
+    }
+  }
+  if (with_lm) {
+    P.step = n_steps - 1;
+    HIPCHK(c, launch(2, P, c->stream));
+  }
+  return MK_OK;
+}
+
+int mk_prefill(mk_ctx* c, const int32_t* prompts, int len) {
+  if (!c || !prompts || len <= 0) return fail(c, MK_ERR_INVALID_ARG, "null prompts or len <= 0");
+  if (!c->have_weights) return fail(c, MK_ERR_STATE, "weights not loaded");
+  if (len > c->cfg.max_seq) return fail(c, MK_ERR_CAPACITY, "prompt longer than max_seq");
+  const int B = c->cfg.batch;
+  for (int64_t i = 0; i < (int64_t)B * len; ++i)
+    if (prompts[i] < 0 || prompts[i] >= c->cfg.vocab) return fail(c, MK_ERR_INVALID_ARG, "token id out of range");
+  int rc = mk_reset(c);
+  if (rc) return rc;
+  const int n = len - 1;
+  if (n > 0) {
+    std::vector<int32_t> f((size_t)n * B);
+    for (int s = 0; s < n; ++s)
+      for (int b = 0; b < B; ++b) f[(size_t)s * B + b] = prompts[(size_t)b * len + s];
+    if ((size_t)n * B > c->force_cap) {
+      if (c->force) {
+        (void)hipFree(c->force);
+        c->allocs.erase(std::find(c->allocs.begin(), c->allocs.end(), (void*)c->force));
+        c->force = nullptr;
+      }
+      if ((rc = dalloc(c, (void**)&c->force, f.size() * 4))) return rc;
+      c->force_cap = f.size();
+    }
+    HIPCHK(c, hipMemcpyAsync(c->force, f.data(), f.size() * 4, hipMemcpyHostToDevice, c->stream));
+    KParams P = make_params(c);
+    P.pos0 = 0;
+    P.n_steps = n;
+    P.force_tok = c->force;
+    P.with_lm = 0;
+    if ((rc = run_per_op_steps(c, P, n, false))) return rc;
+  }
+  std::vector<int32_t> pend(B);
+  for (int b = 0; b < B; ++b) pend[b] = prompts[(size_t)b * len + len - 1];
+  HIPCHK(c, hipMemcpyAsync(c->pending, pend.data(), (size_t)B * 4, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->pos = n;
+  std::fill(c->seq_pos.begin(), c->seq_pos.end(), n);
+  return MK_OK;
+}
+
+int mk_load_kv(mk_ctx* c, int seq, int n_pos, const void* k, const void* v, int32_t pending, int on_device) {
+  if (!c || !k || !v) return fail(c, MK_ERR_INVALID_ARG, "null argument");
+  const mk_model_cfg& cfg = c->cfg;
+  if (seq < 0 || seq >= cfg.batch || n_pos < 0) return fail(c, MK_ERR_INVALID_ARG, "bad seq or n_pos");
+  if (n_pos >= cfg.max_seq) return fail(c, MK_ERR_CAPACITY, "n_pos must leave room for one decode step");
+  if (pending < 0 || pending >= cfg.vocab) return fail(c, MK_ERR_INVALID_ARG, "pending token out of range");
+  const int L = cfg.n_layers, D = cfg.head_dim, Hkv = cfg.n_kv_heads, B = cfg.batch;
+  const hipMemcpyKind kind = on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  const size_t KD = (size_t)Hkv * D;
+  for (int l = 0; l < L && n_pos > 0; ++l)
+    for (int g = 0; g < Hkv; ++g) {
+      const size_t dst = (((size_t)l * B + seq) * Hkv + g) * cfg.max_seq * D;
+      const size_t src = (size_t)l * n_pos * KD + (size_t)g * D;
+      HIPCHK(c, hipMemcpy2DAsync(c->kc + dst, D * 2, (const uint16_t*)k + src, KD * 2, D * 2, n_pos, kind, c->stream));
+      HIPCHK(c, hipMemcpy2DAsync(c->vc + dst, D * 2, (const uint16_t*)v + src, KD * 2, D * 2, n_pos, kind, c->stream));
+    }
+  HIPCHK(c, hipMemcpyAsync(c->pending + seq, &pending, 4, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->seq_pos[seq] = n_pos;
+  c->pos = n_pos;
+  return MK_OK;
+}
+
+int mk_set_mode(mk_ctx* c, int mode) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
+  if (mode != MK_MODE_MEGAKERNEL && mode != MK_MODE_PER_OP) return fail(c, MK_ERR_INVALID_ARG, "unknown mode");
+  c->cfg.mode = mode;
+  return MK_OK;
+}
+
+int mk_get_state(mk_ctx* c, int32_t* pos, int32_t* pending) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
+  if (pos) *pos = c->pos;
+  if (pending) {
+    HIPCHK(c, hipMemcpyAsync(pending, c->pending, (size_t)c->cfg.batch * 4, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+  }
+  return MK_OK;
+}
+
+int mk_decode(mk_ctx* c, int n_steps, int32_t* out_tokens, float* out_logits) {
+  if (!c || n_steps <= 0 || !out_tokens) return fail(c, MK_ERR_INVALID_ARG, "null out_tokens or n_steps <= 0");
+  if (!c->have_weights) return fail(c, MK_ERR_STATE, "weights not loaded");
+  for (int p : c->seq_pos)
+    if (p != c->pos) return fail(c, MK_ERR_STATE, "sequences hold different numbers of positions");
+  if ((int64_t)c->pos + n_steps > c->cfg.max_seq) return fail(c, MK_ERR_CAPACITY, "decode would exceed max_seq");
+  KParams P = make_params(c);
+  P.pos0 = c->pos;
+  P.n_steps = n_steps;
+  P.out_tokens = out_tokens;
+  P.out_logits = out_logits;
+  P.epoch = c->epoch;
+  HIPCHK(c, hipEventRecord(c->ev0, c->stream));
+  if (c->cfg.mode == MK_MODE_MEGAKERNEL) {
+    HIPCHK(c, launch(0, P, c->stream));
+  } else {
+    int rc = run_per_op_steps(c, P, n_steps, true);
+    if (rc) return rc;
+  }
+  HIPCHK(c, hipEventRecord(c->ev1, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  HIPCHK(c, hipEventElapsedTime(&c->last_ms, c->ev0, c->ev1));
+  uint32_t st[8];
+  HIPCHK(c, hipMemcpy(st, c->status, sizeof st, hipMemcpyDeviceToHost));
+  if (st[ST_ABORT] || st[ST_CODE]) {
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "watchdog: worker %u task %u waited on event %u (slot value %u, wanted %u)",
+                  st[ST_CU], st[ST_TASK], st[ST_EVENT], st[ST_SEEN], st[ST_WANT]);
+    return fail(c, MK_ERR_TIMEOUT, buf);
+  }
+  c->pos += n_steps;
+  std::fill(c->seq_pos.begin(), c->seq_pos.end(), c->pos);
+  if (c->cfg.mode == MK_MODE_MEGAKERNEL) c->epoch += (uint32_t)n_steps;
+  return MK_OK;
+}
+
+int mk_get_graph(mk_ctx* c, void* buf, size_t* len) {
+  if (!c || !len) return fail(c, MK_ERR_INVALID_ARG, "null argument");
+  std::vector<uint8_t> bytes = serialize_graph(c->cfg, c->g);
+  if (!buf || *len < bytes.size()) {
+    *len = bytes.size();
+    return buf ? fail(c, MK_ERR_INVALID_ARG, "buffer too small") : MK_OK;
+  }
+  std::memcpy(buf, bytes.data(), bytes.size());
+  *len = bytes.size();
+  return MK_OK;
+}
+
+int mk_last_decode_ms(mk_ctx* c, float* ms) {
+  if (!c || !ms) return fail(c, MK_ERR_INVALID_ARG, "null argument");
+  *ms = c->last_ms;
+  return MK_OK;
+}
+
+}  // extern "C"

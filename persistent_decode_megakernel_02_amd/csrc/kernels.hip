@@ -1,0 +1,912 @@
+// kernels.hip -- task bodies, the persistent decode megakernel and the
+// per-operator ablation kernels, for gfx950 (MI355X, wave64).
+//
+// Runtime model (MPK digest, fr.news.hada.io, "Part 2. Runtime", "Workers"):
+// every workgroup is a worker that stays resident for the whole launch and
+// loops "take next task from my list -> run it -> notify its event".  The
+// scheduler role of that design is replaced by lists fixed at build time
+// (Ada-MK, gist.science, "L'Itinéraire Pré-planifié"), so a worker never asks
+// anyone what to do next; it only waits until its task's event has fired.
+//
+// Memory protocol.  Activations produced by one worker and consumed by
+// others (x, q/k/v, partials, o, a, LM partials) are written and read with
+// device-coherent accesses (sc1: they bypass the non-coherent per-XCD L2
+// state).  A producer drains its stores (s_waitcnt), joins its workgroup at a
+// barrier and then one lane stores the step number into its own slot of the
+// event; a consumer's wave 0 polls every slot of the event, then the
+// workgroup barrier releases the other waves.  Weights and the KV cache are
+// never written by one worker and read by another inside a launch (a KV
+// position is always re-read by the worker that wrote it), so they use plain
+// or non-temporal loads.
+#include <hip/hip_runtime.h>
+
+#include "mk_internal.h"
+
+namespace mk {
+
+constexpr int NT = 512;  // threads per worker
+constexpr int NW = NT / 64;
+constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
+constexpr int DEPTH = 4;   // pipeline groups in flight per wave (16 KB per wave)
+constexpr int RED_FLOATS = 8192;
+constexpr int MISC_BYTES = 4096;
+constexpr int ATT_MAXL = 4;  // K/V 16-byte loads per thread per attention task
+
+// Pointers kept inside the parameter block are generic; casting them to the
+// global address space lets the compiler emit global (not flat) memory
+// instructions and track their completion precisely.
+#define GAS __attribute__((address_space(1)))
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+struct Misc {
+  float r[16];          // RMSNorm scale per sequence
+  int32_t tok[16];      // tokens of this step (layer-0 QKV)
+  float wred[NW][16];   // per-wave partial sums
+  float wval[NW][16];   // per-wave argmax values
+  int32_t widx[NW][16]; // per-wave argmax indices
+  float hr[16];         // QK-norm scales
+  float ml[8][2];       // attention (max, sum) per head
+  int32_t flag;
+};
+static_assert(sizeof(Misc) <= MISC_BYTES, "misc");
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf1(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+extern __shared__ __attribute__((aligned(16))) char g_lds[];
+
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v4u_ __attribute__((ext_vector_type(4)));
+// plain global load / store of any trivially copyable T (size 2 or a multiple of 4)
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+  T r;
+  if constexpr (sizeof(T) == 2) {
+    const uint16_t v = *(const GAS uint16_t*)p;
+    __builtin_memcpy(&r, &v, 2);
+  } else if constexpr (sizeof(T) == 8) {
+    const v2u v = *(const GAS v2u*)p;
+    __builtin_memcpy(&r, &v, 8);
+  } else if constexpr (sizeof(T) % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 16); ++i) {
+      const v4u_ v = ((const GAS v4u_*)p)[i];
+      __builtin_memcpy((char*)&r + 16 * i, &v, 16);
+    }
+  } else {
+    static_assert(sizeof(T) % 4 == 0, "ldg size");
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) {
+      const uint32_t v = ((const GAS uint32_t*)p)[i];
+      __builtin_memcpy((char*)&r + 4 * i, &v, 4);
+    }
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void stg(T* p, const T& val) {
+  if constexpr (sizeof(T) == 16) {
+    v4u_ v;
+    __builtin_memcpy(&v, &val, 16);
+    *(GAS v4u_*)p = v;
+  } else {
+    static_assert(sizeof(T) == 4, "stg size");
+    uint32_t v;
+    __builtin_memcpy(&v, &val, 4);
+    *(GAS uint32_t*)p = v;
+  }
+}
+
+// device-coherent (sc1) scalar accesses for data shared between workers
+__device__ __forceinline__ float ldc(const float* p) {
+  return __hip_atomic_load((const GAS float*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ldc_u(const uint32_t* p) {
+  return __hip_atomic_load((const GAS uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ldc_i(const int32_t* p) {
+  return __hip_atomic_load((const GAS int32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(float* p, float v) {
+  __hip_atomic_store((GAS float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc_u(uint32_t* p, uint32_t v) {
+  __hip_atomic_store((GAS uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc_i(int32_t* p, int32_t v) {
+  __hip_atomic_store((GAS int32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 4 consecutive fp32 activations, device-coherent (sc1) 16-byte load.
+__device__ __forceinline__ v4f ldc4(const float* base, uint32_t elem) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, elem * 4u, 0, 16 /* sc1 */);
+}
+
+// 16 bytes of a streamed, read-once weight row (non-temporal).
+__device__ __forceinline__ uint4 ldw(const uint16_t* p) {
+  v4u v = __builtin_nontemporal_load((const GAS v4u*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return ldg((const uint4*)p); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// larger value wins; equal values: lower index wins
+__device__ __forceinline__ void amax_merge(float& v, int32_t& i, float v2, int32_t i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+__device__ __forceinline__ void wave_amax(float& v, int32_t& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o, 64);
+    int32_t i2 = __shfl_xor(i, o, 64);
+    amax_merge(v, i, v2, i2);
+  }
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// events
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32_t target, uint32_t task, Misc* m) {
+  if (ev == EV_NONE) return true;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const EventRec e = ldg(P.events + ev);
+    const uint32_t* f = P.flags + e.slot0;
+    uint32_t polls = 0;
+    int ok = 0;
+    for (;;) {
+      bool mine = true;
+      uint32_t seen = target;
+      for (uint32_t i = lane; i < e.fanin; i += 64) {
+        uint32_t v = ldc_u(f + i);
+        if ((int32_t)(v - target) < 0) {
+          mine = false;
+          seen = v;
+        }
+      }
+      if (__all(mine)) {
+        ok = 1;
+        break;
+      }
+      ++polls;
+      if ((polls & 63u) == 0) {
+        if (ldc_u(P.status + ST_ABORT)) break;
+        if (polls >= P.watchdog) {
+          uint32_t zero = 0u;
+          if (!mine && __hip_atomic_compare_exchange_strong((GAS uint32_t*)(P.status + ST_CODE), &zero, ERR_WATCHDOG,
+                                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            stc_u(P.status + ST_CU, blockIdx.x);
+            stc_u(P.status + ST_TASK, task);
+            stc_u(P.status + ST_EVENT, ev);
+            stc_u(P.status + ST_SEEN, seen);
+            stc_u(P.status + ST_WANT, target);
+          }
+          if (lane == 0) stc_u(P.status + ST_ABORT, 1u);
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) m->flag = ok;
+  }
+  __syncthreads();
+  return m->flag != 0;
+}
+
+__device__ __forceinline__ void signal_event(const KParams& P, uint32_t ev, uint32_t slot, uint32_t val) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent stores have completed
+  __syncthreads();                // ... and every other wave's
+  if (threadIdx.x == 0) stc_u(P.flags + ldg(P.events + ev).slot0 + slot, val);
+}
+
+// ---------------------------------------------------------------------------
+// tokens: argmax over the LM tiles' partial maxima (lowest index on ties)
+// ---------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float bv[NB];
+  int32_t bi[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    bv[b] = -INFINITY;
+    bi[b] = 0x7fffffff;
+  }
+  for (int i = threadIdx.x; i < P.n_lm; i += NT) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const LmPart* lp = P.lm_part + (size_t)b * P.n_lm + i;
+      float v = ldc(&lp->val);
+      int32_t ix = ldc_i(&lp->idx);
+      amax_merge(bv[b], bi[b], v, ix);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    wave_amax(bv[b], bi[b]);
+    if (lane == 0) {
+      m->wval[w][b] = bv[b];
+      m->widx[w][b] = bi[b];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < NB) {
+    const int b = threadIdx.x;
+    float v = m->wval[0][b];
+    int32_t ix = m->widx[0][b];
+    for (int ww = 1; ww < NW; ++ww) amax_merge(v, ix, m->wval[ww][b], m->widx[ww][b]);
+    m->tok[b] = (ix >= 0 && ix < P.V) ? ix : 0;  // all-NaN logits cannot index outside the vocabulary
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// GEMV task: rows [a0, a1) of one weight matrix against B activation vectors
+// ---------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, int s, bool mega, char* lds) {
+  const int op = (int)t.op, l = (int)t.layer;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  float* xs = (float*)lds;
+  float* red = (float*)(lds + (size_t)P.xs_floats * 4);
+  Misc* m = (Misc*)(lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+  const LayerW LW = ldg(P.layers + (op == OP_LM ? 0 : l));
+
+  const uint16_t* W0;
+  const uint16_t* W1 = nullptr;
+  const uint16_t* gamma = nullptr;
+  int K, RU = 1;
+  switch (op) {
+    case OP_QKV: W0 = LW.wqkv; K = P.H; gamma = LW.attn_norm; break;
+    case OP_WO: W0 = LW.wo; K = P.QD; break;
+    case OP_GU: W0 = LW.wg; W1 = LW.wu; K = P.H; RU = 2; gamma = LW.ffn_norm; break;
+    case OP_DOWN: W0 = LW.wd; K = P.F; break;
+    default: W0 = P.lm_head; K = P.H; gamma = P.final_norm; break;
+  }
+  const bool norm = gamma != nullptr;
+  const bool embed_src = (op == OP_QKV && l == 0);
+  const int u0 = (int)t.a0, nu = (int)t.a1 - (int)t.a0;
+  const int my_units = nu > w ? (nu - w + NW - 1) / NW : 0;
+  const int my_rows = my_units * RU;
+  const int kc = min(K, (P.xs_floats / NB) / 512 * 512);
+  const int nsl = (K + kc - 1) / kc;
+
+  auto rowptr = [&](int r) -> const uint16_t* {
+    const int ui = RU == 2 ? (r >> 1) : r;
+    const uint16_t* base = (RU == 2 && (r & 1)) ? W1 : W0;
+    return base + (size_t)(u0 + w + NW * ui) * K;
+  };
+
+  // pipeline state for one slice
+  uint4 buf[DEPTH][CG];
+  int ir = 0, ig = 0, cr = 0, cgi = 0;
+  int k0 = 0, nch8 = 0, GPR = 1;
+  auto slice_setup = [&](int sl) {
+    k0 = sl * kc;
+    const int ks = min(kc, K - k0);
+    nch8 = ks / 8;
+    const int nch = (nch8 + 63) / 64;
+    GPR = (nch + CG - 1) / CG;
+    ir = ig = cr = cgi = 0;
+  };
+  // Loads are never predicated: lanes past the row end re-read the row's last
+  // chunk (a clamped, in-bounds address) and are zeroed when consumed, so the
+  // steady-state loop is branch-free and its waits count outstanding loads.
+  auto issue_nocheck = [&](uint4 (&b)[CG]) {
+    const uint16_t* p = rowptr(ir) + k0;
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const int j = min((ig * CG + c) * 64 + lane, nch8 - 1);
+      b[c] = ldw(p + (size_t)j * 8);
+    }
+    if (++ig == GPR) {
+      ig = 0;
+      ++ir;
+    }
+  };
+  auto issue = [&](uint4 (&b)[CG]) {
+    if (ir < my_rows) issue_nocheck(b);
+  };
+
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  int sl_cur = 0;
+  auto consume = [&](const uint4 (&bw)[CG]) {
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const int jr = (cgi * CG + c) * 64 + lane;
+      const bool ok = jr < nch8;
+      const int j = ok ? jr : nch8 - 1;
+      const uint32_t wv[4] = {ok ? bw[c].x : 0u, ok ? bw[c].y : 0u, ok ? bw[c].z : 0u, ok ? bw[c].w : 0u};
+      float wf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wf[2 * e] = bf_lo(wv[e]);
+        wf[2 * e + 1] = bf_hi(wv[e]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const v4f x0 = *(const v4f*)(xs + (size_t)b * kc + j * 8);
+        const v4f x1 = *(const v4f*)(xs + (size_t)b * kc + j * 8 + 4);
+        float a = acc[b];
+        a = fmaf(wf[0], x0.x, a);
+        a = fmaf(wf[1], x0.y, a);
+        a = fmaf(wf[2], x0.z, a);
+        a = fmaf(wf[3], x0.w, a);
+        a = fmaf(wf[4], x1.x, a);
+        a = fmaf(wf[5], x1.y, a);
+        a = fmaf(wf[6], x1.z, a);
+        a = fmaf(wf[7], x1.w, a);
+        acc[b] = a;
+      }
+    }
+    if (++cgi == GPR) {
+      cgi = 0;
+      const int ui = RU == 2 ? (cr >> 1) : cr;
+      const int rl = (w + NW * ui) * RU + (RU == 2 ? (cr & 1) : 0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float v = wave_sum(acc[b]);
+        if (lane == 0) red[rl * NB + b] = sl_cur == 0 ? v : red[rl * NB + b] + v;
+        acc[b] = 0.f;
+      }
+      ++cr;
+    }
+  };
+
+  // Weights do not depend on the event: start streaming before waiting.
+  slice_setup(0);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(buf[d]);
+
+  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m)) return false;
+
+  // layer-0 Q/K/V reads the embedding of this step's token
+  if (embed_src) {
+    if (P.force_tok) {
+      if (tid < NB) m->tok[tid] = ldg(P.force_tok + (size_t)s * P.B + tid);
+      __syncthreads();
+    } else if (s == 0) {
+      if (tid < NB) {
+        const int32_t tk = ldg(P.pending + tid);
+        m->tok[tid] = (tk >= 0 && tk < P.V) ? tk : 0;
+      }
+      __syncthreads();
+    } else {
+      reduce_tokens<NB>(P, m);
+      if (t.tile == 0 && P.out_tokens && tid < NB) stg(P.out_tokens + (size_t)(s - 1) * P.B + tid, m->tok[tid]);
+    }
+    // this tile's share of x = embedding (read by the O-projection residual)
+    const int h0 = (int)((int64_t)t.tile * P.H / P.n_qkv), h1 = (int)((int64_t)(t.tile + 1) * P.H / P.n_qkv);
+    for (int i = h0 + tid; i < h1; i += NT)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) stc(P.x + (size_t)b * P.H + i, bf1(ldg(P.embed + (size_t)m->tok[b] * P.H + i)));
+  }
+
+  for (int sl = 0; sl < nsl; ++sl) {
+    sl_cur = sl;
+    if (sl > 0) {
+      __syncthreads();  // every wave is done with the previous slice of xs
+      slice_setup(sl);
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) issue(buf[d]);
+    }
+    // ---- stage activations of this slice into LDS (x * gamma); norm scale on slice 0
+    {
+      const int ks = min(kc, K - k0);
+      float ss[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+      const int e_lo = (sl == 0 && norm) ? 0 : k0, e_hi = (sl == 0 && norm) ? K : k0 + ks;
+      for (int base = e_lo + tid * 4; base < e_hi; base += NT * 4 * 8) {
+        v4f v[8][NB];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = base + u * NT * 4;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            if (e < e_hi) {
+              if (embed_src) {
+                const uint16_t* er = P.embed + (size_t)m->tok[b] * P.H + e;
+                const uint2 q = ldg((const uint2*)er);
+                v[u][b] = v4f{bf_lo(q.x), bf_hi(q.x), bf_lo(q.y), bf_hi(q.y)};
+              } else {
+                const float* src = op == OP_WO ? P.o + (size_t)b * P.QD : op == OP_DOWN ? P.a + (size_t)b * P.F : P.x + (size_t)b * P.H;
+                v[u][b] = ldc4(src, (uint32_t)e);
+              }
+            } else {
+              v[u][b] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = base + u * NT * 4;
+          if (e < e_hi) {
+            float g4[4] = {1.f, 1.f, 1.f, 1.f};
+            if (norm) {
+              const uint2 gq = ldg((const uint2*)(gamma + e));
+              g4[0] = bf_lo(gq.x);
+              g4[1] = bf_hi(gq.x);
+              g4[2] = bf_lo(gq.y);
+              g4[3] = bf_hi(gq.y);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const v4f x = v[u][b];
+              if (norm && sl == 0) ss[b] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+              if (e >= k0 && e < k0 + ks)
+                *(v4f*)(xs + (size_t)b * kc + (e - k0)) = v4f{x.x * g4[0], x.y * g4[1], x.z * g4[2], x.w * g4[3]};
+            }
+          }
+        }
+      }
+      if (norm && sl == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float v = wave_sum(ss[b]);
+          if (lane == 0) m->wred[w][b] = v;
+        }
+        __syncthreads();
+        if (tid < NB) {
+          float tot = 0.f;
+          for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][tid];
+          m->r[tid] = 1.0f / sqrtf(tot / (float)K + P.eps);
+        }
+      }
+      __syncthreads();
+    }
+    // ---- stream this slice's weight rows through the pipeline
+    // Nothing is outstanding here (staging waited for its loads, which were
+    // issued after the prefetch); saying so explicitly gives the compiler an
+    // exact count to start from, so the loop below waits only for the oldest
+    // group instead of draining every load.
+    __builtin_amdgcn_s_waitcnt(0);
+    const int total = my_rows * GPR;
+    int g = 0;
+    for (; g + 2 * DEPTH <= total; g += DEPTH) {  // steady state: DEPTH groups always in flight
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        consume(buf[d]);
+        issue_nocheck(buf[d]);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {  // drain
+      if (g + d < total) {
+        consume(buf[d]);
+        if (g + d + DEPTH < total) issue_nocheck(buf[d]);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (g + DEPTH + d < total) consume(buf[d]);
+  }
+  __syncthreads();
+
+  // ---- epilogue per operator
+  if (op == OP_QKV) {
+    for (int i = tid; i < nu * NB; i += NT) {
+      const int ul = i / NB, b = i - ul * NB;
+      stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, red[ul * NB + b] * m->r[b]);
+    }
+  } else if (op == OP_WO || op == OP_DOWN) {
+    for (int i = tid; i < nu * NB; i += NT) {
+      const int ul = i / NB, b = i - ul * NB;
+      float* xp = P.x + (size_t)b * P.H + u0 + ul;
+      stc(xp, ldc(xp) + red[ul * NB + b]);
+    }
+  } else if (op == OP_GU) {
+    for (int i = tid; i < nu * NB; i += NT) {
+      const int ul = i / NB, b = i - ul * NB;
+      const float gt = red[(ul * 2) * NB + b] * m->r[b];
+      const float up = red[(ul * 2 + 1) * NB + b] * m->r[b];
+      stc(P.a + (size_t)b * P.F + u0 + ul, silu(gt) * up);
+    }
+  } else {  // OP_LM
+    float bv[NB];
+    int32_t bi[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      bv[b] = -INFINITY;
+      bi[b] = 0x7fffffff;
+    }
+    for (int ul = tid; ul < nu; ul += NT) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float logit = red[ul * NB + b] * m->r[b];
+        if (P.out_logits) stg(P.out_logits + ((size_t)s * P.B + b) * P.V + u0 + ul, logit);
+        amax_merge(bv[b], bi[b], logit, u0 + ul);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      wave_amax(bv[b], bi[b]);
+      if (lane == 0) {
+        m->wval[w][b] = bv[b];
+        m->widx[w][b] = bi[b];
+      }
+    }
+    __syncthreads();
+    if (tid < NB) {
+      float v = m->wval[0][tid];
+      int32_t ix = m->widx[0][tid];
+      for (int ww = 1; ww < NW; ++ww) amax_merge(v, ix, m->wval[ww][tid], m->widx[ww][tid]);
+      LmPart* lp = P.lm_part + (size_t)tid * P.n_lm + t.tile;
+      stc(&lp->val, v);
+      stc_i(&lp->idx, ix);
+    }
+  }
+  if (mega) signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+  else __syncthreads();
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Attention task (sequence b, KV head g, split sp): QK-norm + RoPE of the G
+// query heads (and of k when this split holds the current position, which it
+// then appends to the cache), scores over the split's positions, and the
+// split's softmax partial (max m, sum l, unnormalised P.V).  The last split
+// of (b, g) to finish merges all partials in ascending split order:
+//   M = max_s m_s,  o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s.
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, int s, bool mega, char* lds) {
+  const int Hkv = P.Hkv, D = P.D, S = P.S;
+  const int bg = (int)t.a0, b = bg / Hkv, g = bg - b * Hkv, sp = (int)t.a1, l = (int)t.layer;
+  const int pos = P.pos0 + s, N = pos + 1;
+  const int n_act = (N + S - 1) / S;
+  if (sp >= n_act) return true;  // split beyond the current length: nothing to do, nothing to notify
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j0 = sp * S, j1 = min(j0 + S, N);
+  const bool has_cur = (j1 == N);
+  const int jc = has_cur ? pos : j1;  // cached positions [j0, jc)
+  const int LPP = D / 8, lp = tid % LPP, po = tid / LPP, PPB = NT / LPP;
+  const size_t head = ((size_t)(l * P.B + b) * Hkv + g) * P.max_seq;
+  uint16_t* Kh = P.kc + head * D;
+  uint16_t* Vh = P.vc + head * D;
+
+  // cached K/V do not depend on this step: load them before waiting
+  uint4 kr[ATT_MAXL], vr[ATT_MAXL];
+#pragma unroll
+  for (int i = 0; i < ATT_MAXL; ++i) {
+    const int j = j0 + po + i * PPB;
+    if (i * PPB < S && po + i * PPB < S && j < jc) {
+      kr[i] = ld16(Kh + (size_t)j * D + lp * 8);
+      vr[i] = ld16(Vh + (size_t)j * D + lp * 8);
+    } else {
+      kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  float* fl = (float*)lds;
+  Misc* m = (Misc*)(lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m)) return false;
+
+  float* raw = fl;                       // [(G+2) D]: q heads, k, v
+  float* qrot = raw + (G + 2) * D;       // [G D]
+  uint16_t* kcur = (uint16_t*)(qrot + G * D);  // [D]
+  uint16_t* vcur = kcur + D;                   // [D]
+  float* sc = (float*)(vcur + D);              // [G S]
+  float* accw = sc + G * S;                    // [NW G D]
+
+  const float* src = P.qkv + (size_t)b * P.QKVR + (size_t)g * P.RG;
+  for (int i = tid * 4; i < (G + 2) * D; i += NT * 4) *(v4f*)(raw + i) = ldc4(src, (uint32_t)i);
+  __syncthreads();
+  const int nh = G + (has_cur ? 1 : 0);  // heads to rotate (q heads, then k)
+  if (P.qk_norm) {
+    for (int h = w; h < nh; h += NW) {
+      float ss = 0.f;
+      for (int d = lane; d < D; d += 64) ss += raw[h * D + d] * raw[h * D + d];
+      ss = wave_sum(ss);
+      if (lane == 0) m->hr[h] = 1.0f / sqrtf(ss / (float)D + P.eps);
+    }
+    __syncthreads();
+  }
+  const int half = D / 2;
+  const float* cs = P.rope_cos + (size_t)pos * half;
+  const float* sn = P.rope_sin + (size_t)pos * half;
+  const LayerW LW = ldg(P.layers + l);
+  for (int i = tid; i < nh * half; i += NT) {
+    const int h = i / half, k = i - h * half;
+    float x0 = raw[h * D + k], x1 = raw[h * D + k + half];
+    if (P.qk_norm) {
+      const uint16_t* gm = h < G ? LW.q_norm : LW.k_norm;
+      x0 = (x0 * m->hr[h]) * bf1(ldg(gm + k));
+      x1 = (x1 * m->hr[h]) * bf1(ldg(gm + k + half));
+    }
+    const float c = ldg(cs + k), sv = ldg(sn + k);
+    const float y0 = x0 * c - x1 * sv, y1 = x0 * sv + x1 * c;
+    if (h < G) {
+      qrot[h * D + k] = y0;
+      qrot[h * D + k + half] = y1;
+    } else {
+      kcur[k] = f2bf(y0);
+      kcur[k + half] = f2bf(y1);
+    }
+  }
+  if (has_cur)
+    for (int i = tid; i < D; i += NT) vcur[i] = f2bf(raw[(G + 1) * D + i]);
+  __syncthreads();
+  if (has_cur && tid < LPP) {  // append this position's K/V to the cache
+    stg((uint4*)(Kh + (size_t)pos * D + tid * 8), *(const uint4*)(kcur + tid * 8));
+    stg((uint4*)(Vh + (size_t)pos * D + tid * 8), *(const uint4*)(vcur + tid * 8));
+  }
+
+  // ---- scores t_j = (q_h . k_j) / sqrt(D)
+  float q[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[h][e] = qrot[h * D + lp * 8 + e];
+#pragma unroll
+  for (int i = 0; i < ATT_MAXL; ++i) {
+    if (i * PPB < S) {
+      const int jr = po + i * PPB, j = j0 + jr;
+      const uint4 kk = (has_cur && j == pos) ? *(const uint4*)(kcur + lp * 8) : kr[i];
+      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+      float part[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a = fmaf(q[h][2 * e], bf_lo(kw[e]), a);
+          a = fmaf(q[h][2 * e + 1], bf_hi(kw[e]), a);
+        }
+        part[h] = a;
+      }
+      for (int o = LPP / 2; o > 0; o >>= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], o, 64);
+      if (jr < S && j < j1 && lp == 0)
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h * S + jr] = part[h] * P.attn_scale;
+    }
+  }
+  __syncthreads();
+  // ---- split softmax statistics per head
+  const int n = j1 - j0;
+  for (int h = w; h < G; h += NW) {
+    float mx = -INFINITY;
+    for (int jr = lane; jr < n; jr += 64) mx = fmaxf(mx, sc[h * S + jr]);
+    mx = wave_max(mx);
+    float ls = 0.f;
+    for (int jr = lane; jr < n; jr += 64) {
+      const float p = expf(sc[h * S + jr] - mx);
+      sc[h * S + jr] = p;
+      ls += p;
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) {
+      m->ml[h][0] = mx;
+      m->ml[h][1] = ls;
+    }
+  }
+  __syncthreads();
+  // ---- unnormalised P.V
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < ATT_MAXL; ++i) {
+    const int jr = po + i * PPB, j = j0 + jr;
+    if (i * PPB < S && jr < S && j < j1) {
+      const uint4 vv = (has_cur && j == pos) ? *(const uint4*)(vcur + lp * 8) : vr[i];
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = sc[h * S + jr];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[h][2 * e] = fmaf(p, bf_lo(vw[e]), acc[h][2 * e]);
+          acc[h][2 * e + 1] = fmaf(p, bf_hi(vw[e]), acc[h][2 * e + 1]);
+        }
+      }
+    }
+  }
+  for (int o = LPP; o < 64; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+  if (lane < LPP)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) accw[(w * G + h) * D + lp * 8 + e] = acc[h][e];
+  __syncthreads();
+  const size_t pbase = ((size_t)bg * P.NS + sp) * G;
+  for (int i = tid; i < G * D; i += NT) {
+    float v = 0.f;
+    for (int ww = 0; ww < NW; ++ww) v += accw[ww * G * D + i];
+    stc(P.part_acc + pbase * D + i, v);
+  }
+  if (tid < G) {
+    stc(P.part_ml + (pbase + tid) * 2, m->ml[tid][0]);
+    stc(P.part_ml + (pbase + tid) * 2 + 1, m->ml[tid][1]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // ---- last arriver merges
+  if (n_act > 1) {
+    if (tid == 0) {
+      uint32_t* tk = P.tickets + ((size_t)l * P.B + b) * Hkv + g;
+      const uint32_t old = __hip_atomic_fetch_add((GAS uint32_t*)tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == (uint32_t)(n_act - 1);
+      if (last) stc_u(tk, 0u);
+      m->flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (!m->flag) return true;
+  }
+  const size_t b0 = (size_t)bg * P.NS;
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < n_act; ++s2) M = fmaxf(M, ldc(P.part_ml + ((b0 + s2) * G + h) * 2));
+    float num = 0.f, den = 0.f;
+    for (int s2 = 0; s2 < n_act; ++s2) {
+      const size_t pi = (b0 + s2) * G + h;
+      const float e = expf(ldc(P.part_ml + pi * 2) - M);
+      num += e * ldc(P.part_acc + pi * D + (i - h * D));
+      den += e * ldc(P.part_ml + pi * 2 + 1);
+    }
+    stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, num / den);
+  }
+  if (mega) signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+  else __syncthreads();
+  return true;
+}
+
+template <int NB>
+__device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int s, bool mega, char* lds) {
+  if (t.op == OP_ATTN) {
+    switch (P.G) {
+      case 1: return task_attn<1>(P, t, s, mega, lds);
+      case 2: return task_attn<2>(P, t, s, mega, lds);
+      default: return task_attn<4>(P, t, s, mega, lds);
+    }
+  }
+  return task_gemv<NB>(P, t, s, mega, lds);
+}
+
+// The megakernel: one launch runs n_steps decode steps of the whole model.
+template <int NB>
+__global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
+  char* lds = g_lds;
+  const uint32_t off = ldg(P.list_off + blockIdx.x), n = ldg(P.list_len + blockIdx.x);
+  for (int s = 0; s < P.n_steps; ++s) {
+    for (uint32_t i = 0; i < n; ++i) {
+      const TaskRec t = ldg(P.tasks + ldg(P.cu_tasks + off + i));
+      if (!run_task<NB>(P, t, s, true, lds)) return;
+    }
+  }
+  if (blockIdx.x == 0) {
+    // last step's token: wait for every LM tile of the final step
+    Misc* m = (Misc*)(lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+    const uint32_t ev_lm = (uint32_t)(P.L * (P.Hkv + 4));
+    if (!wait_event(P, ev_lm, P.epoch + (uint32_t)P.n_steps, 0xffffffffu, m)) return;
+    reduce_tokens<NB>(P, m);
+    if (threadIdx.x < NB) {
+      if (P.out_tokens) stg(P.out_tokens + (size_t)(P.n_steps - 1) * P.B + threadIdx.x, m->tok[threadIdx.x]);
+      stg(P.pending + threadIdx.x, m->tok[threadIdx.x]);
+    }
+  }
+}
+
+// Ablation: one launch per operator instance, same tasks on the same workers.
+template <int NB>
+__global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
+  char* lds = g_lds;
+  for (int i = P.op_first; i < P.op_first + P.op_count; ++i)
+    if (ldg(P.task_cu + i) == blockIdx.x) run_task<NB>(P, ldg(P.tasks + i), P.step, false, lds);
+}
+
+template <int NB>
+__global__ __launch_bounds__(NT, 1) void mk_finish_tokens(KParams P) {
+  Misc* m = (Misc*)(g_lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+  reduce_tokens<NB>(P, m);
+  if (threadIdx.x < NB) {
+    if (P.out_tokens) stg(P.out_tokens + (size_t)P.step * P.B + threadIdx.x, m->tok[threadIdx.x]);
+    stg(P.pending + threadIdx.x, m->tok[threadIdx.x]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch helpers
+// ---------------------------------------------------------------------------
+size_t lds_bytes(const KParams& P) { return (size_t)P.xs_floats * 4 + RED_FLOATS * 4 + MISC_BYTES; }
+
+template <int NB>
+static hipError_t launch_nb(int kind, const KParams& P, hipStream_t st) {
+  const size_t sh = lds_bytes(P);
+  KParams Q = P;
+  if (kind == 0) {
+    void* args[] = {&Q};
+    return hipLaunchCooperativeKernel((const void*)mk_persistent<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
+  } else if (kind == 1) {
+    hipLaunchKernelGGL(mk_per_op<NB>, dim3(P.n_workers), dim3(NT), sh, st, Q);
+  } else {
+    hipLaunchKernelGGL(mk_finish_tokens<NB>, dim3(1), dim3(NT), sh, st, Q);
+  }
+  return hipGetLastError();
+}
+
+template <int NB>
+static hipError_t set_attrs() {
+  const int sh = 163840;
+  hipError_t e = hipFuncSetAttribute((const void*)mk_persistent<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)mk_per_op<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)mk_finish_tokens<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+}
+
+hipError_t prepare_kernels(int B) {
+  switch (B) {
+    case 1: return set_attrs<1>();
+    case 2: return set_attrs<2>();
+    case 4: return set_attrs<4>();
+    case 8: return set_attrs<8>();
+    default: return set_attrs<16>();
+  }
+}
+
+// kind: 0 persistent (cooperative), 1 one operator instance, 2 final token
+hipError_t launch(int kind, const KParams& P, hipStream_t st) {
+  switch (P.B) {
+    case 1: return launch_nb<1>(kind, P, st);
+    case 2: return launch_nb<2>(kind, P, st);
+    case 4: return launch_nb<4>(kind, P, st);
+    case 8: return launch_nb<8>(kind, P, st);
+    default: return launch_nb<16>(kind, P, st);
+  }
+}
+
+int max_coresident_workers(int B, size_t lds) {
+  int per_cu = 0;
+  const void* f = (const void*)mk_persistent<1>;
+  switch (B) {
+    case 2: f = (const void*)mk_persistent<2>; break;
+    case 4: f = (const void*)mk_persistent<4>; break;
+    case 8: f = (const void*)mk_persistent<8>; break;
+    case 16: f = (const void*)mk_persistent<16>; break;
+    default: break;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, NT, lds) != hipSuccess) return -1;
+  return per_cu;
+}
+
+}  // namespace mk

@@ -1,0 +1,113 @@
+// mk_internal.h -- records shared by the host builder/runtime and the HIP kernels.
+//
+// Vocabulary follows the MPK digest (fr.news.hada.io, "Part 1. Compilateur"):
+// a *task* is a unit of work given to one compute unit, an *event* is a
+// synchronisation point between tasks, and a task waits on at most one event
+// and notifies at most one.  An event fires when every producer slot holds the
+// current step's value ("Exécution pilotée par événements": counters that
+// reach a threshold); here each producer owns one 32-bit slot, so firing
+// needs no atomic read-modify-write on a shared counter.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+enum Op : uint32_t {
+  OP_QKV = 1,   // norm + fused Q/K/V projection rows (one KV-head group per tile)
+  OP_ATTN = 2,  // QK-norm + RoPE + KV append + split-KV attention partial (+ merge)
+  OP_WO = 3,    // O-projection rows + residual
+  OP_GU = 4,    // norm + gate/up row pairs + SwiGLU
+  OP_DOWN = 5,  // down-projection rows + residual
+  OP_LM = 6,    // final norm + LM-head rows + per-tile argmax
+};
+
+constexpr uint32_t EV_NONE = 0xffffffffu;
+
+// One task; 32 bytes on the device.
+struct TaskRec {
+  uint32_t op;        // Op
+  uint32_t layer;     // decoder layer (0 for OP_LM)
+  uint32_t tile;      // index of the task within its operator
+  uint32_t a0, a1;    // GEMV: unit range [a0, a1); ATTN: a0 = b*Hkv + g, a1 = split index
+  uint32_t wait_ev;   // event waited on (EV_NONE: none)
+  uint32_t wait_lag;  // 1: the event belongs to the previous decode step
+  uint32_t sig_ev;    // event notified (slot sig_slot)
+  uint32_t sig_slot;
+  uint32_t pad[3];
+};
+static_assert(sizeof(TaskRec) == 48, "TaskRec layout");
+
+struct EventRec {
+  uint32_t fanin;  // number of producer slots
+  uint32_t slot0;  // first slot in the flag array
+};
+
+struct LayerW {
+  const uint16_t* wqkv;  // [(Hq + 2 Hkv) D, H], rows grouped per KV head: G q heads, k, v
+  const uint16_t* wo;    // [H, Hq D]
+  const uint16_t* wg;    // [F, H]
+  const uint16_t* wu;    // [F, H]
+  const uint16_t* wd;    // [H, F]
+  const uint16_t* attn_norm;  // [H]
+  const uint16_t* ffn_norm;   // [H]
+  const uint16_t* q_norm;     // [D] or null
+  const uint16_t* k_norm;     // [D] or null
+};
+
+struct LmPart {
+  float val;
+  int32_t idx;
+};
+
+// status[0]: abort flag; status[1..7]: first error record
+enum : uint32_t { ST_ABORT = 0, ST_CODE = 1, ST_CU = 2, ST_TASK = 3, ST_EVENT = 4, ST_SEEN = 5, ST_WANT = 6 };
+constexpr uint32_t ERR_WATCHDOG = 1;
+
+struct KParams {
+  // model shape
+  int32_t L, H, Hq, Hkv, D, F, V, G, RG, QKVR, QD, B, max_seq, S, NS, qk_norm;
+  float eps, attn_scale;
+  // tiling
+  int32_t n_workers, n_qkv, n_wo, n_gu, n_down, n_lm;
+  int32_t xs_floats;  // activation staging capacity in LDS (floats)
+  // weights
+  const LayerW* layers;
+  const uint16_t* embed;
+  const uint16_t* final_norm;
+  const uint16_t* lm_head;
+  const float* rope_cos;  // [max_seq][D/2]
+  const float* rope_sin;
+  // KV cache [L][B][Hkv][max_seq][D] bf16
+  uint16_t* kc;
+  uint16_t* vc;
+  // activations (fp32)
+  float* x;         // [B][H]
+  float* qkv;       // [B][QKVR]
+  float* o;         // [B][QD]
+  float* a;         // [B][F]
+  float* part_ml;   // [B][Hkv][NS][G][2]
+  float* part_acc;  // [B][Hkv][NS][G][D]
+  uint32_t* tickets;  // [L][B][Hkv]
+  LmPart* lm_part;    // [B][n_lm]
+  // tokens
+  int32_t* pending;           // [B]
+  int32_t* out_tokens;        // [n_steps][B] or null
+  float* out_logits;          // [n_steps][B][V] or null
+  const int32_t* force_tok;   // [n_steps][B] or null (prefill)
+  // graph
+  uint32_t* flags;
+  const EventRec* events;
+  const TaskRec* tasks;
+  const uint32_t* task_cu;
+  const uint32_t* list_off;
+  const uint32_t* list_len;
+  const uint32_t* cu_tasks;
+  uint32_t* status;
+  // run
+  int32_t pos0, n_steps, with_lm;
+  uint32_t epoch, watchdog;
+  // per-operator launch
+  int32_t op_first, op_count, step;
+};
+
+}  // namespace mk

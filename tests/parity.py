@@ -1,0 +1,50 @@
+"""Shared driver for GPU-vs-oracle parity checks (used by the gpu tests and smoke)."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import pyoracle as po
+from persistent_decode_megakernel_02_amd import synth
+
+MAX_ABS = 3e-2       # per-step max |logit error|
+MEAN_ABS = 3e-3      # per-step mean |logit error|
+STRICT_STEPS = 32    # greedy tokens must agree on the first 32 steps
+GAP = 0.05           # later divergence allowed only where the oracle's top-2 gap is below this
+
+
+def top2_gap(x: np.ndarray) -> float:
+    s = np.sort(x)
+    return float(s[-1] - s[-2])
+
+
+def oracle_for(shape, weights, max_seq, n_seq, n_threads=1):
+    w16 = [synth.bf16_bits(t) for _, t in weights]
+    return po.Oracle(shape, w16, max_seq=max_seq, n_seq=n_seq, n_threads=n_threads)
+
+
+def compare_free_running(orc: "po.Oracle", seq: int, first_token: int, gpu_tokens: np.ndarray,
+                         gpu_logits: np.ndarray | None, n_check: int | None = None, label: str = ""):
+    """Oracle decodes on its own from first_token; compare step by step.
+
+    Returns the number of steps compared.  Raises AssertionError with details on a violation.
+    """
+    n = len(gpu_tokens) if n_check is None else min(n_check, len(gpu_tokens))
+    tok = int(first_token)
+    for i in range(n):
+        lo = orc.step(seq, tok)
+        if gpu_logits is not None:
+            d = np.abs(gpu_logits[i].astype(np.float64) - lo.astype(np.float64))
+            assert np.all(np.isfinite(gpu_logits[i])), f"{label} step {i}: non-finite GPU logits"
+            assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, \
+                f"{label} step {i}: max|d|={d.max():.3e} mean|d|={d.mean():.3e}"
+        ot = po.argmax(lo)
+        gt = int(gpu_tokens[i])
+        if gpu_logits is not None:
+            assert gt == int(np.argmax(gpu_logits[i])), f"{label} step {i}: token is not the argmax of its logits"
+        if gt != ot:
+            gap = top2_gap(lo)
+            assert i >= STRICT_STEPS and gap < GAP, \
+                f"{label} step {i}: GPU token {gt} != oracle {ot} (oracle top-2 gap {gap:.4f})"
+            return i + 1
+        tok = ot
+    return n
