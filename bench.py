@@ -1,0 +1,191 @@
+"""Benchmark: greedy decode of the Llama-3-8B-shaped decoder at batch 1.
+
+Workload (the MPK digest's decode benchmark, fr.news.hada.io, "Valeur clé de
+MPK"): a 39-token prompt, then 512 greedy decode steps, no speculative
+decoding, on random bf16 weights of the 8B shape.  A "step" is one decode
+step of the whole model (one token).  The timed region is ONE mk_decode
+call, i.e. one persistent-kernel launch covering --steps steps, with the
+prompt already prefilled and every input resident in HBM.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode ms/token (8B-shape, bs=1) + achieved HBM GB/s vs ~8 TB/s peak"
+PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(shape, batch, start_pos, n_steps):
+    """Weights streamed once per step plus, per sequence, K/V of every attended position read and one written."""
+    from persistent_decode_megakernel_02_amd.configs import kv_bytes_per_step, weight_bytes
+    w = weight_bytes(shape) * n_steps
+    kv = sum(kv_bytes_per_step(shape, start_pos + i + 1) for i in range(n_steps)) * batch
+    return w + kv
+
+
+def cpu_baseline(shape, host_weights, sample_layers=4):
+    """The oracle as it stands, single-threaded, on a bounded sample of the same shape.
+
+    One full 8B-shape step takes ~30 s on one core, so the sample is one decode step of two truncations of
+    the model that keep every matrix size: 0 layers (embedding, final norm, LM head) and `sample_layers`
+    layers.  Per-token time = t0 + n_layers * (t_k - t0) / k (every layer has the same shape; attention
+    over the workload's few hundred positions adds < 1% and is left out)."""
+    from dataclasses import replace
+
+    from persistent_decode_megakernel_02_amd import synth
+    from tests.parity import oracle_for
+
+    per_layer = len(synth.canonical_names(replace(shape, n_layers=1))) - 3
+
+    def one_step(n_layers):
+        sub = replace(shape, n_layers=n_layers)
+        ws = host_weights[:1 + n_layers * per_layer] + host_weights[-2:]
+        orc = oracle_for(sub, ws, max_seq=1, n_seq=1, n_threads=1)
+        t0 = time.perf_counter()
+        orc.step(0, 1)
+        dt = time.perf_counter() - t0
+        orc.close()
+        return dt
+
+    t0 = one_step(0)
+    tk = one_step(sample_layers)
+    return (t0 + shape.n_layers * (tk - t0) / sample_layers) * 1000.0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="llama8b_decode512")
+    ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--split", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding is a design, not a measured path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from persistent_decode_megakernel_02_amd import binding as mk
+    from persistent_decode_megakernel_02_amd import synth
+    from persistent_decode_megakernel_02_amd.configs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    shape, B = w.model, w.batch
+    K, W = args.steps, args.warmup
+    max_seq = w.start_pos + max(K, W)
+    torch.cuda.set_device(0)
+    log(f"workload {w.name}: generating weights on cuda:0")
+    weights = synth.make_weights(shape, seed=w.seed, device="cuda")
+    seqs = synth.make_sequences(shape, B, w.prompt_len, w.kv_prefill, seed=w.seed, device="cuda")
+    eng = mk.Engine(shape, batch=B, max_seq=max_seq, split=args.split)
+    eng.load_weights(weights)
+    host_weights = None
+    if not args.no_cpu:
+        log("copying weights to host for the CPU baseline")
+        host_weights = [(n, t.cpu()) for n, t in weights]
+    del weights
+    torch.cuda.empty_cache()
+
+    def restore():
+        if w.prompt_len > 0:
+            eng.prefill(seqs["prompts"].cpu().numpy())
+        else:
+            for b in range(B):
+                eng.load_kv(b, seqs["k"][b], seqs["v"][b], int(seqs["pending"][b]))
+
+    toks = torch.empty((max(K, W), B), dtype=torch.int32, device="cuda")
+    logits = torch.empty((max(K, W), B, shape.vocab), dtype=torch.float32, device="cuda")
+
+    def timed(mode, n):
+        eng.set_mode(mode)
+        restore()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        mk.mk_decode(eng.ctx, n, toks, logits)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1000.0
+        return e0.elapsed_time(e1), eng.last_ms(), wall
+
+    log(f"warmup: {W} steps (megakernel)")
+    if W > 0:
+        timed(mk.MK_MODE_MEGAKERNEL, W)
+    log(f"timed: {K} steps in one persistent launch")
+    ms_torch, ms_kernel, ms_wall = timed(mk.MK_MODE_MEGAKERNEL, K)
+    first_tokens = toks[: min(K, 8), 0].cpu().tolist()
+    mega_toks, mega_logits = toks[:K].clone(), logits[:K].clone()
+    ms_per_step = ms_torch / K
+    nbytes = algorithmic_bytes(shape, B, w.start_pos, K)
+    achieved = nbytes / (ms_kernel * 1e-3) / 1e9
+    roofline_ms = nbytes / K / (PEAK_GBS * 1e9) * 1e3
+    log(f"megakernel: {ms_per_step:.4f} ms/token ({ms_kernel:.2f} ms kernel, {ms_wall:.2f} ms wall), "
+        f"{achieved:.1f} GB/s, roofline {roofline_ms:.4f} ms/token, first tokens {first_tokens}")
+
+    ablation, identical = None, None
+    if not args.no_ablation:
+        log(f"ablation: {K} steps, one launch per operator")
+        a_torch, a_kernel, _ = timed(mk.MK_MODE_PER_OP, K)
+        ablation = a_torch / K
+        identical = bool(torch.equal(mega_toks, toks[:K]) and
+                         torch.equal(mega_logits.view(torch.int32), logits[:K].view(torch.int32)))
+        log(f"per-operator: {ablation:.4f} ms/token; bit-identical to the megakernel: {identical}")
+        eng.set_mode(mk.MK_MODE_MEGAKERNEL)
+
+    cpu = None
+    if host_weights is not None:
+        log("CPU baseline: oracle, 1 thread, one step of 0- and 4-layer truncations of the same shape")
+        eng.close()
+        ms_cpu = cpu_baseline(shape, host_weights, sample_layers=4)
+        cpu = {"value": round(ms_cpu, 1), "unit": "ms/token", "cores": 1, "kind": "oracle",
+               "sample": f"one decode step of 0-layer and 4-layer truncations of the {w.name} shape (same matrix "
+                         f"sizes), extrapolated linearly to {shape.n_layers} layers; single thread"}
+        log(f"CPU oracle: {ms_cpu:.1f} ms/token")
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 5),
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "prompt_tokens": w.prompt_len, "kv_prefill": w.kv_prefill,
+                   "decode_steps": K, "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
+                   "activations": "f32", "mode": "persistent megakernel, one launch"},
+        "tokens_per_s": round(B * 1000.0 / ms_per_step, 2),
+        "ablation_per_op_ms_per_step": round(ablation, 5) if ablation else None,
+        "ablation_bit_identical": identical,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "roofline_ms_per_step": round(roofline_ms, 5), "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
