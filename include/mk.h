@@ -149,6 +149,18 @@ int mk_reset(mk_ctx* ctx);
  * with HIP events on the context's stream around the launch(es). */
 int mk_last_decode_ms(mk_ctx* ctx, float* ms);
 
+/* Tracing (diagnostics).  mk_set_trace(ctx, step) makes the next megakernel
+ * mk_decode record, for decode step `step` of that call (0-based; -1
+ * disables), four device wall-clock stamps per task of every worker: task
+ * start, event satisfied, inputs staged (GEMV tasks), task end; 0 where a
+ * point was not reached (e.g. attention splits beyond the current length).
+ * mk_get_trace copies them as uint64 [n_workers][max_list][4] into out
+ * (host, *len words; with out == NULL only the sizes are returned) and
+ * reports the clock rate in kHz. */
+int mk_set_trace(mk_ctx* ctx, int step);
+int mk_get_trace(mk_ctx* ctx, uint64_t* out, size_t* len, int32_t* n_workers, int32_t* max_list,
+                 int32_t* clock_khz);
+
 /* Text of the last error on ctx (or of the last failed mk_create when ctx
  * is NULL).  Owned by the library; valid until the next call on ctx. */
 const char* mk_last_error(mk_ctx* ctx);

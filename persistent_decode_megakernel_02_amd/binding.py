@@ -39,7 +39,8 @@ class MkTensor(C.Structure):
 
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_load_kv", "mk_decode", "mk_set_mode", "mk_get_state",
-           "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_last_error", "mk_destroy"]
+           "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
+           "mk_last_error", "mk_destroy"]
 
 _lib = None
 
@@ -64,6 +65,9 @@ def lib():
         L.mk_build_graph.argtypes = [C.POINTER(MkModelCfg), C.c_int, vp, C.POINTER(sz)]
         L.mk_reset.argtypes = [vp]
         L.mk_last_decode_ms.argtypes = [vp, C.POINTER(C.c_float)]
+        L.mk_set_trace.argtypes = [vp, C.c_int]
+        L.mk_get_trace.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(sz), C.POINTER(i32), C.POINTER(i32),
+                                   C.POINTER(i32)]
         L.mk_last_error.argtypes = [vp]
         L.mk_last_error.restype = C.c_char_p
         L.mk_destroy.argtypes = [vp]
@@ -166,6 +170,20 @@ def mk_last_decode_ms(ctx) -> float:
     ms = C.c_float()
     _check(lib().mk_last_decode_ms(ctx, C.byref(ms)), ctx)
     return ms.value
+
+
+def mk_set_trace(ctx, step: int):
+    _check(lib().mk_set_trace(ctx, step), ctx)
+
+
+def mk_get_trace(ctx):
+    """Returns (uint64 array [n_workers, max_list, 4], clock_khz)."""
+    n = C.c_size_t(0)
+    nw, ml, khz = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib().mk_get_trace(ctx, None, C.byref(n), C.byref(nw), C.byref(ml), C.byref(khz)), ctx)
+    out = np.zeros(n.value, dtype=np.uint64)
+    _check(lib().mk_get_trace(ctx, out.ctypes.data_as(C.POINTER(C.c_uint64)), C.byref(n), None, None, None), ctx)
+    return out.reshape(nw.value, ml.value, 4), khz.value
 
 
 def mk_last_error(ctx=None) -> str:

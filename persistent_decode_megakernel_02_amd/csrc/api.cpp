@@ -46,9 +46,9 @@ struct mk_ctx {
   float *rope_cos = nullptr, *rope_sin = nullptr;
   uint16_t *kc = nullptr, *vc = nullptr;
   size_t kv_elems = 0;
-  float *x = nullptr, *qkv = nullptr, *o = nullptr, *a = nullptr, *part_ml = nullptr, *part_acc = nullptr;
-  uint32_t* tickets = nullptr;
-  size_t n_tickets = 0;
+  float *x = nullptr, *qkv = nullptr, *o = nullptr, *a = nullptr;
+  TV *part_ml = nullptr, *part_acc = nullptr;
+  size_t n_part_ml = 0, n_part_acc = 0;
   LmPart* lm_part = nullptr;
   int32_t* pending = nullptr;
   int32_t* force = nullptr;
@@ -65,6 +65,10 @@ struct mk_ctx {
   uint32_t epoch = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float last_ms = 0.f;
+  // tracing
+  int trace_step = -1;
+  uint64_t* trace = nullptr;
+  int trace_stride = 0;
 };
 
 static std::string g_create_err;
@@ -96,6 +100,7 @@ static std::string validate(const mk_model_cfg& cfg) {
   if (cfg.n_q_heads <= 0 || cfg.n_kv_heads <= 0 || cfg.n_q_heads % cfg.n_kv_heads) return "bad head counts";
   const int G = cfg.n_q_heads / cfg.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return "query heads per KV head must be 1, 2 or 4";
+  if (cfg.head_dim != 64 && cfg.head_dim != 128) return "head_dim must be 64 or 128";
   if (cfg.mode != MK_MODE_MEGAKERNEL && cfg.mode != MK_MODE_PER_OP) return "unknown mode";
   if (!(cfg.rms_eps > 0.f) || !(cfg.rope_theta > 0.0)) return "rms_eps and rope_theta must be positive";
   return "";
@@ -262,10 +267,10 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if ((rc = dalloc(c, (void**)&c->qkv, (size_t)B * QKVR * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->o, (size_t)B * QD * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->a, (size_t)B * F * 4))) return bail(rc);
-  if ((rc = dalloc(c, (void**)&c->part_ml, (size_t)B * Hkv * NS * G * 2 * 4))) return bail(rc);
-  if ((rc = dalloc(c, (void**)&c->part_acc, (size_t)B * Hkv * NS * G * D * 4))) return bail(rc);
-  c->n_tickets = (size_t)L * B * Hkv;
-  if ((rc = dalloc(c, (void**)&c->tickets, c->n_tickets * 4))) return bail(rc);
+  c->n_part_ml = (size_t)B * Hkv * NS * G * 2;
+  c->n_part_acc = (size_t)B * Hkv * NS * G * D;
+  if ((rc = dalloc(c, (void**)&c->part_ml, c->n_part_ml * sizeof(TV)))) return bail(rc);
+  if ((rc = dalloc(c, (void**)&c->part_acc, c->n_part_acc * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->lm_part, (size_t)B * c->g.n_lm * sizeof(LmPart)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->pending, (size_t)B * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->flags, (size_t)c->g.n_slots * 4))) return bail(rc);
@@ -311,7 +316,8 @@ const char* mk_last_error(mk_ctx* c) { return c ? c->err.c_str() : g_create_err.
 int mk_reset(mk_ctx* c) {
   if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
   HIPCHK(c, hipMemsetAsync(c->flags, 0, (size_t)c->g.n_slots * 4, c->stream));
-  HIPCHK(c, hipMemsetAsync(c->tickets, 0, c->n_tickets * 4, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->part_ml, 0, c->n_part_ml * sizeof(TV), c->stream));
+  HIPCHK(c, hipMemsetAsync(c->part_acc, 0, c->n_part_acc * sizeof(TV), c->stream));
   HIPCHK(c, hipMemsetAsync(c->status, 0, 64, c->stream));
   HIPCHK(c, hipMemsetAsync(c->pending, 0, (size_t)c->cfg.batch * 4, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
@@ -410,7 +416,8 @@ static KParams make_params(mk_ctx* c) {
   P.a = c->a;
   P.part_ml = c->part_ml;
   P.part_acc = c->part_acc;
-  P.tickets = c->tickets;
+  P.ntag = (uint32_t)c->g.events.size();
+  P.epoch = c->epoch;
   P.lm_part = c->lm_part;
   P.pending = c->pending;
   P.flags = c->flags;
@@ -423,6 +430,9 @@ static KParams make_params(mk_ctx* c) {
   P.status = c->status;
   P.watchdog = cfg.watchdog_polls ? cfg.watchdog_polls : kDefaultWatchdog;
   P.with_lm = 1;
+  P.trace = nullptr;
+  P.trace_step = -1;
+  P.trace_stride = c->trace_stride;
   return P;
 }
 
@@ -435,7 +445,8 @@ static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
     for (size_t r = 0; r < n_ranges; ++r) {
       P.op_first = (int)g.op_ranges[r].first;
       P.op_count = (int)g.op_ranges[r].count;
-      HIPCHK(c, launch(1, P, c->stream));
+      const bool attn = g.tasks[g.op_ranges[r].first].op == OP_ATTN;
+      HIPCHK(c, launch(attn ? 3 : 1, P, c->stream));
     }
   }
   if (with_lm) {
@@ -475,6 +486,7 @@ int mk_prefill(mk_ctx* c, const int32_t* prompts, int len) {
     P.force_tok = c->force;
     P.with_lm = 0;
     if ((rc = run_per_op_steps(c, P, n, false))) return rc;
+    c->epoch += (uint32_t)n;
   }
   std::vector<int32_t> pend(B);
   for (int b = 0; b < B; ++b) pend[b] = prompts[(size_t)b * len + len - 1];
@@ -537,6 +549,11 @@ int mk_decode(mk_ctx* c, int n_steps, int32_t* out_tokens, float* out_logits) {
   P.out_tokens = out_tokens;
   P.out_logits = out_logits;
   P.epoch = c->epoch;
+  if (c->trace && c->trace_step >= 0 && c->trace_step < n_steps && c->cfg.mode == MK_MODE_MEGAKERNEL) {
+    HIPCHK(c, hipMemsetAsync(c->trace, 0, (size_t)c->g.n_workers * c->trace_stride * 4 * 8, c->stream));
+    P.trace = c->trace;
+    P.trace_step = c->trace_step;
+  }
   HIPCHK(c, hipEventRecord(c->ev0, c->stream));
   if (c->cfg.mode == MK_MODE_MEGAKERNEL) {
     HIPCHK(c, launch(0, P, c->stream));
@@ -557,7 +574,7 @@ int mk_decode(mk_ctx* c, int n_steps, int32_t* out_tokens, float* out_logits) {
   }
   c->pos += n_steps;
   std::fill(c->seq_pos.begin(), c->seq_pos.end(), c->pos);
-  if (c->cfg.mode == MK_MODE_MEGAKERNEL) c->epoch += (uint32_t)n_steps;
+  c->epoch += (uint32_t)n_steps;
   return MK_OK;
 }
 
@@ -570,6 +587,41 @@ int mk_get_graph(mk_ctx* c, void* buf, size_t* len) {
   }
   std::memcpy(buf, bytes.data(), bytes.size());
   *len = bytes.size();
+  return MK_OK;
+}
+
+int mk_set_trace(mk_ctx* c, int step) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
+  if (step >= 0 && !c->trace) {
+    uint32_t mx = 0;
+    for (uint32_t n : c->g.list_len) mx = std::max(mx, n);
+    c->trace_stride = (int)mx;
+    int rc = dalloc(c, (void**)&c->trace, (size_t)c->g.n_workers * mx * 4 * 8);
+    if (rc) return rc;
+    HIPCHK(c, hipMemset(c->trace, 0, (size_t)c->g.n_workers * mx * 4 * 8));
+  }
+  c->trace_step = step;
+  return MK_OK;
+}
+
+int mk_get_trace(mk_ctx* c, uint64_t* out, size_t* len, int32_t* n_workers, int32_t* max_list, int32_t* clock_khz) {
+  if (!c || !len) return fail(c, MK_ERR_INVALID_ARG, "null argument");
+  if (!c->trace) return fail(c, MK_ERR_STATE, "tracing was never enabled");
+  const size_t need = (size_t)c->g.n_workers * c->trace_stride * 4;
+  if (n_workers) *n_workers = c->g.n_workers;
+  if (max_list) *max_list = c->trace_stride;
+  if (clock_khz) {
+    int khz = 0;
+    HIPCHK(c, hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, c->device));
+    *clock_khz = khz;
+  }
+  if (!out) {
+    *len = need;
+    return MK_OK;
+  }
+  if (*len < need) return fail(c, MK_ERR_INVALID_ARG, "trace buffer too small");
+  HIPCHK(c, hipMemcpy(out, c->trace, need * 8, hipMemcpyDeviceToHost));
+  *len = need;
   return MK_OK;
 }
 

@@ -143,15 +143,45 @@ __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
 }
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return ldg((const uint4*)p); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane reductions in VALU (DPP row operations and the gfx950
+// permlane swaps), no LDS traffic.  Every lane of a group receives the same,
+// bit-identical result (each step adds the same two operands on all lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float xor16_pair(float v) {  // lanes i and i^16 both get v_i + v_{i^16}
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_pair(float v) {  // lanes i and i^32 both get v_i + v_{i^32}
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// sum over aligned groups of N lanes (N = 4, 8, 16)
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);                 // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);                 // quad_perm [2,3,0,1]
+  if (N >= 8) v += dpp<0x141>(v);    // row_half_mirror
+  if (N >= 16) v += dpp<0x140>(v);   // row_mirror
   return v;
 }
+__device__ __forceinline__ float wave_sum(float v) { return xor32_pair(xor16_pair(group_sum<16>(v))); }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return xor32_pair_max(xor16_pair_max(v));
 }
 // larger value wins; equal values: lower index wins
 __device__ __forceinline__ void amax_merge(float& v, int32_t& i, float v2, int32_t i2) {
@@ -174,7 +204,8 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // ---------------------------------------------------------------------------
 // events
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32_t target, uint32_t task, Misc* m) {
+__device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32_t target, uint32_t task, Misc* m,
+                                           uint64_t* tr = nullptr) {
   if (ev == EV_NONE) return true;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -218,6 +249,7 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
     if (lane == 0) m->flag = ok;
   }
   __syncthreads();
+  if (tr && threadIdx.x == 0) tr[1] = wall_clock64();
   return m->flag != 0;
 }
 
@@ -272,7 +304,8 @@ __device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
 // GEMV task: rows [a0, a1) of one weight matrix against B activation vectors
 // ---------------------------------------------------------------------------
 template <int NB>
-__device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, int s, bool mega, char* lds) {
+__device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
+                                          uint64_t* tr) {
   const int op = (int)t.op, l = (int)t.layer;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
   float* xs = (float*)lds;
@@ -355,8 +388,9 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const v4f x0 = *(const v4f*)(xs + (size_t)b * kc + j * 8);
-        const v4f x1 = *(const v4f*)(xs + (size_t)b * kc + j * 8 + 4);
+        // two planes per sequence: elements 0-3 and 4-7 of every 8-element chunk
+        const v4f x0 = *(const v4f*)(xs + (size_t)b * kc + j * 4);
+        const v4f x1 = *(const v4f*)(xs + (size_t)b * kc + (kc >> 1) + j * 4);
         float a = acc[b];
         a = fmaf(wf[0], x0.x, a);
         a = fmaf(wf[1], x0.y, a);
@@ -388,7 +422,10 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) issue(buf[d]);
 
-  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m)) return false;
+  // a wait on the previous step is met by the launch boundary at the first step of a call
+  if (mega && !(s == 0 && t.wait_lag) &&
+      !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m, tr))
+    return false;
 
   // layer-0 Q/K/V reads the embedding of this step's token
   if (embed_src) {
@@ -427,10 +464,11 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 #pragma unroll
       for (int b = 0; b < NB; ++b) ss[b] = 0.f;
       const int e_lo = (sl == 0 && norm) ? 0 : k0, e_hi = (sl == 0 && norm) ? K : k0 + ks;
-      for (int base = e_lo + tid * 4; base < e_hi; base += NT * 4 * 8) {
-        v4f v[8][NB];
+      constexpr int SU = NB >= 8 ? 1 : 8 / NB;  // 16-byte loads in flight per thread and sequence
+      for (int base = e_lo + tid * 4; base < e_hi; base += NT * 4 * SU) {
+        v4f v[SU][NB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < SU; ++u) {
           const int e = base + u * NT * 4;
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
@@ -449,7 +487,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
           }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < SU; ++u) {
           const int e = base + u * NT * 4;
           if (e < e_hi) {
             float g4[4] = {1.f, 1.f, 1.f, 1.f};
@@ -464,28 +502,26 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
             for (int b = 0; b < NB; ++b) {
               const v4f x = v[u][b];
               if (norm && sl == 0) ss[b] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-              if (e >= k0 && e < k0 + ks)
-                *(v4f*)(xs + (size_t)b * kc + (e - k0)) = v4f{x.x * g4[0], x.y * g4[1], x.z * g4[2], x.w * g4[3]};
+              if (e >= k0 && e < k0 + ks) {
+                const int el = e - k0;
+                *(v4f*)(xs + (size_t)b * kc + ((el >> 2) & 1) * (kc >> 1) + (el >> 3) * 4) =
+                    v4f{x.x * g4[0], x.y * g4[1], x.z * g4[2], x.w * g4[3]};
+              }
             }
           }
         }
       }
-      if (norm && sl == 0) {
+      if (norm && sl == 0) {  // per-wave partial sums; the scale itself is formed in the epilogue
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const float v = wave_sum(ss[b]);
           if (lane == 0) m->wred[w][b] = v;
         }
-        __syncthreads();
-        if (tid < NB) {
-          float tot = 0.f;
-          for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][tid];
-          m->r[tid] = 1.0f / sqrtf(tot / (float)K + P.eps);
-        }
       }
       __syncthreads();
     }
     // ---- stream this slice's weight rows through the pipeline
+    if (tr && sl == 0 && tid == 0) tr[2] = wall_clock64();
     // Nothing is outstanding here (staging waited for its loads, which were
     // issued after the prefetch); saying so explicitly gives the compiler an
     // exact count to start from, so the loop below waits only for the oldest
@@ -513,11 +549,20 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   }
   __syncthreads();
 
+  // ---- RMSNorm scale r = 1/sqrt(mean(x^2) + eps), applied after the dot products
+  float rs[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float tot = 0.f;
+    for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][b];
+    rs[b] = norm ? 1.0f / sqrtf(tot / (float)K + P.eps) : 1.0f;
+  }
+
   // ---- epilogue per operator
   if (op == OP_QKV) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, red[ul * NB + b] * m->r[b]);
+      stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, red[ul * NB + b] * rs[b]);
     }
   } else if (op == OP_WO || op == OP_DOWN) {
     for (int i = tid; i < nu * NB; i += NT) {
@@ -528,8 +573,8 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   } else if (op == OP_GU) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      const float gt = red[(ul * 2) * NB + b] * m->r[b];
-      const float up = red[(ul * 2 + 1) * NB + b] * m->r[b];
+      const float gt = red[(ul * 2) * NB + b] * rs[b];
+      const float up = red[(ul * 2 + 1) * NB + b] * rs[b];
       stc(P.a + (size_t)b * P.F + u0 + ul, silu(gt) * up);
     }
   } else {  // OP_LM
@@ -543,7 +588,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     for (int ul = tid; ul < nu; ul += NT) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float logit = red[ul * NB + b] * m->r[b];
+        const float logit = red[ul * NB + b] * rs[b];
         if (P.out_logits) stg(P.out_logits + ((size_t)s * P.B + b) * P.V + u0 + ul, logit);
         amax_merge(bv[b], bi[b], logit, u0 + ul);
       }
@@ -566,8 +611,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       stc_i(&lp->idx, ix);
     }
   }
-  if (mega) signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
-  else __syncthreads();
+  signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
   return true;
 }
 
@@ -575,32 +619,49 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 // Attention task (sequence b, KV head g, split sp): QK-norm + RoPE of the G
 // query heads (and of k when this split holds the current position, which it
 // then appends to the cache), scores over the split's positions, and the
-// split's softmax partial (max m, sum l, unnormalised P.V).  The last split
-// of (b, g) to finish merges all partials in ascending split order:
-//   M = max_s m_s,  o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s.
+// split's softmax partial: max m, sum l = sum_j e^{t_j - m}, and the
+// unnormalised acc = sum_j e^{t_j - m} v_j (FlashDecoding-style split-KV, as
+// in the Mirage article's attention search space).  Partials are stored with
+// their step tag.  The split holding the current position merges all splits
+// in ascending order with the online rule
+//   M' = max(M, m_s); num = num e^{M - M'} + acc_s e^{m_s - M'};
+//   den = den e^{M - M'} + l_s e^{m_s - M'};   o = num / den.
 // ---------------------------------------------------------------------------
-template <int G>
-__device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, int s, bool mega, char* lds) {
-  const int Hkv = P.Hkv, D = P.D, S = P.S;
+__device__ __forceinline__ void st_tv(TV* p, float v, uint32_t tag) {
+  const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
+  __hip_atomic_store((GAS uint64_t*)p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tv(const TV* p) {
+  return __hip_atomic_load((const GAS uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tv_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ bool tv_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
+template <int G, int LPP>
+__device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
+                                          uint64_t* tr) {
+  constexpr int D = LPP * 8, PPB = NT / LPP;
+  const int Hkv = P.Hkv, S = P.S;
   const int bg = (int)t.a0, b = bg / Hkv, g = bg - b * Hkv, sp = (int)t.a1, l = (int)t.layer;
   const int pos = P.pos0 + s, N = pos + 1;
   const int n_act = (N + S - 1) / S;
-  if (sp >= n_act) return true;  // split beyond the current length: nothing to do, nothing to notify
+  if (sp >= n_act) return true;  // split beyond the current length: nothing to do
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j0 = sp * S, j1 = min(j0 + S, N);
-  const bool has_cur = (j1 == N);
+  const bool has_cur = (j1 == N);  // this split holds the current position and merges
   const int jc = has_cur ? pos : j1;  // cached positions [j0, jc)
-  const int LPP = D / 8, lp = tid % LPP, po = tid / LPP, PPB = NT / LPP;
+  const int lp = tid % LPP, po = tid / LPP;
   const size_t head = ((size_t)(l * P.B + b) * Hkv + g) * P.max_seq;
   uint16_t* Kh = P.kc + head * D;
   uint16_t* Vh = P.vc + head * D;
+  const uint32_t tag = (P.epoch + (uint32_t)s) * P.ntag + t.sig_ev + 1u;
 
   // cached K/V do not depend on this step: load them before waiting
   uint4 kr[ATT_MAXL], vr[ATT_MAXL];
 #pragma unroll
   for (int i = 0; i < ATT_MAXL; ++i) {
     const int j = j0 + po + i * PPB;
-    if (i * PPB < S && po + i * PPB < S && j < jc) {
+    if (po + i * PPB < S && j < jc) {
       kr[i] = ld16(Kh + (size_t)j * D + lp * 8);
       vr[i] = ld16(Vh + (size_t)j * D + lp * 8);
     } else {
@@ -610,10 +671,10 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
 
   float* fl = (float*)lds;
   Misc* m = (Misc*)(lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
-  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m)) return false;
+  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr)) return false;
 
-  float* raw = fl;                       // [(G+2) D]: q heads, k, v
-  float* qrot = raw + (G + 2) * D;       // [G D]
+  float* raw = fl;                             // [(G+2) D]: q heads, k, v
+  float* qrot = raw + (G + 2) * D;             // [G D]
   uint16_t* kcur = (uint16_t*)(qrot + G * D);  // [D]
   uint16_t* vcur = kcur + D;                   // [D]
   float* sc = (float*)(vcur + D);              // [G S]
@@ -632,7 +693,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
     __syncthreads();
   }
-  const int half = D / 2;
+  constexpr int half = D / 2;
   const float* cs = P.rope_cos + (size_t)pos * half;
   const float* sn = P.rope_sin + (size_t)pos * half;
   const LayerW LW = ldg(P.layers + l);
@@ -662,7 +723,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     stg((uint4*)(Vh + (size_t)pos * D + tid * 8), *(const uint4*)(vcur + tid * 8));
   }
 
-  // ---- scores t_j = (q_h . k_j) / sqrt(D)
+  // ---- scores t_j = (q_h . k_j) / sqrt(D); LPP lanes share one position
   float q[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -674,7 +735,6 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
       const int jr = po + i * PPB, j = j0 + jr;
       const uint4 kk = (has_cur && j == pos) ? *(const uint4*)(kcur + lp * 8) : kr[i];
       const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-      float part[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float a = 0.f;
@@ -683,14 +743,9 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
           a = fmaf(q[h][2 * e], bf_lo(kw[e]), a);
           a = fmaf(q[h][2 * e + 1], bf_hi(kw[e]), a);
         }
-        part[h] = a;
+        a = group_sum<LPP>(a);
+        if (jr < S && j < j1 && lp == 0) sc[h * S + jr] = a * P.attn_scale;
       }
-      for (int o = LPP / 2; o > 0; o >>= 1)
-#pragma unroll
-        for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], o, 64);
-      if (jr < S && j < j1 && lp == 0)
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[h * S + jr] = part[h] * P.attn_scale;
     }
   }
   __syncthreads();
@@ -736,70 +791,110 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
       }
     }
   }
-  for (int o = LPP; o < 64; o <<= 1)
+  // sum over the positions of this wave: lanes with the same lp
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+      if (LPP == 8) v += dpp<0x128>(v);  // row_ror:8 (lane i and i^8)
+      acc[h][e] = xor32_pair(xor16_pair(v));
+    }
   if (lane < LPP)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) accw[(w * G + h) * D + lp * 8 + e] = acc[h][e];
   __syncthreads();
+  // ---- this split's partial, tagged with the step
   const size_t pbase = ((size_t)bg * P.NS + sp) * G;
   for (int i = tid; i < G * D; i += NT) {
     float v = 0.f;
     for (int ww = 0; ww < NW; ++ww) v += accw[ww * G * D + i];
-    stc(P.part_acc + pbase * D + i, v);
+    st_tv(P.part_acc + pbase * D + i, v, tag);
   }
   if (tid < G) {
-    stc(P.part_ml + (pbase + tid) * 2, m->ml[tid][0]);
-    stc(P.part_ml + (pbase + tid) * 2 + 1, m->ml[tid][1]);
+    st_tv(P.part_ml + (pbase + tid) * 2, m->ml[tid][0], tag);
+    st_tv(P.part_ml + (pbase + tid) * 2 + 1, m->ml[tid][1], tag);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // ---- last arriver merges
-  if (n_act > 1) {
-    if (tid == 0) {
-      uint32_t* tk = P.tickets + ((size_t)l * P.B + b) * Hkv + g;
-      const uint32_t old = __hip_atomic_fetch_add((GAS uint32_t*)tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = old == (uint32_t)(n_act - 1);
-      if (last) stc_u(tk, 0u);
-      m->flag = last ? 1 : 0;
-    }
+  if (!has_cur) {
     __syncthreads();
-    if (!m->flag) return true;
+    return true;
   }
+  // ---- merge every split of (b, g), ascending, polling the others' partials
   const size_t b0 = (size_t)bg * P.NS;
+  uint32_t polls = 0;
+  bool ok_all = true;
   for (int i = tid; i < G * D; i += NT) {
-    const int h = i / D;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < n_act; ++s2) M = fmaxf(M, ldc(P.part_ml + ((b0 + s2) * G + h) * 2));
-    float num = 0.f, den = 0.f;
-    for (int s2 = 0; s2 < n_act; ++s2) {
-      const size_t pi = (b0 + s2) * G + h;
-      const float e = expf(ldc(P.part_ml + pi * 2) - M);
-      num += e * ldc(P.part_acc + pi * D + (i - h * D));
-      den += e * ldc(P.part_ml + pi * 2 + 1);
+    const int h = i / D, d = i - h * D;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int c0 = 0; c0 < n_act && ok_all; c0 += 8) {
+      // issue the loads of up to 8 splits together, then re-poll any not yet written
+      uint64_t wm[8], wl[8], wa[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (c0 + k < n_act) {
+          const size_t pi = (b0 + c0 + k) * G + h;
+          wm[k] = ld_tv(P.part_ml + pi * 2);
+          wl[k] = ld_tv(P.part_ml + pi * 2 + 1);
+          wa[k] = ld_tv(P.part_acc + pi * D + d);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (c0 + k < n_act) {
+          const size_t pi = (b0 + c0 + k) * G + h;
+          while (ok_all && !(tv_ok(wm[k], tag) && tv_ok(wl[k], tag) && tv_ok(wa[k], tag))) {
+            if (++polls > P.watchdog) ok_all = false;
+            __builtin_amdgcn_s_sleep(1);
+            wm[k] = ld_tv(P.part_ml + pi * 2);
+            wl[k] = ld_tv(P.part_ml + pi * 2 + 1);
+            wa[k] = ld_tv(P.part_acc + pi * D + d);
+          }
+          const float ms = tv_val(wm[k]);
+          const float Mn = fmaxf(M, ms);
+          const float so = expf(M - Mn), sn2 = expf(ms - Mn);
+          num = num * so + tv_val(wa[k]) * sn2;
+          den = den * so + tv_val(wl[k]) * sn2;
+          M = Mn;
+        }
+      }
     }
+    if (!ok_all) break;
     stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, num / den);
   }
-  if (mega) signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
-  else __syncthreads();
-  return true;
+  if (!ok_all) {
+    uint32_t zero = 0u;
+    if (__hip_atomic_compare_exchange_strong((GAS uint32_t*)(P.status + ST_CODE), &zero, ERR_WATCHDOG,
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+      stc_u(P.status + ST_CU, blockIdx.x);
+      stc_u(P.status + ST_TASK, t.tile);
+      stc_u(P.status + ST_EVENT, t.sig_ev);
+    }
+    stc_u(P.status + ST_ABORT, 1u);
+  }
+  signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+  return ldc_u(P.status + ST_ABORT) == 0u;
 }
 
 template <int NB>
-__device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int s, bool mega, char* lds) {
+__device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
+                                         uint64_t* tr = nullptr) {
   if (t.op == OP_ATTN) {
+    if (P.D == 64) {
+      switch (P.G) {
+        case 1: return task_attn<1, 8>(P, t, s, mega, lds, tr);
+        case 2: return task_attn<2, 8>(P, t, s, mega, lds, tr);
+        default: return task_attn<4, 8>(P, t, s, mega, lds, tr);
+      }
+    }
     switch (P.G) {
-      case 1: return task_attn<1>(P, t, s, mega, lds);
-      case 2: return task_attn<2>(P, t, s, mega, lds);
-      default: return task_attn<4>(P, t, s, mega, lds);
+      case 1: return task_attn<1, 16>(P, t, s, mega, lds, tr);
+      case 2: return task_attn<2, 16>(P, t, s, mega, lds, tr);
+      default: return task_attn<4, 16>(P, t, s, mega, lds, tr);
     }
   }
-  return task_gemv<NB>(P, t, s, mega, lds);
+  return task_gemv<NB>(P, t, s, mega, lds, tr);
 }
 
 // The megakernel: one launch runs n_steps decode steps of the whole model.
@@ -810,7 +905,10 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   for (int s = 0; s < P.n_steps; ++s) {
     for (uint32_t i = 0; i < n; ++i) {
       const TaskRec t = ldg(P.tasks + ldg(P.cu_tasks + off + i));
-      if (!run_task<NB>(P, t, s, true, lds)) return;
+      uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + i) * 4 : nullptr;
+      if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
+      if (!run_task<NB>(P, t, s, true, lds, tr)) return;
+      if (tr && threadIdx.x == 0) tr[3] = wall_clock64();
     }
   }
   if (blockIdx.x == 0) {
@@ -858,6 +956,10 @@ static hipError_t launch_nb(int kind, const KParams& P, hipStream_t st) {
     return hipLaunchCooperativeKernel((const void*)mk_persistent<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
   } else if (kind == 1) {
     hipLaunchKernelGGL(mk_per_op<NB>, dim3(P.n_workers), dim3(NT), sh, st, Q);
+  } else if (kind == 3) {
+    // cooperative: an attention merger polls partials written by other workgroups of the same launch
+    void* args[] = {&Q};
+    return hipLaunchCooperativeKernel((const void*)mk_per_op<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
   } else {
     hipLaunchKernelGGL(mk_finish_tokens<NB>, dim3(1), dim3(NT), sh, st, Q);
   }
@@ -884,7 +986,7 @@ hipError_t prepare_kernels(int B) {
   }
 }
 
-// kind: 0 persistent (cooperative), 1 one operator instance, 2 final token
+// kind: 0 persistent (cooperative), 1 one operator instance, 2 final token, 3 attention operator instance
 hipError_t launch(int kind, const KParams& P, hipStream_t st) {
   switch (P.B) {
     case 1: return launch_nb<1>(kind, P, st);

@@ -59,6 +59,14 @@ struct LmPart {
   int32_t idx;
 };
 
+// A value with the sequence tag of the step that wrote it, stored and loaded
+// as one 64-bit word: a reader that sees the expected tag also sees the
+// value written with it.  Tag of event ev at global step n: n * ntag + ev + 1.
+struct TV {
+  float v;
+  uint32_t tag;
+};
+
 // status[0]: abort flag; status[1..7]: first error record
 enum : uint32_t { ST_ABORT = 0, ST_CODE = 1, ST_CU = 2, ST_TASK = 3, ST_EVENT = 4, ST_SEEN = 5, ST_WANT = 6 };
 constexpr uint32_t ERR_WATCHDOG = 1;
@@ -85,9 +93,8 @@ struct KParams {
   float* qkv;       // [B][QKVR]
   float* o;         // [B][QD]
   float* a;         // [B][F]
-  float* part_ml;   // [B][Hkv][NS][G][2]
-  float* part_acc;  // [B][Hkv][NS][G][D]
-  uint32_t* tickets;  // [L][B][Hkv]
+  TV* part_ml;      // [B][Hkv][NS][G][2] split max and sum, tagged
+  TV* part_acc;     // [B][Hkv][NS][G][D] split unnormalised P.V, tagged
   LmPart* lm_part;    // [B][n_lm]
   // tokens
   int32_t* pending;           // [B]
@@ -105,9 +112,13 @@ struct KParams {
   uint32_t* status;
   // run
   int32_t pos0, n_steps, with_lm;
-  uint32_t epoch, watchdog;
+  uint32_t epoch, watchdog;  // epoch: decode steps run by this context so far (any mode, prefill included)
+  uint32_t ntag;             // tag period: number of events
   // per-operator launch
   int32_t op_first, op_count, step;
+  // optional trace of one decode step: [worker][list index][4] wall-clock stamps
+  uint64_t* trace;
+  int32_t trace_step, trace_stride;
 };
 
 }  // namespace mk
