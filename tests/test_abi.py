@@ -1,0 +1,35 @@
+"""The C ABI library loads and exports every entry point that include/mk.h declares (CPU only)."""
+import ctypes
+import os
+import re
+
+from persistent_decode_megakernel_02_amd import binding as mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "mk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ("mk_create", "mk_load_weights", "mk_prefill", "mk_decode", "mk_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mk.LIB_PATH)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared()) <= set(mk.EXPORTS)
+
+
+def test_error_reporting_without_context():
+    import pytest
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_build_graph(mk.make_cfg(__import__("persistent_decode_megakernel_02_amd.configs").configs.TINY, 5, 64), 8)
+    assert e.value.code == -1
+    assert "batch" in mk.mk_last_error(None)
