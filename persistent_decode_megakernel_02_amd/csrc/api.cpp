@@ -110,11 +110,11 @@ static int check_capacity(const mk_model_cfg& cfg, const Graph& g, std::string* 
   const int D = cfg.head_dim, G = cfg.n_q_heads / cfg.n_kv_heads;
   const int S = g.split;
   const int lpp = D / 8, ppb = 512 / lpp;
-  if (S > 4 * ppb) {
-    *why = "split too large for head_dim (at most 16384 / head_dim)";
+  if (S > 5 * ppb) {
+    *why = "split too large for head_dim (at most 20480 / head_dim)";
     return MK_ERR_UNSUPPORTED;
   }
-  const int att_floats = (G + 2) * D + G * D + D + G * S + 8 * G * D;
+  const int att_floats = (G + 2) * D + G * D + D + G * S + std::max(8 * G * D, 3 * G * g.n_splits);
   if (att_floats > kXsFloats) {
     *why = "attention working set exceeds LDS";
     return MK_ERR_UNSUPPORTED;

@@ -42,8 +42,16 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   if (D % 8 || D > 256 || 64 % (D / 8)) return "head_dim must be 64/8*2^k-compatible: D%8==0, D<=256, (D/8) | 64";
   if (G > 8) return "at most 8 query heads per KV head";
   if (c.hidden % 8 || c.ffn % 8) return "hidden and ffn must be multiples of 8";
-  const int S = c.split > 0 ? c.split : kDefaultSplit;
-  if (S > 32768 / D) return "split * head_dim must be <= 32768";
+  // Default split: enough splits that the (sequence, KV head, split) tasks of a
+  // full cache fill the workers once, each split between 64 positions and the
+  // per-task register budget (5 * 4096 / D positions).
+  const int smax = 5 * 4096 / D;
+  int S = c.split;
+  if (S <= 0) {
+    const int ns_target = std::max(1, n_workers / std::max(1, c.batch * Hkv));
+    S = std::min(smax, std::max(kDefaultSplit, (c.max_seq + ns_target - 1) / ns_target));
+  }
+  if (S > smax) return "split must be <= 5 * 4096 / head_dim";
   g.n_workers = n_workers;
   g.split = S;
   g.n_splits = (c.max_seq + S - 1) / S;

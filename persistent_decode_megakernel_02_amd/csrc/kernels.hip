@@ -30,7 +30,7 @@ constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
 constexpr int DEPTH = 4;   // pipeline groups in flight per wave (16 KB per wave)
 constexpr int RED_FLOATS = 8192;
 constexpr int MISC_BYTES = 4096;
-constexpr int ATT_MAXL = 4;  // K/V 16-byte loads per thread per attention task
+constexpr int ATT_MAXL = 5;  // K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8))
 
 // Pointers kept inside the parameter block are generic; casting them to the
 // global address space lets the compiler emit global (not flat) memory
@@ -821,47 +821,64 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     __syncthreads();
     return true;
   }
-  // ---- merge every split of (b, g), ascending, polling the others' partials
+  // ---- merge every split of (b, g) in ascending order, polling the others' partials:
+  //   M = max_s m_s,  den = sum_s e^{m_s - M} l_s,  o = sum_s e^{m_s - M} acc_s / den.
+  // Pass 1 gathers every (m_s, l_s) into LDS in one round trip; pass 2 issues
+  // the accumulator loads of up to 16 splits at once.
   const size_t b0 = (size_t)bg * P.NS;
   uint32_t polls = 0;
   bool ok_all = true;
-  for (int i = tid; i < G * D; i += NT) {
+  __syncthreads();                    // every thread is done reading the P.V scratch and m->ml
+  float* mls = accw;                  // [G][n_act][2], reuses the P.V scratch
+  float* scl = accw + 2 * G * n_act;  // [G][n_act] weights e^{m_s - M}
+  for (int i = tid; i < G * n_act; i += NT) {
+    const int h = i / n_act, s2 = i - h * n_act;
+    const size_t pi = (b0 + s2) * G + h;
+    uint64_t wm = ld_tv(P.part_ml + pi * 2), wl = ld_tv(P.part_ml + pi * 2 + 1);
+    while (ok_all && !(tv_ok(wm, tag) && tv_ok(wl, tag))) {
+      if (++polls > P.watchdog) ok_all = false;
+      __builtin_amdgcn_s_sleep(1);
+      wm = ld_tv(P.part_ml + pi * 2);
+      wl = ld_tv(P.part_ml + pi * 2 + 1);
+    }
+    mls[(h * n_act + s2) * 2] = tv_val(wm);
+    mls[(h * n_act + s2) * 2 + 1] = tv_val(wl);
+  }
+  __syncthreads();
+  if (tid < G) {
+    const int h = tid;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < n_act; ++s2) M = fmaxf(M, mls[(h * n_act + s2) * 2]);
+    float den = 0.f;
+    for (int s2 = 0; s2 < n_act; ++s2) {
+      const float e = expf(mls[(h * n_act + s2) * 2] - M);
+      scl[h * n_act + s2] = e;
+      den += e * mls[(h * n_act + s2) * 2 + 1];
+    }
+    m->ml[h][1] = den;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D && ok_all; i += NT) {
     const int h = i / D, d = i - h * D;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int c0 = 0; c0 < n_act && ok_all; c0 += 8) {
-      // issue the loads of up to 8 splits together, then re-poll any not yet written
-      uint64_t wm[8], wl[8], wa[8];
+    float num = 0.f;
+    for (int c0 = 0; c0 < n_act && ok_all; c0 += 16) {
+      uint64_t wa[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (c0 + k < n_act) {
-          const size_t pi = (b0 + c0 + k) * G + h;
-          wm[k] = ld_tv(P.part_ml + pi * 2);
-          wl[k] = ld_tv(P.part_ml + pi * 2 + 1);
-          wa[k] = ld_tv(P.part_acc + pi * D + d);
-        }
-      }
+      for (int k = 0; k < 16; ++k)
+        if (c0 + k < n_act) wa[k] = ld_tv(P.part_acc + ((b0 + c0 + k) * G + h) * D + d);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 16; ++k) {
         if (c0 + k < n_act) {
-          const size_t pi = (b0 + c0 + k) * G + h;
-          while (ok_all && !(tv_ok(wm[k], tag) && tv_ok(wl[k], tag) && tv_ok(wa[k], tag))) {
+          while (ok_all && !tv_ok(wa[k], tag)) {
             if (++polls > P.watchdog) ok_all = false;
             __builtin_amdgcn_s_sleep(1);
-            wm[k] = ld_tv(P.part_ml + pi * 2);
-            wl[k] = ld_tv(P.part_ml + pi * 2 + 1);
-            wa[k] = ld_tv(P.part_acc + pi * D + d);
+            wa[k] = ld_tv(P.part_acc + ((b0 + c0 + k) * G + h) * D + d);
           }
-          const float ms = tv_val(wm[k]);
-          const float Mn = fmaxf(M, ms);
-          const float so = expf(M - Mn), sn2 = expf(ms - Mn);
-          num = num * so + tv_val(wa[k]) * sn2;
-          den = den * so + tv_val(wl[k]) * sn2;
-          M = Mn;
+          num += scl[h * n_act + c0 + k] * tv_val(wa[k]);
         }
       }
     }
-    if (!ok_all) break;
-    stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, num / den);
+    if (ok_all) stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, num / m->ml[h][1]);
   }
   if (!ok_all) {
     uint32_t zero = 0u;

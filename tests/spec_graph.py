@@ -47,7 +47,11 @@ class Task:
 
 def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
     G = Hq // Hkv
-    S = split if split > 0 else 64
+    if split > 0:
+        S = split
+    else:  # splits of a full cache fill the workers once; 64 <= S <= 5 * 4096 / D
+        ns_target = max(1, workers // max(1, B * Hkv))
+        S = min(5 * 4096 // D, max(64, -(-max_seq // ns_target)))
     NS = -(-max_seq // S)
     RG = (G + 2) * D
     TG = min(max(1, workers // Hkv), RG)
