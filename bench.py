@@ -36,6 +36,23 @@ def algorithmic_bytes(shape, batch, start_pos, n_steps):
     return w + kv
 
 
+def measured_traffic(workload, n_steps):
+    """HBM bytes per launch from the committed counter summary, or None.
+
+    The summary holds FETCH_SIZE + WRITE_SIZE of the persistent kernel per decode step, scaled by what the
+    same counters read for the library's known-volume probes.  It counts only while the kernel source is the
+    one it was taken on (sha256 prefix recorded beside the numbers); otherwise the figure is stale."""
+    import hashlib
+    f = os.path.join(ROOT, "profiles", f"mk_persistent_{workload}_hbm_traffic.json")
+    src = os.path.join(ROOT, "persistent_decode_megakernel_02_amd", "csrc", "kernels.hip")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["kernel_sha256_prefix"]:
+        return None
+    return rec["traffic_bytes_per_step"] * n_steps
+
+
 def cpu_baseline(shape, host_weights, sample_layers=4):
     """The oracle as it stands, single-threaded, on a bounded sample of the same shape.
 
@@ -74,6 +91,7 @@ def main():
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--probe-gib", type=float, default=8.0, help="read-probe buffer (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -150,6 +168,14 @@ def main():
         log(f"per-operator: {ablation:.4f} ms/token; bit-identical to the megakernel: {identical}")
         eng.set_mode(mk.MK_MODE_MEGAKERNEL)
 
+    probe = None
+    if args.probe_gib > 0:
+        eng.close()
+        nb = int(args.probe_gib * (1 << 30))
+        probe = {"read_GBps": round(mk.mk_read_bandwidth(nb, 3), 1), "copy_GBps": round(mk.mk_copy_bandwidth(nb, 3), 1),
+                 "bytes": nb}
+        log(f"plain read probe: {probe['read_GBps']} GB/s, copy probe: {probe['copy_GBps']} GB/s")
+
     cpu = None
     if host_weights is not None:
         log("CPU baseline: oracle, 1 thread, one step of 0- and 4-layer truncations of the same shape")
@@ -160,6 +186,7 @@ def main():
                          f"sizes), extrapolated linearly to {shape.n_layers} layers; single thread"}
         log(f"CPU oracle: {ms_cpu:.1f} ms/token")
 
+    traffic = measured_traffic(w.name, K)
     out = {
         "metric": METRIC,
         "value": round(ms_per_step, 5),
@@ -180,9 +207,11 @@ def main():
         "ablation_per_op_ms_per_step": round(ablation, 5) if ablation else None,
         "ablation_bit_identical": identical,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                      "roofline_ms_per_step": round(roofline_ms, 5), "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
+        "stream_probe": probe,
+        "frac_of_measured_read_peak": round(achieved / probe["read_GBps"], 4) if probe else None,
     }
     print(json.dumps(out), flush=True)
 

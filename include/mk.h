@@ -145,6 +145,19 @@ int mk_build_graph(const mk_model_cfg* cfg, int n_workers, void* buf, size_t* le
 /* Zero positions, pending tokens, event flags and tickets (weights kept). */
 int mk_reset(mk_ctx* ctx);
 
+/* Measured streaming-read rate of this device: a plain kernel reads a
+ * zero-filled buffer of `bytes` (rounded down to a whole number of 16-byte
+ * chunks per compute unit; >= 1 MiB) `iters` times with the same 16-byte
+ * non-temporal loads the GEMV tasks use; *gbps receives bytes*iters/time.
+ * Context-free: allocates and frees its own buffer on the current device,
+ * runs on the null stream.  Errors: INVALID_ARG, OOM, HIP. */
+int mk_read_bandwidth(size_t bytes, int iters, float* gbps);
+
+/* Same, but the kernel copies the first half of the buffer into the second
+ * (bytes/2 read and bytes/2 written per pass); *gbps counts read + write
+ * bytes.  Serves as the known-volume kernel for byte counters. */
+int mk_copy_bandwidth(size_t bytes, int iters, float* gbps);
+
 /* Duration in milliseconds of the last mk_decode's kernel work, measured
  * with HIP events on the context's stream around the launch(es). */
 int mk_last_decode_ms(mk_ctx* ctx, float* ms);

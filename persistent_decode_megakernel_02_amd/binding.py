@@ -40,6 +40,7 @@ class MkTensor(C.Structure):
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_load_kv", "mk_decode", "mk_set_mode", "mk_get_state",
            "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
+           "mk_read_bandwidth", "mk_copy_bandwidth",
            "mk_last_error", "mk_destroy"]
 
 _lib = None
@@ -65,6 +66,8 @@ def lib():
         L.mk_build_graph.argtypes = [C.POINTER(MkModelCfg), C.c_int, vp, C.POINTER(sz)]
         L.mk_reset.argtypes = [vp]
         L.mk_last_decode_ms.argtypes = [vp, C.POINTER(C.c_float)]
+        L.mk_read_bandwidth.argtypes = [sz, C.c_int, C.POINTER(C.c_float)]
+        L.mk_copy_bandwidth.argtypes = [sz, C.c_int, C.POINTER(C.c_float)]
         L.mk_set_trace.argtypes = [vp, C.c_int]
         L.mk_get_trace.argtypes = [vp, C.POINTER(C.c_uint64), C.POINTER(sz), C.POINTER(i32), C.POINTER(i32),
                                    C.POINTER(i32)]
@@ -170,6 +173,18 @@ def mk_last_decode_ms(ctx) -> float:
     ms = C.c_float()
     _check(lib().mk_last_decode_ms(ctx, C.byref(ms)), ctx)
     return ms.value
+
+
+def mk_read_bandwidth(nbytes: int, iters: int = 5) -> float:
+    g = C.c_float()
+    _check(lib().mk_read_bandwidth(nbytes, iters, C.byref(g)))
+    return g.value
+
+
+def mk_copy_bandwidth(nbytes: int, iters: int = 5) -> float:
+    g = C.c_float()
+    _check(lib().mk_copy_bandwidth(nbytes, iters, C.byref(g)))
+    return g.value
 
 
 def mk_set_trace(ctx, step: int):

@@ -20,6 +20,8 @@
 namespace mk {
 hipError_t prepare_kernels(int B);
 hipError_t launch(int kind, const KParams& P, hipStream_t st);
+hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* out, hipStream_t st);
+hipError_t launch_copy_probe(void* buf, size_t bytes, int n_wg, hipStream_t st);
 size_t lds_bytes(const KParams& P);
 int max_coresident_workers(int B, size_t lds);
 constexpr int kXsFloats = 28672;
@@ -624,6 +626,49 @@ int mk_get_trace(mk_ctx* c, uint64_t* out, size_t* len, int32_t* n_workers, int3
   *len = need;
   return MK_OK;
 }
+
+static int stream_probe(size_t bytes, int iters, bool copy, float* gbps) {
+  if (!gbps || bytes < ((size_t)1 << 20) || iters <= 0) return fail(nullptr, MK_ERR_INVALID_ARG, "bad argument");
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(nullptr, MK_ERR_HIP, "no device");
+  const int n_wg = prop.multiProcessorCount;
+  bytes = bytes / ((size_t)32 * n_wg) * ((size_t)32 * n_wg);
+  void* buf = nullptr;
+  uint32_t* out = nullptr;
+  if (hipMalloc(&buf, bytes) != hipSuccess) return fail(nullptr, MK_ERR_OOM, "probe buffer");
+  if (hipMalloc((void**)&out, 256) != hipSuccess) {
+    (void)hipFree(buf);
+    return fail(nullptr, MK_ERR_OOM, "probe buffer");
+  }
+  hipEvent_t e0, e1;
+  int rc = MK_OK;
+  if (hipMemset(buf, 0, bytes) != hipSuccess || hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    rc = fail(nullptr, MK_ERR_HIP, "probe setup");
+  } else {
+    auto run = [&]() {
+      return copy ? launch_copy_probe(buf, bytes, n_wg, nullptr) : launch_read_probe(buf, bytes, n_wg, out, nullptr);
+    };
+    if (run() != hipSuccess) rc = fail(nullptr, MK_ERR_HIP, "probe launch");
+    (void)hipEventRecord(e0, nullptr);
+    for (int i = 0; i < iters && rc == MK_OK; ++i)
+      if (run() != hipSuccess) rc = fail(nullptr, MK_ERR_HIP, "probe launch");
+    (void)hipEventRecord(e1, nullptr);
+    float ms = 0.f;
+    if (rc == MK_OK && (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+      rc = fail(nullptr, MK_ERR_HIP, "probe timing");
+    if (rc == MK_OK) *gbps = (float)((double)bytes * iters / (ms * 1e-3) / 1e9);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+  }
+  (void)hipFree(out);
+  (void)hipFree(buf);
+  return rc;
+}
+
+int mk_read_bandwidth(size_t bytes, int iters, float* gbps) { return stream_probe(bytes, iters, false, gbps); }
+int mk_copy_bandwidth(size_t bytes, int iters, float* gbps) { return stream_probe(bytes, iters, true, gbps); }
 
 int mk_last_decode_ms(mk_ctx* c, float* ms) {
   if (!c || !ms) return fail(c, MK_ERR_INVALID_ARG, "null argument");

@@ -960,6 +960,59 @@ __global__ __launch_bounds__(NT, 1) void mk_finish_tokens(KParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// Plain streaming read of a buffer: the achievable HBM read rate with the same
+// loads the GEMV tasks use (16-byte non-temporal, one contiguous block per
+// workgroup), and a kernel of known traffic for calibrating byte counters.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void mk_read_probe(const uint16_t* __restrict__ p, size_t per_wg16, uint32_t* out) {
+  const uint16_t* q = p + (size_t)blockIdx.x * per_wg16 * 8;
+  uint32_t acc = 0;
+  for (size_t i = threadIdx.x; i < per_wg16; i += (size_t)NT * 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t j = i + (size_t)u * NT;
+      v[u] = j < per_wg16 ? ldw(q + j * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;  // keeps the loads; never true for the zero-filled buffer
+}
+
+// Copy of one half of a buffer into the other (known read and write volume).
+__global__ __launch_bounds__(NT) void mk_copy_probe(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t per_wg16) {
+  const uint4* q = src + (size_t)blockIdx.x * per_wg16;
+  uint4* o = dst + (size_t)blockIdx.x * per_wg16;
+  for (size_t i = threadIdx.x; i < per_wg16; i += (size_t)NT * 4) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t j = i + (size_t)u * NT;
+      v[u] = j < per_wg16 ? ldw((const uint16_t*)(q + j)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t j = i + (size_t)u * NT;
+      if (j < per_wg16) stg(o + j, v[u]);
+    }
+  }
+}
+
+hipError_t launch_copy_probe(void* buf, size_t bytes, int n_wg, hipStream_t st) {
+  const size_t half16 = bytes / 32;
+  const size_t per_wg16 = half16 / (size_t)n_wg;
+  hipLaunchKernelGGL(mk_copy_probe, dim3(n_wg), dim3(NT), 0, st, (const uint4*)buf, (uint4*)buf + half16, per_wg16);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* out, hipStream_t st) {
+  const size_t per_wg16 = bytes / 16 / (size_t)n_wg;
+  hipLaunchKernelGGL(mk_read_probe, dim3(n_wg), dim3(NT), 0, st, (const uint16_t*)buf, per_wg16, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // host-side launch helpers
 // ---------------------------------------------------------------------------
 size_t lds_bytes(const KParams& P) { return (size_t)P.xs_floats * 4 + RED_FLOATS * 4 + MISC_BYTES; }
