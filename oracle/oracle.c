@@ -11,8 +11,13 @@
  * gated MLP -> down-projection + residual; then final RMSNorm, LM head and
  * greedy argmax.  Each primitive below names the passage that defines it.
  *
- * Precision: fp32 everywhere, bf16 weights and KV cache, sequential sums in
- * ascending index.  Build with -ffp-contract=off and without -ffast-math so
+ * Precision.  The decoder's stored activations are fp32: the residual
+ * stream x, the raw q/k/v projections, each attention head's output o, the
+ * SwiGLU output a and the logits.  Weights and the KV cache are bf16.  Every
+ * operator computes its result in fp64 from those stored inputs (sums
+ * sequential in ascending index) and rounds once, to fp32, where the decoder
+ * stores it; the rotated key is such an fp32 value before its bf16 rounding
+ * for the cache.  Build with -ffp-contract=off and without -ffast-math so
  * every multiply and add is rounded separately, as written.
  */
 #include "oracle.h"
@@ -43,37 +48,38 @@ uint16_t orc_f32_to_bf16(float f) {
 /* ------------------------------------------------------------------ */
 /* Linear layer y = W x (Mirage article, "Case 1: Normalization +      */
 /* Linear": the MatMul that follows the norm).  Each output row is a   */
-/* sequential fp32 sum over k = 0..cols-1.  Four rows are walked side  */
-/* by side for instruction-level parallelism; no row's sum is split or */
+/* sequential fp64 sum over k = 0..cols-1; every product of a bf16     */
+/* weight and an input is exact in fp64.  Four rows are walked side by */
+/* side for instruction-level parallelism; no row's sum is split or    */
 /* reordered.  With n_threads > 1 disjoint row blocks go to threads,   */
 /* which cannot change any result.                                     */
 /* ------------------------------------------------------------------ */
-static void matvec_rows(const uint16_t* W, int r0, int r1, int cols, const float* x, float* y) {
+static void matvec_rows(const uint16_t* W, int r0, int r1, int cols, const double* x, double* y) {
   int r = r0;
   for (; r + 4 <= r1; r += 4) {
     const uint16_t* w0 = W + (size_t)r * cols;
     const uint16_t* w1 = w0 + cols;
     const uint16_t* w2 = w1 + cols;
     const uint16_t* w3 = w2 + cols;
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
     for (int k = 0; k < cols; ++k) {
-      float xk = x[k];
-      a0 += orc_bf16_to_f32(w0[k]) * xk;
-      a1 += orc_bf16_to_f32(w1[k]) * xk;
-      a2 += orc_bf16_to_f32(w2[k]) * xk;
-      a3 += orc_bf16_to_f32(w3[k]) * xk;
+      double xk = x[k];
+      a0 += (double)orc_bf16_to_f32(w0[k]) * xk;
+      a1 += (double)orc_bf16_to_f32(w1[k]) * xk;
+      a2 += (double)orc_bf16_to_f32(w2[k]) * xk;
+      a3 += (double)orc_bf16_to_f32(w3[k]) * xk;
     }
     y[r] = a0; y[r + 1] = a1; y[r + 2] = a2; y[r + 3] = a3;
   }
   for (; r < r1; ++r) {
     const uint16_t* w = W + (size_t)r * cols;
-    float a = 0.0f;
-    for (int k = 0; k < cols; ++k) a += orc_bf16_to_f32(w[k]) * x[k];
+    double a = 0.0;
+    for (int k = 0; k < cols; ++k) a += (double)orc_bf16_to_f32(w[k]) * x[k];
     y[r] = a;
   }
 }
 
-void orc_matvec(const uint16_t* W, int rows, int cols, const float* x, float* y, int n_threads) {
+void orc_matvec(const uint16_t* W, int rows, int cols, const double* x, double* y, int n_threads) {
   if (n_threads <= 1 || rows < 64) {
     matvec_rows(W, 0, rows, cols, x, y);
     return;
@@ -88,28 +94,27 @@ void orc_matvec(const uint16_t* W, int rows, int cols, const float* x, float* y,
 
 /* ------------------------------------------------------------------ */
 /* RMSNorm (Mirage article, "Case 1": the norm divides x by the root   */
-/* mean square; the weight gamma scales each element).                 */
-/*   y_i = (x_i * (1 / sqrt(mean(x^2) + eps))) * gamma_i               */
+/* mean square; the weight gamma scales each element), in fp64:        */
+/*   y_i = x_i * (1 / sqrt(mean(x^2) + eps)) * gamma_i                 */
 /* ------------------------------------------------------------------ */
-void orc_rmsnorm(const float* x, const uint16_t* gamma, int n, float eps, float* y) {
-  float ss = 0.0f;
-  for (int i = 0; i < n; ++i) ss += x[i] * x[i];
-  float r = 1.0f / sqrtf(ss / (float)n + eps);
-  for (int i = 0; i < n; ++i) y[i] = (x[i] * r) * orc_bf16_to_f32(gamma[i]);
+void orc_rmsnorm(const float* x, const uint16_t* gamma, int n, float eps, double* y) {
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+  double r = 1.0 / sqrt(ss / (double)n + (double)eps);
+  for (int i = 0; i < n; ++i) y[i] = (double)x[i] * r * (double)orc_bf16_to_f32(gamma[i]);
 }
 
 /* ------------------------------------------------------------------ */
 /* Rotary position embedding, rotate-half pairing (i, i + d/2) with    */
-/* frequency theta^(-2i/d).  Angle, cos and sin in fp64, then rounded  */
-/* to fp32; the rotation itself in fp32.                               */
+/* frequency theta^(-2i/d); angle, cos, sin and the rotation in fp64.  */
 /* ------------------------------------------------------------------ */
-void orc_rope(float* x, int d, int pos, double theta) {
+void orc_rope(double* x, int d, int pos, double theta) {
   int half = d / 2;
   for (int i = 0; i < half; ++i) {
     double inv_freq = pow(theta, -2.0 * (double)i / (double)d);
     double ang = (double)pos * inv_freq;
-    float c = (float)cos(ang), s = (float)sin(ang);
-    float x0 = x[i], x1 = x[i + half];
+    double c = cos(ang), s = sin(ang);
+    double x0 = x[i], x1 = x[i + half];
     x[i] = x0 * c - x1 * s;
     x[i + half] = x0 * s + x1 * c;
   }
@@ -118,35 +123,36 @@ void orc_rope(float* x, int d, int pos, double theta) {
 /* ------------------------------------------------------------------ */
 /* Attention for one query head (Mirage article, attention example:   */
 /* A = Q K, S = softmax(A), O = S V), with the usual 1/sqrt(d) scale.  */
-/* Softmax subtracts the row max before exponentiating.                */
+/* Softmax subtracts the row max before exponentiating.  All in fp64;  */
+/* the head's output is rounded once to fp32:                           */
+/*   o_c = (sum_j e^{s_j - m} v_jc) / (sum_j e^{s_j - m})              */
 /* ------------------------------------------------------------------ */
-void orc_attend(const float* q, const uint16_t* K, const uint16_t* V, int n, int d, int ld, float* out) {
-  float* s = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
-  float scale = (float)(1.0 / sqrt((double)d));
-  float m = -INFINITY;
+void orc_attend(const double* q, const uint16_t* K, const uint16_t* V, int n, int d, int ld, float* out) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double scale = 1.0 / sqrt((double)d);
+  double m = -INFINITY;
   for (int j = 0; j < n; ++j) {
     const uint16_t* kj = K + (size_t)j * ld;
-    float dot = 0.0f;
-    for (int c = 0; c < d; ++c) dot += q[c] * orc_bf16_to_f32(kj[c]);
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += q[c] * (double)orc_bf16_to_f32(kj[c]);
     s[j] = dot * scale;
     if (s[j] > m) m = s[j];
   }
-  float l = 0.0f;
+  double l = 0.0;
   for (int j = 0; j < n; ++j) {
-    s[j] = expf(s[j] - m);
+    s[j] = exp(s[j] - m);
     l += s[j];
   }
-  for (int j = 0; j < n; ++j) s[j] = s[j] / l;
   for (int c = 0; c < d; ++c) {
-    float o = 0.0f;
-    for (int j = 0; j < n; ++j) o += s[j] * orc_bf16_to_f32(V[(size_t)j * ld + c]);
-    out[c] = o;
+    double o = 0.0;
+    for (int j = 0; j < n; ++j) o += s[j] * (double)orc_bf16_to_f32(V[(size_t)j * ld + c]);
+    out[c] = (float)(o / l);
   }
   free(s);
 }
 
-/* SiLU of the gated MLP (Mirage article, "Case 3: Gated MLP"). */
-float orc_silu(float z) { return z / (1.0f + expf(-z)); }
+/* SiLU of the gated MLP (Mirage article, "Case 3: Gated MLP"), fp64. */
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
 int orc_argmax(const float* x, int n) {
   int best = 0;
@@ -251,17 +257,22 @@ int orc_seq_step(orc_seq* s, int token, float* logits) {
   const int G = Hq / Hkv, QD = Hq * D, KD = Hkv * D, nt = c->n_threads;
   const int pos = s->pos;
   if (pos >= c->max_seq || token < 0 || token >= c->vocab) return -1;
+  const int HF = H > F ? H : F;
 
+  /* stored activations (fp32) */
   float* x = (float*)malloc(sizeof(float) * H);
-  float* h = (float*)malloc(sizeof(float) * (H > F ? H : F));
   float* q = (float*)malloc(sizeof(float) * QD);
   float* k = (float*)malloc(sizeof(float) * KD);
   float* v = (float*)malloc(sizeof(float) * KD);
   float* o = (float*)malloc(sizeof(float) * QD);
-  float* t = (float*)malloc(sizeof(float) * H);
-  float* gt = (float*)malloc(sizeof(float) * F);
-  float* up = (float*)malloc(sizeof(float) * F);
-  float* tmp = (float*)malloc(sizeof(float) * D);
+  float* a = (float*)malloc(sizeof(float) * F);
+  /* intermediates (fp64) */
+  double* h = (double*)malloc(sizeof(double) * HF);
+  double* y = (double*)malloc(sizeof(double) * (QD > HF ? QD : HF));
+  double* gt = (double*)malloc(sizeof(double) * F);
+  double* up = (double*)malloc(sizeof(double) * F);
+  double* qh = (double*)malloc(sizeof(double) * QD);
+  double* kh = (double*)malloc(sizeof(double) * D);
 
   /* embedding lookup */
   for (int i = 0; i < H; ++i) x[i] = orc_bf16_to_f32(W[0][(size_t)token * H + i]);
@@ -274,53 +285,60 @@ int orc_seq_step(orc_seq* s, int token, float* logits) {
     const int b = c->qk_norm ? 7 : 5;
     const uint16_t *ffn_norm = Lw[b], *wg = Lw[b + 1], *wu = Lw[b + 2], *wd = Lw[b + 3];
 
-    /* attention sublayer */
+    /* attention sublayer: q, k, v stored in fp32 */
     orc_rmsnorm(x, attn_norm, H, c->rms_eps, h);
-    orc_matvec(wq, QD, H, h, q, nt);
-    orc_matvec(wk, KD, H, h, k, nt);
-    orc_matvec(wv, KD, H, h, v, nt);
+    orc_matvec(wq, QD, H, h, y, nt);
+    for (int i = 0; i < QD; ++i) q[i] = (float)y[i];
+    orc_matvec(wk, KD, H, h, y, nt);
+    for (int i = 0; i < KD; ++i) k[i] = (float)y[i];
+    orc_matvec(wv, KD, H, h, y, nt);
+    for (int i = 0; i < KD; ++i) v[i] = (float)y[i];
+    /* per-head QK-norm and RoPE in fp64 */
     for (int hh = 0; hh < Hq; ++hh) {
-      if (c->qk_norm) {
-        orc_rmsnorm(q + hh * D, q_norm, D, c->rms_eps, tmp);
-        memcpy(q + hh * D, tmp, sizeof(float) * D);
-      }
-      orc_rope(q + hh * D, D, pos, c->rope_theta);
-    }
-    for (int g = 0; g < Hkv; ++g) {
-      if (c->qk_norm) {
-        orc_rmsnorm(k + g * D, k_norm, D, c->rms_eps, tmp);
-        memcpy(k + g * D, tmp, sizeof(float) * D);
-      }
-      orc_rope(k + g * D, D, pos, c->rope_theta);
+      if (c->qk_norm) orc_rmsnorm(q + hh * D, q_norm, D, c->rms_eps, qh + hh * D);
+      else for (int i = 0; i < D; ++i) qh[hh * D + i] = (double)q[hh * D + i];
+      orc_rope(qh + hh * D, D, pos, c->rope_theta);
     }
     uint16_t* Kl = s->K + (size_t)l * c->max_seq * KD;
     uint16_t* Vl = s->V + (size_t)l * c->max_seq * KD;
-    for (int i = 0; i < KD; ++i) {
-      Kl[(size_t)pos * KD + i] = orc_f32_to_bf16(k[i]);
-      Vl[(size_t)pos * KD + i] = orc_f32_to_bf16(v[i]);
+    for (int g = 0; g < Hkv; ++g) {
+      if (c->qk_norm) orc_rmsnorm(k + g * D, k_norm, D, c->rms_eps, kh);
+      else for (int i = 0; i < D; ++i) kh[i] = (double)k[g * D + i];
+      orc_rope(kh, D, pos, c->rope_theta);
+      /* the rotated key is an fp32 value; the cache holds it, and v, in bf16 */
+      for (int i = 0; i < D; ++i) {
+        Kl[(size_t)pos * KD + g * D + i] = orc_f32_to_bf16((float)kh[i]);
+        Vl[(size_t)pos * KD + g * D + i] = orc_f32_to_bf16(v[g * D + i]);
+      }
     }
     for (int hh = 0; hh < Hq; ++hh) {
       int g = hh / G; /* consecutive query heads share one KV head */
-      orc_attend(q + hh * D, Kl + g * D, Vl + g * D, pos + 1, D, KD, o + hh * D);
+      orc_attend(qh + hh * D, Kl + g * D, Vl + g * D, pos + 1, D, KD, o + hh * D);
     }
-    orc_matvec(wo, H, QD, o, t, nt);
-    for (int i = 0; i < H; ++i) x[i] = x[i] + t[i];
+    for (int i = 0; i < QD; ++i) qh[i] = (double)o[i];
+    orc_matvec(wo, H, QD, qh, y, nt);
+    for (int i = 0; i < H; ++i) x[i] = (float)((double)x[i] + y[i]);
 
     /* MLP sublayer */
     orc_rmsnorm(x, ffn_norm, H, c->rms_eps, h);
     orc_matvec(wg, F, H, h, gt, nt);
     orc_matvec(wu, F, H, h, up, nt);
-    for (int i = 0; i < F; ++i) gt[i] = orc_silu(gt[i]) * up[i];
-    orc_matvec(wd, H, F, gt, t, nt);
-    for (int i = 0; i < H; ++i) x[i] = x[i] + t[i];
+    for (int i = 0; i < F; ++i) a[i] = (float)(orc_silu(gt[i]) * up[i]);
+    for (int i = 0; i < F; ++i) h[i] = (double)a[i];
+    orc_matvec(wd, H, F, h, y, nt);
+    for (int i = 0; i < H; ++i) x[i] = (float)((double)x[i] + y[i]);
   }
 
   if (logits) {
     const int n = orc_n_weights(c);
+    double* lg = (double*)malloc(sizeof(double) * c->vocab);
     orc_rmsnorm(x, W[n - 2], H, c->rms_eps, h);
-    orc_matvec(W[n - 1], c->vocab, H, h, logits, nt);
+    orc_matvec(W[n - 1], c->vocab, H, h, lg, nt);
+    for (int i = 0; i < c->vocab; ++i) logits[i] = (float)lg[i];
+    free(lg);
   }
   s->pos = pos + 1;
-  free(x); free(h); free(q); free(k); free(v); free(o); free(t); free(gt); free(up); free(tmp);
+  free(x); free(q); free(k); free(v); free(o); free(a);
+  free(h); free(y); free(gt); free(up); free(qh); free(kh);
   return 0;
 }

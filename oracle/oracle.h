@@ -14,10 +14,14 @@
  * Linear" for RMSNorm, "Case 3: Gated MLP" for SwiGLU, "Case 4.1" for QK-Norm,
  * and the attention example matmul -> softmax -> matmul).
  *
- * Arithmetic: fp32 activations, bf16 weights widened exactly to fp32, every
- * dot product summed sequentially in ascending index (no reassociation,
- * built with -ffp-contract=off), KV cache rounded to bf16 (round to nearest
- * even) on append.  RoPE angles in fp64, rounded to fp32 cos/sin.
+ * Arithmetic: stored activations (residual stream, raw q/k/v, attention
+ * output, SwiGLU output, logits) are fp32; bf16 weights are widened exactly.
+ * Every operator evaluates in fp64 from its stored inputs -- dot products
+ * summed sequentially in ascending index (no reassociation, built with
+ * -ffp-contract=off), RMSNorm, RoPE (angles, cos, sin and rotation), softmax
+ * with exp, SiLU -- and rounds once to fp32 where the result is stored.  The
+ * KV cache holds the fp32 rotated key and the fp32 value rounded to bf16
+ * (round to nearest even).
  */
 #ifndef MK_ORACLE_H
 #define MK_ORACLE_H
@@ -61,15 +65,16 @@ int orc_seq_step(orc_seq* s, int token, float* logits);
 /* ---- the primitives the decoder is made of (exported so tests can pin them) ---- */
 float orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16(float f);
-/* y[r] = sum_k W[r][k] * x[k], W bf16 [rows][cols] */
-void orc_matvec(const uint16_t* W, int rows, int cols, const float* x, float* y, int n_threads);
-/* y = x * (1/sqrt(mean(x^2)+eps)) * gamma */
-void orc_rmsnorm(const float* x, const uint16_t* gamma, int n, float eps, float* y);
-/* rotate-half RoPE of one head vector of length d at position pos */
-void orc_rope(float* x, int d, int pos, double theta);
-/* single-head softmax attention over n cached bf16 keys/values (row stride ld) */
-void orc_attend(const float* q, const uint16_t* K, const uint16_t* V, int n, int d, int ld, float* out);
-float orc_silu(float z);
+/* y[r] = sum_k W[r][k] * x[k] in fp64, W bf16 [rows][cols] */
+void orc_matvec(const uint16_t* W, int rows, int cols, const double* x, double* y, int n_threads);
+/* y = x * (1/sqrt(mean(x^2)+eps)) * gamma, in fp64 */
+void orc_rmsnorm(const float* x, const uint16_t* gamma, int n, float eps, double* y);
+/* rotate-half RoPE of one head vector of length d at position pos, in place, fp64 */
+void orc_rope(double* x, int d, int pos, double theta);
+/* single-head softmax attention over n cached bf16 keys/values (row stride ld),
+ * evaluated in fp64; the output is rounded to fp32 */
+void orc_attend(const double* q, const uint16_t* K, const uint16_t* V, int n, int d, int ld, float* out);
+double orc_silu(double z);
 /* index of the largest value, lowest index on ties */
 int orc_argmax(const float* x, int n);
 

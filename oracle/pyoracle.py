@@ -24,7 +24,7 @@ def lib():
     global _lib
     if _lib is None:
         L = C.CDLL(ensure_built())
-        u16p, f32p = C.POINTER(C.c_uint16), C.POINTER(C.c_float)
+        u16p, f32p, f64p = C.POINTER(C.c_uint16), C.POINTER(C.c_float), C.POINTER(C.c_double)
         L.orc_n_weights.argtypes = [C.POINTER(OrcCfg)]
         L.orc_weight_numel.argtypes = [C.POINTER(OrcCfg), C.c_int]
         L.orc_weight_numel.restype = C.c_int64
@@ -41,12 +41,12 @@ def lib():
         L.orc_bf16_to_f32.restype = C.c_float
         L.orc_f32_to_bf16.argtypes = [C.c_float]
         L.orc_f32_to_bf16.restype = C.c_uint16
-        L.orc_matvec.argtypes = [u16p, C.c_int, C.c_int, f32p, f32p, C.c_int]
-        L.orc_rmsnorm.argtypes = [f32p, u16p, C.c_int, C.c_float, f32p]
-        L.orc_rope.argtypes = [f32p, C.c_int, C.c_int, C.c_double]
-        L.orc_attend.argtypes = [f32p, u16p, u16p, C.c_int, C.c_int, C.c_int, f32p]
-        L.orc_silu.argtypes = [C.c_float]
-        L.orc_silu.restype = C.c_float
+        L.orc_matvec.argtypes = [u16p, C.c_int, C.c_int, f64p, f64p, C.c_int]
+        L.orc_rmsnorm.argtypes = [f32p, u16p, C.c_int, C.c_float, f64p]
+        L.orc_rope.argtypes = [f64p, C.c_int, C.c_int, C.c_double]
+        L.orc_attend.argtypes = [f64p, u16p, u16p, C.c_int, C.c_int, C.c_int, f32p]
+        L.orc_silu.argtypes = [C.c_double]
+        L.orc_silu.restype = C.c_double
         L.orc_argmax.argtypes = [f32p, C.c_int]
         _lib = L
     return _lib
@@ -55,6 +55,11 @@ def lib():
 def _f32(a):
     a = np.ascontiguousarray(a, dtype=np.float32)
     return a, a.ctypes.data_as(C.POINTER(C.c_float))
+
+
+def _f64(a):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(C.POINTER(C.c_double))
 
 
 def _u16(a):
@@ -72,31 +77,35 @@ def f32_to_bf16(f: float) -> int:
 
 
 def matvec(W16: np.ndarray, x: np.ndarray, n_threads: int = 1) -> np.ndarray:
+    """fp64 W @ x (x is taken as float64)."""
     rows, cols = W16.shape
     W16, wp = _u16(W16)
-    x, xp = _f32(x)
-    y = np.zeros(rows, np.float32)
-    lib().orc_matvec(wp, rows, cols, xp, y.ctypes.data_as(C.POINTER(C.c_float)), n_threads)
+    x, xp = _f64(x)
+    y = np.zeros(rows, np.float64)
+    lib().orc_matvec(wp, rows, cols, xp, y.ctypes.data_as(C.POINTER(C.c_double)), n_threads)
     return y
 
 
 def rmsnorm(x: np.ndarray, gamma16: np.ndarray, eps: float) -> np.ndarray:
+    """fp64 RMSNorm of an fp32 vector."""
     x, xp = _f32(x)
     gamma16, gp = _u16(gamma16)
-    y = np.zeros_like(x)
-    lib().orc_rmsnorm(xp, gp, x.size, eps, y.ctypes.data_as(C.POINTER(C.c_float)))
+    y = np.zeros(x.size, np.float64)
+    lib().orc_rmsnorm(xp, gp, x.size, eps, y.ctypes.data_as(C.POINTER(C.c_double)))
     return y
 
 
 def rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
-    x = np.array(x, dtype=np.float32, copy=True)
-    lib().orc_rope(x.ctypes.data_as(C.POINTER(C.c_float)), x.size, pos, theta)
+    """fp64 rotate-half RoPE."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    lib().orc_rope(x.ctypes.data_as(C.POINTER(C.c_double)), x.size, pos, theta)
     return x
 
 
 def attend(q: np.ndarray, K16: np.ndarray, V16: np.ndarray) -> np.ndarray:
+    """fp64 attention of one head; fp32 output."""
     n, d = K16.shape
-    q, qp = _f32(q)
+    q, qp = _f64(q)
     K16, kp = _u16(K16)
     V16, vp = _u16(V16)
     o = np.zeros(d, np.float32)

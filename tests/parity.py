@@ -8,8 +8,16 @@ from persistent_decode_megakernel_02_amd import synth
 
 MAX_ABS = 3e-2       # per-step max |logit error|
 MEAN_ABS = 3e-3      # per-step mean |logit error|
-STRICT_STEPS = 32    # greedy tokens must agree on the first 32 steps
-GAP = 0.05           # later divergence allowed only where the oracle's top-2 gap is below this
+STRICT_STEPS = 32    # without logits to compare, greedy tokens must agree on the first 32 steps
+GAP = 0.05           # a divergence is allowed only where the oracle's top-2 gap is below this
+
+# Token rule.  The two sides round k and v to bf16 before caching them, so an fp32 difference far below
+# the logit tolerance can move one cached element by a bf16 ulp and shift later logits by ~1e-4; where
+# the oracle's best two logits are closer than that, either token is correct at the precision both sides
+# compute in.  A mismatch is therefore accepted, at any step, only as such a near-tie: the oracle's logit
+# of the GPU's token lies within twice the step's measured max |logit error| of the oracle's best logit,
+# and that gap is below GAP.  The free-running comparison ends there (continuing would feed one side's
+# token to the other).
 
 
 def top2_gap(x: np.ndarray) -> float:
@@ -43,8 +51,14 @@ def compare_free_running(orc: "po.Oracle", seq: int, first_token: int, gpu_token
             assert gt == int(np.argmax(gpu_logits[i])), f"{label} step {i}: token is not the argmax of its logits"
         if gt != ot:
             gap = top2_gap(lo)
-            assert i >= STRICT_STEPS and gap < GAP, \
-                f"{label} step {i}: GPU token {gt} != oracle {ot} (oracle top-2 gap {gap:.4f})"
+            if gpu_logits is None:
+                assert i >= STRICT_STEPS and gap < GAP, \
+                    f"{label} step {i}: GPU token {gt} != oracle {ot} (oracle top-2 gap {gap:.4f})"
+            else:
+                miss = float(lo[ot]) - float(lo[gt])
+                assert miss <= 2.0 * d.max() and miss < GAP, \
+                    f"{label} step {i}: GPU token {gt} != oracle {ot}: oracle logits differ by {miss:.3e} " \
+                    f"(max|d| {d.max():.3e}, top-2 gap {gap:.4f})"
             return i + 1
         tok = ot
     return n

@@ -3,7 +3,11 @@
 Used only to pin the CPU oracle: the oracle decodes token by token through a
 bf16 KV cache; this reference recomputes every prefix from scratch with a
 causal mask in float64, rounding K (after RoPE) and V to bf16 exactly where a
-cache would hold them.  It shares no code with the oracle.
+cache would hold them.  With store32=True it also rounds to fp32 where the
+decoder stores an activation (raw q/k/v, rotated k, attention output,
+residual stream after each sublayer, SwiGLU output, logits); with
+store32=False everything else stays float64.  It shares no code with the
+oracle.
 """
 import numpy as np
 import torch
@@ -33,14 +37,20 @@ def rope_rows(x, positions, theta):
     return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
 
 
-def forward_logits(shape, w: dict, tokens, kv_prefix=None):
+def f32(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def forward_logits(shape, w: dict, tokens, kv_prefix=None, store32=False):
     """Logits [T, V] for every position of `tokens` (all positions causal).
 
     w maps canonical names to float64 arrays.  kv_prefix optionally gives
     pre-filled (K, V) as float64 [L, P, Hkv*D] occupying positions 0..P-1.
     """
+    st = f32 if store32 else (lambda a: a)
     H, D, Hq, Hkv = shape.hidden, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
-    G, eps = Hq // Hkv, shape.rms_eps
+    G = Hq // Hkv
+    eps = float(np.float32(shape.rms_eps))  # the decoder carries eps as an fp32 value
     T = len(tokens)
     P = 0 if kv_prefix is None else kv_prefix[0].shape[1]
     pos = np.arange(P, P + T)
@@ -48,14 +58,14 @@ def forward_logits(shape, w: dict, tokens, kv_prefix=None):
     for layer in range(shape.n_layers):
         p = f"layers.{layer}."
         h = rms(x, w[p + "attn_norm"], eps)
-        q = (h @ w[p + "wq"].T).reshape(T, Hq, D).transpose(1, 0, 2)
-        k = (h @ w[p + "wk"].T).reshape(T, Hkv, D).transpose(1, 0, 2)
-        v = (h @ w[p + "wv"].T).reshape(T, Hkv, D).transpose(1, 0, 2)
+        q = st(h @ w[p + "wq"].T).reshape(T, Hq, D).transpose(1, 0, 2)
+        k = st(h @ w[p + "wk"].T).reshape(T, Hkv, D).transpose(1, 0, 2)
+        v = st(h @ w[p + "wv"].T).reshape(T, Hkv, D).transpose(1, 0, 2)
         if shape.qk_norm:
             q = rms(q, w[p + "q_norm"], eps)
             k = rms(k, w[p + "k_norm"], eps)
         q = rope_rows(q, pos, shape.rope_theta)
-        k = bf16_round(rope_rows(k, pos, shape.rope_theta))
+        k = bf16_round(st(rope_rows(k, pos, shape.rope_theta)))
         v = bf16_round(v)
         if P:
             kp = kv_prefix[0][layer].reshape(P, Hkv, D).transpose(1, 0, 2)
@@ -71,10 +81,10 @@ def forward_logits(shape, w: dict, tokens, kv_prefix=None):
             s = np.where(mask, -np.inf, s)
             s = s - s.max(axis=1, keepdims=True)
             e = np.exp(s)
-            o[hh] = (e / e.sum(axis=1, keepdims=True)) @ v[g]
-        x = x + o.transpose(1, 0, 2).reshape(T, Hq * D) @ w[p + "wo"].T
+            o[hh] = st((e @ v[g]) / e.sum(axis=1, keepdims=True))
+        x = st(x + o.transpose(1, 0, 2).reshape(T, Hq * D) @ w[p + "wo"].T)
         h2 = rms(x, w[p + "ffn_norm"], eps)
         gt = h2 @ w[p + "w_gate"].T
         up = h2 @ w[p + "w_up"].T
-        x = x + (gt / (1.0 + np.exp(-gt)) * up) @ w[p + "w_down"].T
-    return rms(x, w["final_norm"], eps) @ w["lm_head"].T
+        x = st(x + st(gt / (1.0 + np.exp(-gt)) * up) @ w[p + "w_down"].T)
+    return st(rms(x, w["final_norm"], eps) @ w["lm_head"].T)

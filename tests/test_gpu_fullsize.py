@@ -1,0 +1,178 @@
+"""GPU parity at the full Llama-3-8B and Chameleon-7B shapes, in the launch configuration the benchmark
+times (one worker per compute unit, default split, max_seq = start position + decode steps).
+
+The oracle (16 threads) recomputes the first decode steps one by one.  What it cannot reach at the full
+length is covered by properties that hold at any length: every token is the argmax of its own logits,
+every logit is finite, and the per-operator launches and a run split over two launches reproduce the
+single persistent launch bit for bit.
+
+Every case prints its name before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from persistent_decode_megakernel_02_amd import binding as mk  # noqa: E402
+from persistent_decode_megakernel_02_amd import synth  # noqa: E402
+from persistent_decode_megakernel_02_amd.configs import WORKLOADS  # noqa: E402
+from tests.parity import compare_free_running, oracle_for  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ORACLE_THREADS = 16
+N_ORACLE_STEPS = 3
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+class Model:
+    def __init__(self, shape, seed=0):
+        self.shape = shape
+        self.weights = synth.make_weights(shape, seed=seed, device="cuda")
+        self._host = None
+
+    def host(self):
+        if self._host is None:
+            self._host = [(n, t.cpu()) for n, t in self.weights]
+        return self._host
+
+    def free(self):
+        self.weights, self._host = None, None
+        torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def llama():
+    m = Model(WORKLOADS["llama8b_decode512"].model)
+    yield m
+    m.free()
+
+
+def engine_for(model, w, n_steps):
+    eng = mk.Engine(model.shape, batch=w.batch, max_seq=w.start_pos + n_steps)
+    eng.load_weights(model.weights)
+    return eng
+
+
+def sequences(w):
+    return synth.make_sequences(w.model, w.batch, w.prompt_len, w.kv_prefill, seed=w.seed, device="cuda")
+
+
+def restore(eng, w, seqs):
+    if w.prompt_len > 0:
+        eng.prefill(seqs["prompts"].cpu().numpy())
+    else:
+        for b in range(w.batch):
+            eng.load_kv(b, seqs["k"][b], seqs["v"][b], int(seqs["pending"][b]))
+
+
+def check_properties(toks, logits, label):
+    assert np.all(np.isfinite(logits)), f"{label}: non-finite logits"
+    am = logits.argmax(axis=-1)
+    assert np.array_equal(am, toks), f"{label}: a token is not the argmax of its logits"
+    assert toks.min() >= 0 and toks.max() < logits.shape[-1]
+
+
+def oracle_check(model, w, seqs, toks, logits, n_check, label):
+    B = w.batch
+    orc = oracle_for(model.shape, model.host(), max_seq=w.start_pos + n_check, n_seq=B, n_threads=ORACLE_THREADS)
+    try:
+        for b in range(B):
+            if w.prompt_len > 0:
+                prompt = seqs["prompts"][b].cpu().numpy()
+                for t in prompt[:-1]:
+                    orc.step(b, int(t), want_logits=False)
+                first = int(prompt[-1])
+            else:
+                k = synth.bf16_bits(seqs["k"][b])
+                v = synth.bf16_bits(seqs["v"][b])
+                orc.set_kv(b, k, v)
+                first = int(seqs["pending"][b])
+            compare_free_running(orc, b, first, toks[:, b], logits[:, b], n_check=n_check, label=f"{label} seq {b}")
+    finally:
+        orc.close()
+
+
+def test_llama8b_prompt512_matches_oracle_and_modes(llama):
+    w = WORKLOADS["llama8b_decode512"]
+    K = w.n_steps
+    say(f"{w.name}: one persistent launch of {K} steps")
+    seqs = sequences(w)
+    eng = engine_for(llama, w, K)
+    try:
+        restore(eng, w, seqs)
+        toks, logits = eng.decode(K)
+        torch.cuda.synchronize()
+        t_mega, l_mega = toks.cpu().numpy(), logits.cpu().numpy()
+        check_properties(t_mega, l_mega, w.name)
+
+        say(f"{w.name}: two launches of {K // 2} steps")
+        restore(eng, w, seqs)
+        t1, l1 = eng.decode(K // 2)
+        t2, l2 = eng.decode(K - K // 2)
+        torch.cuda.synchronize()
+        assert np.array_equal(np.concatenate([t1.cpu().numpy(), t2.cpu().numpy()]), t_mega)
+        assert np.array_equal(np.concatenate([l1.cpu().numpy(), l2.cpu().numpy()]).view(np.int32),
+                              l_mega.view(np.int32)), "split launch differs from one launch"
+        del t1, l1, t2, l2
+
+        say(f"{w.name}: per-operator launches, {K} steps")
+        eng.set_mode(mk.MK_MODE_PER_OP)
+        restore(eng, w, seqs)
+        tp, lp = eng.decode(K)
+        torch.cuda.synchronize()
+        assert np.array_equal(tp.cpu().numpy(), t_mega)
+        assert np.array_equal(lp.cpu().numpy().view(np.int32), l_mega.view(np.int32)), "per-op differs"
+        del tp, lp
+    finally:
+        eng.close()
+    say(f"{w.name}: oracle, first {N_ORACLE_STEPS} steps")
+    oracle_check(llama, w, seqs, t_mega, l_mega, N_ORACLE_STEPS, w.name)
+
+
+@pytest.mark.parametrize("name", ["llama8b_ctx4096", "llama8b_b1_ctx1024", "llama8b_b4_ctx1024",
+                                  "llama8b_b8_ctx1024", "llama8b_b16_ctx1024"])
+def test_llama8b_prefilled_kv_matches_oracle(llama, name):
+    w = WORKLOADS[name]
+    K = w.n_steps
+    say(f"{name}: one persistent launch of {K} steps (batch {w.batch}, {w.kv_prefill} cached positions)")
+    seqs = sequences(w)
+    eng = engine_for(llama, w, K)
+    try:
+        restore(eng, w, seqs)
+        toks, logits = eng.decode(K)
+        torch.cuda.synchronize()
+        t, lg = toks.cpu().numpy(), logits.cpu().numpy()
+        del toks, logits
+    finally:
+        eng.close()
+    check_properties(t, lg, name)
+    say(f"{name}: oracle, first {N_ORACLE_STEPS if w.batch == 1 else 2} steps")
+    oracle_check(llama, w, seqs, t, lg, N_ORACLE_STEPS if w.batch == 1 else 2, name)
+
+
+def test_chameleon7b_ctx4096_matches_oracle(llama):
+    llama.free()  # the 8B weights are no longer needed by any later case in this module
+    w = WORKLOADS["chameleon7b_ctx4096"]
+    K = w.n_steps
+    say(f"{w.name}: one persistent launch of {K} steps")
+    model = Model(w.model)
+    try:
+        seqs = sequences(w)
+        eng = engine_for(model, w, K)
+        try:
+            restore(eng, w, seqs)
+            toks, logits = eng.decode(K)
+            torch.cuda.synchronize()
+            t, lg = toks.cpu().numpy(), logits.cpu().numpy()
+            del toks, logits
+        finally:
+            eng.close()
+        check_properties(t, lg, w.name)
+        say(f"{w.name}: oracle, first {N_ORACLE_STEPS} steps")
+        oracle_check(model, w, seqs, t, lg, N_ORACLE_STEPS, w.name)
+    finally:
+        model.free()

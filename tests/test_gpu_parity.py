@@ -16,6 +16,10 @@ pytestmark = pytest.mark.gpu
 
 TINY_MHA_QK = ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=4, head_dim=64, ffn=688, vocab=512,
                          qk_norm=True)
+# wide enough that at batch 8 and 16 the activations exceed the LDS staging area and every GEMV runs in
+# K slices (the last one ragged)
+WIDE = ModelShape(n_layers=2, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn=5632, vocab=3000,
+                  rope_theta=500000.0)
 TINY_G4 = ModelShape(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1000, vocab=2000,
                      rope_theta=500000.0)
 
@@ -38,10 +42,10 @@ def run_prompt_case(shape, batch, prompt_len, n_steps, mode=mk.MK_MODE_MEGAKERNE
     return weights, seqs, out
 
 
-def check_against_oracle(shape, weights, seqs, toks, logits, n_steps, label):
+def check_against_oracle(shape, weights, seqs, toks, logits, n_steps, label, n_threads=1):
     batch = toks.shape[1]
     P = seqs["prompts"].shape[1]
-    orc = oracle_for(shape, weights, max_seq=P - 1 + n_steps, n_seq=batch)
+    orc = oracle_for(shape, weights, max_seq=P - 1 + n_steps, n_seq=batch, n_threads=n_threads)
     for b in range(batch):
         prompt = seqs["prompts"][b].numpy()
         for t in prompt[:-1]:
@@ -124,3 +128,10 @@ def test_prefilled_kv_matches_oracle():
     for b in range(B):
         orc.set_kv(b, synth.bf16_bits(seqs["k"][b]), synth.bf16_bits(seqs["v"][b]))
         compare_free_running(orc, b, int(seqs["pending"][b]), toks[:, b], logits[:, b], label=f"kv seq {b}")
+
+
+@pytest.mark.parametrize("batch,prompt,steps", [(8, 9, 24), (16, 5, 20)])
+def test_k_sliced_batches_match_oracle(batch, prompt, steps):
+    say(f"wide batch={batch}: K-sliced activation staging")
+    w, s, (toks, logits) = run_prompt_case(WIDE, batch, prompt, steps)
+    check_against_oracle(WIDE, w, s, toks, logits, steps, f"wide-b{batch}", n_threads=16)
