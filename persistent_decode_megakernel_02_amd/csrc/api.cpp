@@ -24,15 +24,22 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* 
 hipError_t launch_copy_probe(void* buf, size_t bytes, int n_wg, hipStream_t st);
 size_t lds_bytes(const KParams& P);
 int max_coresident_workers(int B, size_t lds);
-constexpr int kXsFloats = 28672;
-constexpr int kRedFloats = 8192;
+constexpr int kLdsBytes = 163840;  // one worker per compute unit takes all of its LDS
+constexpr int kMiscBytes = 4096;   // per-worker scalars at the top of LDS (same size as in the kernels)
 constexpr uint32_t kDefaultWatchdog = 1u << 22;  // ~1-2 us per poll: several seconds, far above any healthy wait
 }  // namespace mk
 
 using namespace mk;
 
+// LDS of one worker: [activation staging, fp64][GEMV row sums, fp64][misc].  Attention tasks reuse the
+// space below misc for q/k/v, rotated queries, scores and per-wave P.V sums.
+struct LdsPlan {
+  int xs_doubles, red_doubles, red_off, misc_off;
+};
+
 struct mk_ctx {
   mk_model_cfg cfg{};
+  LdsPlan lds{};
   Graph g;
   hipStream_t stream = nullptr;
   int device = 0;
@@ -45,7 +52,7 @@ struct mk_ctx {
   LayerW* d_layers = nullptr;
   std::vector<LayerW> h_layers;
   uint16_t *embed = nullptr, *final_norm = nullptr, *lm_head = nullptr;
-  float *rope_cos = nullptr, *rope_sin = nullptr;
+  double *rope_cos = nullptr, *rope_sin = nullptr;
   uint16_t *kc = nullptr, *vc = nullptr;
   size_t kv_elems = 0;
   float *x = nullptr, *qkv = nullptr, *o = nullptr, *a = nullptr;
@@ -108,26 +115,33 @@ static std::string validate(const mk_model_cfg& cfg) {
   return "";
 }
 
-static int check_capacity(const mk_model_cfg& cfg, const Graph& g, std::string* why) {
-  const int D = cfg.head_dim, G = cfg.n_q_heads / cfg.n_kv_heads;
+static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::string* why) {
+  const int D = cfg.head_dim, G = cfg.n_q_heads / cfg.n_kv_heads, B = cfg.batch;
   const int S = g.split;
   const int lpp = D / 8, ppb = 512 / lpp;
   if (S > 5 * ppb) {
     *why = "split too large for head_dim (at most 20480 / head_dim)";
     return MK_ERR_UNSUPPORTED;
   }
-  const int att_floats = (G + 2) * D + G * D + D + G * S + std::max(8 * G * D, 3 * G * g.n_splits);
-  if (att_floats > kXsFloats) {
+  const int64_t att_bytes = (int64_t)(G + 2) * D * 4 + (int64_t)G * D * 8 + 2 * D * 2 + (int64_t)G * S * 8 +
+                            (int64_t)std::max(8 * G * D, 3 * G * g.n_splits) * 8;
+  auto maxrows = [](int R, int T) { return (R + T - 1) / T; };
+  const int worst = std::max({maxrows(cfg.hidden, g.n_wo), maxrows(cfg.ffn, g.n_gu) * 2, maxrows(cfg.hidden, g.n_down),
+                              maxrows(cfg.vocab, g.n_lm), (G + 2) * D / g.qkv_tiles_per_group + 1});
+  LdsPlan L;
+  L.red_doubles = (worst * B + 1) / 2 * 2;
+  L.misc_off = kLdsBytes - kMiscBytes;
+  L.red_off = L.misc_off - L.red_doubles * 8;
+  L.xs_doubles = L.red_off / 8;
+  if (L.xs_doubles / B < 512) {
+    *why = "a GEMV tile has too many rows for LDS at this batch (use more workers or a smaller batch)";
+    return MK_ERR_UNSUPPORTED;
+  }
+  if (att_bytes > L.misc_off) {
     *why = "attention working set exceeds LDS";
     return MK_ERR_UNSUPPORTED;
   }
-  auto maxrows = [](int R, int T) { return (R + T - 1) / T; };
-  int worst = std::max({maxrows(cfg.hidden, g.n_wo) * 1, maxrows(cfg.ffn, g.n_gu) * 2, maxrows(cfg.vocab, g.n_lm),
-                        (G + 2) * D / g.qkv_tiles_per_group + 1});
-  if ((int64_t)worst * cfg.batch > kRedFloats) {
-    *why = "a GEMV tile has too many rows for the reduction buffer (use more workers or a smaller batch)";
-    return MK_ERR_UNSUPPORTED;
-  }
+  *out = L;
   return MK_OK;
 }
 
@@ -171,12 +185,14 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   int nw = cfg.n_workers > 0 ? cfg.n_workers : prop.multiProcessorCount;
   why = build_graph(cfg, nw, &c->g);
   if (!why.empty()) return bail(fail(c, MK_ERR_UNSUPPORTED, why));
-  int rc = check_capacity(cfg, c->g, &why);
+  LdsPlan lp{};
+  int rc = plan_lds(cfg, c->g, &lp, &why);
   if (rc) return bail(fail(c, rc, why));
+  c->lds = lp;
   if (prepare_kernels(cfg.batch) != hipSuccess) return bail(fail(c, MK_ERR_HIP, "hipFuncSetAttribute failed"));
   {
     KParams tmp{};
-    tmp.xs_floats = kXsFloats;
+    tmp.misc_off = lp.misc_off;
     const int per_cu = max_coresident_workers(cfg.batch, lds_bytes(tmp));
     if (per_cu < 1 || (int64_t)per_cu * prop.multiProcessorCount < nw)
       return bail(fail(c, MK_ERR_UNSUPPORTED, "workers cannot all be resident at once (cooperative launch)"));
@@ -243,20 +259,20 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
     return bail(fail(c, MK_ERR_HIP, "layer table upload"));
   (void)G;
 
-  // ---- RoPE tables: angle pos * theta^(-2i/D) in fp64, rounded to fp32
+  // ---- RoPE tables: angle pos * theta^(-2i/D), cos and sin, all in fp64
   {
     const int half = D / 2;
-    std::vector<float> hc((size_t)cfg.max_seq * half), hs(hc.size());
+    std::vector<double> hc((size_t)cfg.max_seq * half), hs(hc.size());
     for (int p = 0; p < cfg.max_seq; ++p)
       for (int i = 0; i < half; ++i) {
         const double ang = (double)p * std::pow(cfg.rope_theta, -2.0 * (double)i / (double)D);
-        hc[(size_t)p * half + i] = (float)std::cos(ang);
-        hs[(size_t)p * half + i] = (float)std::sin(ang);
+        hc[(size_t)p * half + i] = std::cos(ang);
+        hs[(size_t)p * half + i] = std::sin(ang);
       }
-    if ((rc = dalloc(c, (void**)&c->rope_cos, hc.size() * 4))) return bail(rc);
-    if ((rc = dalloc(c, (void**)&c->rope_sin, hs.size() * 4))) return bail(rc);
-    if (hipMemcpy(c->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(c->rope_sin, hs.data(), hs.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+    if ((rc = dalloc(c, (void**)&c->rope_cos, hc.size() * 8))) return bail(rc);
+    if ((rc = dalloc(c, (void**)&c->rope_sin, hs.size() * 8))) return bail(rc);
+    if (hipMemcpy(c->rope_cos, hc.data(), hc.size() * 8, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(c->rope_sin, hs.data(), hs.size() * 8, hipMemcpyHostToDevice) != hipSuccess)
       return bail(fail(c, MK_ERR_HIP, "rope upload"));
   }
 
@@ -269,8 +285,8 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if ((rc = dalloc(c, (void**)&c->qkv, (size_t)B * QKVR * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->o, (size_t)B * QD * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->a, (size_t)B * F * 4))) return bail(rc);
-  c->n_part_ml = (size_t)B * Hkv * NS * G * 2;
-  c->n_part_acc = (size_t)B * Hkv * NS * G * D;
+  c->n_part_ml = (size_t)B * Hkv * NS * G * 2 * 2;  // (max, sum), each fp64 as two tagged words
+  c->n_part_acc = (size_t)B * Hkv * NS * G * D * 2;
   if ((rc = dalloc(c, (void**)&c->part_ml, c->n_part_ml * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->part_acc, c->n_part_acc * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->lm_part, (size_t)B * c->g.n_lm * sizeof(LmPart)))) return bail(rc);
@@ -396,14 +412,17 @@ static KParams make_params(mk_ctx* c) {
   P.NS = c->g.n_splits;
   P.qk_norm = cfg.qk_norm;
   P.eps = cfg.rms_eps;
-  P.attn_scale = (float)(1.0 / std::sqrt((double)cfg.head_dim));
+  P.attn_scale = 1.0 / std::sqrt((double)cfg.head_dim);
   P.n_workers = c->g.n_workers;
   P.n_qkv = c->g.n_qkv;
   P.n_wo = c->g.n_wo;
   P.n_gu = c->g.n_gu;
   P.n_down = c->g.n_down;
   P.n_lm = c->g.n_lm;
-  P.xs_floats = kXsFloats;
+  P.xs_doubles = c->lds.xs_doubles;
+  P.red_doubles = c->lds.red_doubles;
+  P.red_off = c->lds.red_off;
+  P.misc_off = c->lds.misc_off;
   P.layers = c->d_layers;
   P.embed = c->embed;
   P.final_norm = c->final_norm;

@@ -28,7 +28,6 @@ constexpr int NT = 512;  // threads per worker
 constexpr int NW = NT / 64;
 constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
 constexpr int DEPTH = 4;   // pipeline groups in flight per wave (16 KB per wave)
-constexpr int RED_FLOATS = 8192;
 constexpr int MISC_BYTES = 4096;
 constexpr int ATT_MAXL = 5;  // K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8))
 
@@ -38,16 +37,16 @@ constexpr int ATT_MAXL = 5;  // K/V 16-byte loads per thread per attention task 
 #define GAS __attribute__((address_space(1)))
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v2d __attribute__((ext_vector_type(2)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 struct Misc {
-  float r[16];          // RMSNorm scale per sequence
   int32_t tok[16];      // tokens of this step (layer-0 QKV)
-  float wred[NW][16];   // per-wave partial sums
+  double wred[NW][16];  // per-wave partial sums of squares (RMSNorm)
   float wval[NW][16];   // per-wave argmax values
   int32_t widx[NW][16]; // per-wave argmax indices
-  float hr[16];         // QK-norm scales
-  float ml[8][2];       // attention (max, sum) per head
+  double hr[16];        // QK-norm scales
+  double ml[8][2];      // attention (max, sum) per head
   int32_t flag;
 };
 static_assert(sizeof(Misc) <= MISC_BYTES, "misc");
@@ -183,6 +182,50 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0x140>(v));
   return xor32_pair_max(xor16_pair_max(v));
 }
+// fp64 versions: the two 32-bit halves move through the same lane permutation
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double xor16_pair_d(double v) {
+  const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+  return __hiloint2double((int)h[0], (int)l[0]) + __hiloint2double((int)h[1], (int)l[1]);
+}
+__device__ __forceinline__ double xor32_pair_d(double v) {
+  const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+  return __hiloint2double((int)h[0], (int)l[0]) + __hiloint2double((int)h[1], (int)l[1]);
+}
+__device__ __forceinline__ double xor16_pair_max_d(double v) {
+  const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+  return fmax(__hiloint2double((int)h[0], (int)l[0]), __hiloint2double((int)h[1], (int)l[1]));
+}
+__device__ __forceinline__ double xor32_pair_max_d(double v) {
+  const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)__double2loint(v), (uint32_t)__double2loint(v), false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)__double2hiint(v), (uint32_t)__double2hiint(v), false, false);
+  return fmax(__hiloint2double((int)h[0], (int)l[0]), __hiloint2double((int)h[1], (int)l[1]));
+}
+template <int N>
+__device__ __forceinline__ double group_sum_d(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  if (N >= 8) v += dpp_d<0x141>(v);
+  if (N >= 16) v += dpp_d<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) { return xor32_pair_d(xor16_pair_d(group_sum_d<16>(v))); }
+__device__ __forceinline__ double wave_max_d(double v) {
+  v = fmax(v, dpp_d<0xB1>(v));
+  v = fmax(v, dpp_d<0x4E>(v));
+  v = fmax(v, dpp_d<0x141>(v));
+  v = fmax(v, dpp_d<0x140>(v));
+  return xor32_pair_max_d(xor16_pair_max_d(v));
+}
+
 // larger value wins; equal values: lower index wins
 __device__ __forceinline__ void amax_merge(float& v, int32_t& i, float v2, int32_t i2) {
   if (v2 > v || (v2 == v && i2 < i)) {
@@ -199,7 +242,7 @@ __device__ __forceinline__ void wave_amax(float& v, int32_t& i) {
   }
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ double silu_d(double z) { return z / (1.0 + exp(-z)); }
 
 // ---------------------------------------------------------------------------
 // events
@@ -301,16 +344,19 @@ __device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMV task: rows [a0, a1) of one weight matrix against B activation vectors
+// GEMV task: rows [a0, a1) of one weight matrix against B activation vectors.
+// Numerics: the staged activation x_k * gamma_k and every product with a bf16
+// weight are exact in fp64; each row is summed in fp64 (lane-serial, then a
+// fixed tree) and the result is rounded once to fp32 where it is stored.
 // ---------------------------------------------------------------------------
 template <int NB>
 __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                           uint64_t* tr) {
   const int op = (int)t.op, l = (int)t.layer;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
-  float* xs = (float*)lds;
-  float* red = (float*)(lds + (size_t)P.xs_floats * 4);
-  Misc* m = (Misc*)(lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+  double* xs = (double*)lds;
+  double* red = (double*)(lds + P.red_off);
+  Misc* m = (Misc*)(lds + P.misc_off);
   const LayerW LW = ldg(P.layers + (op == OP_LM ? 0 : l));
 
   const uint16_t* W0;
@@ -329,7 +375,8 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   const int u0 = (int)t.a0, nu = (int)t.a1 - (int)t.a0;
   const int my_units = nu > w ? (nu - w + NW - 1) / NW : 0;
   const int my_rows = my_units * RU;
-  const int kc = min(K, (P.xs_floats / NB) / 512 * 512);
+  const int kc = min(K, (P.xs_doubles / NB) / 512 * 512);
+  const int ps = kc >> 2;  // one plane: elements (2p, 2p+1) of every 8-element chunk, kc/8 pairs
   const int nsl = (K + kc - 1) / kc;
 
   auto rowptr = [&](int r) -> const uint16_t* {
@@ -369,9 +416,9 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     if (ir < my_rows) issue_nocheck(b);
   };
 
-  float acc[NB];
+  double acc[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  for (int b = 0; b < NB; ++b) acc[b] = 0.0;
   int sl_cur = 0;
   auto consume = [&](const uint4 (&bw)[CG]) {
 #pragma unroll
@@ -380,26 +427,29 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       const bool ok = jr < nch8;
       const int j = ok ? jr : nch8 - 1;
       const uint32_t wv[4] = {ok ? bw[c].x : 0u, ok ? bw[c].y : 0u, ok ? bw[c].z : 0u, ok ? bw[c].w : 0u};
-      float wf[8];
+      double wd[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        wf[2 * e] = bf_lo(wv[e]);
-        wf[2 * e + 1] = bf_hi(wv[e]);
+        wd[2 * e] = (double)bf_lo(wv[e]);
+        wd[2 * e + 1] = (double)bf_hi(wv[e]);
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        // two planes per sequence: elements 0-3 and 4-7 of every 8-element chunk
-        const v4f x0 = *(const v4f*)(xs + (size_t)b * kc + j * 4);
-        const v4f x1 = *(const v4f*)(xs + (size_t)b * kc + (kc >> 1) + j * 4);
-        float a = acc[b];
-        a = fmaf(wf[0], x0.x, a);
-        a = fmaf(wf[1], x0.y, a);
-        a = fmaf(wf[2], x0.z, a);
-        a = fmaf(wf[3], x0.w, a);
-        a = fmaf(wf[4], x1.x, a);
-        a = fmaf(wf[5], x1.y, a);
-        a = fmaf(wf[6], x1.z, a);
-        a = fmaf(wf[7], x1.w, a);
+        // four planes per sequence, so that consecutive lanes read consecutive 16-byte pairs
+        const double* xb = xs + (size_t)b * kc + j * 2;
+        const v2d x0 = *(const v2d*)(xb);
+        const v2d x1 = *(const v2d*)(xb + ps);
+        const v2d x2 = *(const v2d*)(xb + 2 * ps);
+        const v2d x3 = *(const v2d*)(xb + 3 * ps);
+        double a = acc[b];
+        a = fma(wd[0], x0.x, a);
+        a = fma(wd[1], x0.y, a);
+        a = fma(wd[2], x1.x, a);
+        a = fma(wd[3], x1.y, a);
+        a = fma(wd[4], x2.x, a);
+        a = fma(wd[5], x2.y, a);
+        a = fma(wd[6], x3.x, a);
+        a = fma(wd[7], x3.y, a);
         acc[b] = a;
       }
     }
@@ -409,9 +459,9 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       const int rl = (w + NW * ui) * RU + (RU == 2 ? (cr & 1) : 0);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float v = wave_sum(acc[b]);
+        const double v = wave_sum_d(acc[b]);
         if (lane == 0) red[rl * NB + b] = sl_cur == 0 ? v : red[rl * NB + b] + v;
-        acc[b] = 0.f;
+        acc[b] = 0.0;
       }
       ++cr;
     }
@@ -457,12 +507,12 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) issue(buf[d]);
     }
-    // ---- stage activations of this slice into LDS (x * gamma); norm scale on slice 0
+    // ---- stage activations of this slice into LDS (x * gamma, exact in fp64); sum of squares on slice 0
     {
       const int ks = min(kc, K - k0);
-      float ss[NB];
+      double ss[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+      for (int b = 0; b < NB; ++b) ss[b] = 0.0;
       const int e_lo = (sl == 0 && norm) ? 0 : k0, e_hi = (sl == 0 && norm) ? K : k0 + ks;
       constexpr int SU = NB >= 8 ? 1 : 8 / NB;  // 16-byte loads in flight per thread and sequence
       for (int base = e_lo + tid * 4; base < e_hi; base += NT * 4 * SU) {
@@ -501,11 +551,15 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
               const v4f x = v[u][b];
-              if (norm && sl == 0) ss[b] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+              if (norm && sl == 0) {
+                const double d0 = x.x, d1 = x.y, d2 = x.z, d3 = x.w;
+                ss[b] += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
+              }
               if (e >= k0 && e < k0 + ks) {
                 const int el = e - k0;
-                *(v4f*)(xs + (size_t)b * kc + ((el >> 2) & 1) * (kc >> 1) + (el >> 3) * 4) =
-                    v4f{x.x * g4[0], x.y * g4[1], x.z * g4[2], x.w * g4[3]};
+                double* xb = xs + (size_t)b * kc + ((el >> 2) & 1) * 2 * ps + (el >> 3) * 2;
+                *(v2d*)xb = v2d{(double)x.x * (double)g4[0], (double)x.y * (double)g4[1]};
+                *(v2d*)(xb + ps) = v2d{(double)x.z * (double)g4[2], (double)x.w * (double)g4[3]};
               }
             }
           }
@@ -514,7 +568,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       if (norm && sl == 0) {  // per-wave partial sums; the scale itself is formed in the epilogue
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const float v = wave_sum(ss[b]);
+          const double v = wave_sum_d(ss[b]);
           if (lane == 0) m->wred[w][b] = v;
         }
       }
@@ -549,33 +603,33 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   }
   __syncthreads();
 
-  // ---- RMSNorm scale r = 1/sqrt(mean(x^2) + eps), applied after the dot products
-  float rs[NB];
+  // ---- RMSNorm scale r = 1/sqrt(mean(x^2) + eps) in fp64, applied after the dot products
+  double rs[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float tot = 0.f;
+    double tot = 0.0;
     for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][b];
-    rs[b] = norm ? 1.0f / sqrtf(tot / (float)K + P.eps) : 1.0f;
+    rs[b] = norm ? 1.0 / sqrt(tot / (double)K + (double)P.eps) : 1.0;
   }
 
   // ---- epilogue per operator
   if (op == OP_QKV) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, red[ul * NB + b] * rs[b]);
+      stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, (float)(red[ul * NB + b] * rs[b]));
     }
   } else if (op == OP_WO || op == OP_DOWN) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
       float* xp = P.x + (size_t)b * P.H + u0 + ul;
-      stc(xp, ldc(xp) + red[ul * NB + b]);
+      stc(xp, (float)((double)ldc(xp) + red[ul * NB + b]));
     }
   } else if (op == OP_GU) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      const float gt = red[(ul * 2) * NB + b] * rs[b];
-      const float up = red[(ul * 2 + 1) * NB + b] * rs[b];
-      stc(P.a + (size_t)b * P.F + u0 + ul, silu(gt) * up);
+      const double gt = red[(ul * 2) * NB + b] * rs[b];
+      const double up = red[(ul * 2 + 1) * NB + b] * rs[b];
+      stc(P.a + (size_t)b * P.F + u0 + ul, (float)(silu_d(gt) * up));
     }
   } else {  // OP_LM
     float bv[NB];
@@ -588,7 +642,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     for (int ul = tid; ul < nu; ul += NT) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float logit = red[ul * NB + b] * rs[b];
+        const float logit = (float)(red[ul * NB + b] * rs[b]);
         if (P.out_logits) stg(P.out_logits + ((size_t)s * P.B + b) * P.V + u0 + ul, logit);
         amax_merge(bv[b], bi[b], logit, u0 + ul);
       }
@@ -621,21 +675,26 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 // then appends to the cache), scores over the split's positions, and the
 // split's softmax partial: max m, sum l = sum_j e^{t_j - m}, and the
 // unnormalised acc = sum_j e^{t_j - m} v_j (FlashDecoding-style split-KV, as
-// in the Mirage article's attention search space).  Partials are stored with
-// their step tag.  The split holding the current position merges all splits
-// in ascending order with the online rule
-//   M' = max(M, m_s); num = num e^{M - M'} + acc_s e^{m_s - M'};
-//   den = den e^{M - M'} + l_s e^{m_s - M'};   o = num / den.
+// in the Mirage article's attention search space).  Everything is evaluated
+// in fp64; partials are stored as tagged fp64 words.  The split holding the
+// current position merges all splits in ascending order:
+//   M = max_s m_s;  den = sum_s e^{m_s - M} l_s;  o = sum_s e^{m_s - M} acc_s / den,
+// and rounds o once to fp32.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void st_tv(TV* p, float v, uint32_t tag) {
-  const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
+__device__ __forceinline__ void st_tv(TV* p, uint32_t bits, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | bits;
   __hip_atomic_store((GAS uint64_t*)p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_tv(const TV* p) {
   return __hip_atomic_load((const GAS uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float tv_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 __device__ __forceinline__ bool tv_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+// an fp64 value as two tagged words: p[0] low half, p[1] high half
+__device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
+  st_tv(p, (uint32_t)__double2loint(v), tag);
+  st_tv(p + 1, (uint32_t)__double2hiint(v), tag);
+}
+__device__ __forceinline__ double tvd_val(uint64_t lo, uint64_t hi) { return __hiloint2double((int)(uint32_t)hi, (int)(uint32_t)lo); }
 
 template <int G, int LPP>
 __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
@@ -669,16 +728,15 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
   }
 
-  float* fl = (float*)lds;
-  Misc* m = (Misc*)(lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+  Misc* m = (Misc*)(lds + P.misc_off);
   if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr)) return false;
 
-  float* raw = fl;                             // [(G+2) D]: q heads, k, v
-  float* qrot = raw + (G + 2) * D;             // [G D]
+  float* raw = (float*)lds;                    // [(G+2) D]: q heads, k, v as stored (fp32)
+  double* qrot = (double*)(raw + (G + 2) * D); // [G D]
   uint16_t* kcur = (uint16_t*)(qrot + G * D);  // [D]
   uint16_t* vcur = kcur + D;                   // [D]
-  float* sc = (float*)(vcur + D);              // [G S]
-  float* accw = sc + G * S;                    // [NW G D]
+  double* sc = (double*)(vcur + D);            // [G S]
+  double* accw = sc + G * S;                   // [NW G D]
 
   const float* src = P.qkv + (size_t)b * P.QKVR + (size_t)g * P.RG;
   for (int i = tid * 4; i < (G + 2) * D; i += NT * 4) *(v4f*)(raw + i) = ldc4(src, (uint32_t)i);
@@ -686,33 +744,33 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   const int nh = G + (has_cur ? 1 : 0);  // heads to rotate (q heads, then k)
   if (P.qk_norm) {
     for (int h = w; h < nh; h += NW) {
-      float ss = 0.f;
-      for (int d = lane; d < D; d += 64) ss += raw[h * D + d] * raw[h * D + d];
-      ss = wave_sum(ss);
-      if (lane == 0) m->hr[h] = 1.0f / sqrtf(ss / (float)D + P.eps);
+      double ss = 0.0;
+      for (int d = lane; d < D; d += 64) ss += (double)raw[h * D + d] * (double)raw[h * D + d];
+      ss = wave_sum_d(ss);
+      if (lane == 0) m->hr[h] = 1.0 / sqrt(ss / (double)D + (double)P.eps);
     }
     __syncthreads();
   }
   constexpr int half = D / 2;
-  const float* cs = P.rope_cos + (size_t)pos * half;
-  const float* sn = P.rope_sin + (size_t)pos * half;
+  const double* cs = P.rope_cos + (size_t)pos * half;
+  const double* sn = P.rope_sin + (size_t)pos * half;
   const LayerW LW = ldg(P.layers + l);
   for (int i = tid; i < nh * half; i += NT) {
     const int h = i / half, k = i - h * half;
-    float x0 = raw[h * D + k], x1 = raw[h * D + k + half];
+    double x0 = raw[h * D + k], x1 = raw[h * D + k + half];
     if (P.qk_norm) {
       const uint16_t* gm = h < G ? LW.q_norm : LW.k_norm;
-      x0 = (x0 * m->hr[h]) * bf1(ldg(gm + k));
-      x1 = (x1 * m->hr[h]) * bf1(ldg(gm + k + half));
+      x0 = (x0 * m->hr[h]) * (double)bf1(ldg(gm + k));
+      x1 = (x1 * m->hr[h]) * (double)bf1(ldg(gm + k + half));
     }
-    const float c = ldg(cs + k), sv = ldg(sn + k);
-    const float y0 = x0 * c - x1 * sv, y1 = x0 * sv + x1 * c;
+    const double c = ldg(cs + k), sv = ldg(sn + k);
+    const double y0 = x0 * c - x1 * sv, y1 = x0 * sv + x1 * c;
     if (h < G) {
       qrot[h * D + k] = y0;
       qrot[h * D + k + half] = y1;
-    } else {
-      kcur[k] = f2bf(y0);
-      kcur[k + half] = f2bf(y1);
+    } else {  // the rotated key is an fp32 value; the cache holds it in bf16
+      kcur[k] = f2bf((float)y0);
+      kcur[k + half] = f2bf((float)y1);
     }
   }
   if (has_cur)
@@ -724,7 +782,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   }
 
   // ---- scores t_j = (q_h . k_j) / sqrt(D); LPP lanes share one position
-  float q[G][8];
+  double q[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -737,13 +795,13 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
       const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float a = 0.f;
+        double a = 0.0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a = fmaf(q[h][2 * e], bf_lo(kw[e]), a);
-          a = fmaf(q[h][2 * e + 1], bf_hi(kw[e]), a);
+          a = fma(q[h][2 * e], (double)bf_lo(kw[e]), a);
+          a = fma(q[h][2 * e + 1], (double)bf_hi(kw[e]), a);
         }
-        a = group_sum<LPP>(a);
+        a = group_sum_d<LPP>(a);
         if (jr < S && j < j1 && lp == 0) sc[h * S + jr] = a * P.attn_scale;
       }
     }
@@ -752,16 +810,16 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   // ---- split softmax statistics per head
   const int n = j1 - j0;
   for (int h = w; h < G; h += NW) {
-    float mx = -INFINITY;
-    for (int jr = lane; jr < n; jr += 64) mx = fmaxf(mx, sc[h * S + jr]);
-    mx = wave_max(mx);
-    float ls = 0.f;
+    double mx = -INFINITY;
+    for (int jr = lane; jr < n; jr += 64) mx = fmax(mx, sc[h * S + jr]);
+    mx = wave_max_d(mx);
+    double ls = 0.0;
     for (int jr = lane; jr < n; jr += 64) {
-      const float p = expf(sc[h * S + jr] - mx);
+      const double p = exp(sc[h * S + jr] - mx);
       sc[h * S + jr] = p;
       ls += p;
     }
-    ls = wave_sum(ls);
+    ls = wave_sum_d(ls);
     if (lane == 0) {
       m->ml[h][0] = mx;
       m->ml[h][1] = ls;
@@ -769,11 +827,11 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   }
   __syncthreads();
   // ---- unnormalised P.V
-  float acc[G][8];
+  double acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0;
 #pragma unroll
   for (int i = 0; i < ATT_MAXL; ++i) {
     const int jr = po + i * PPB, j = j0 + jr;
@@ -782,11 +840,11 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
       const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = sc[h * S + jr];
+        const double p = sc[h * S + jr];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[h][2 * e] = fmaf(p, bf_lo(vw[e]), acc[h][2 * e]);
-          acc[h][2 * e + 1] = fmaf(p, bf_hi(vw[e]), acc[h][2 * e + 1]);
+          acc[h][2 * e] = fma(p, (double)bf_lo(vw[e]), acc[h][2 * e]);
+          acc[h][2 * e + 1] = fma(p, (double)bf_hi(vw[e]), acc[h][2 * e + 1]);
         }
       }
     }
@@ -796,9 +854,9 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = acc[h][e];
-      if (LPP == 8) v += dpp<0x128>(v);  // row_ror:8 (lane i and i^8)
-      acc[h][e] = xor32_pair(xor16_pair(v));
+      double v = acc[h][e];
+      if (LPP == 8) v += dpp_d<0x128>(v);  // row_ror:8 (lane i and i^8)
+      acc[h][e] = xor32_pair_d(xor16_pair_d(v));
     }
   if (lane < LPP)
 #pragma unroll
@@ -809,49 +867,50 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   // ---- this split's partial, tagged with the step
   const size_t pbase = ((size_t)bg * P.NS + sp) * G;
   for (int i = tid; i < G * D; i += NT) {
-    float v = 0.f;
+    double v = 0.0;
     for (int ww = 0; ww < NW; ++ww) v += accw[ww * G * D + i];
-    st_tv(P.part_acc + pbase * D + i, v, tag);
+    st_tvd(P.part_acc + (pbase * D + i) * 2, v, tag);
   }
   if (tid < G) {
-    st_tv(P.part_ml + (pbase + tid) * 2, m->ml[tid][0], tag);
-    st_tv(P.part_ml + (pbase + tid) * 2 + 1, m->ml[tid][1], tag);
+    st_tvd(P.part_ml + ((pbase + tid) * 2) * 2, m->ml[tid][0], tag);
+    st_tvd(P.part_ml + ((pbase + tid) * 2 + 1) * 2, m->ml[tid][1], tag);
   }
   if (!has_cur) {
     __syncthreads();
     return true;
   }
-  // ---- merge every split of (b, g) in ascending order, polling the others' partials:
-  //   M = max_s m_s,  den = sum_s e^{m_s - M} l_s,  o = sum_s e^{m_s - M} acc_s / den.
+  // ---- merge every split of (b, g) in ascending order, polling the others' partials.
   // Pass 1 gathers every (m_s, l_s) into LDS in one round trip; pass 2 issues
-  // the accumulator loads of up to 16 splits at once.
+  // the accumulator loads of up to 8 splits at once.
   const size_t b0 = (size_t)bg * P.NS;
   uint32_t polls = 0;
   bool ok_all = true;
   __syncthreads();                    // every thread is done reading the P.V scratch and m->ml
-  float* mls = accw;                  // [G][n_act][2], reuses the P.V scratch
-  float* scl = accw + 2 * G * n_act;  // [G][n_act] weights e^{m_s - M}
+  double* mls = accw;                 // [G][n_act][2], reuses the P.V scratch
+  double* scl = accw + 2 * G * n_act; // [G][n_act] weights e^{m_s - M}
   for (int i = tid; i < G * n_act; i += NT) {
     const int h = i / n_act, s2 = i - h * n_act;
-    const size_t pi = (b0 + s2) * G + h;
-    uint64_t wm = ld_tv(P.part_ml + pi * 2), wl = ld_tv(P.part_ml + pi * 2 + 1);
-    while (ok_all && !(tv_ok(wm, tag) && tv_ok(wl, tag))) {
+    const TV* pm = P.part_ml + (((b0 + s2) * G + h) * 2) * 2;  // m: pm[0..1], l: pm[2..3]
+    uint64_t w0 = ld_tv(pm), w1 = ld_tv(pm + 1), w2 = ld_tv(pm + 2), w3 = ld_tv(pm + 3);
+    while (ok_all && !(tv_ok(w0, tag) && tv_ok(w1, tag) && tv_ok(w2, tag) && tv_ok(w3, tag))) {
       if (++polls > P.watchdog) ok_all = false;
       __builtin_amdgcn_s_sleep(1);
-      wm = ld_tv(P.part_ml + pi * 2);
-      wl = ld_tv(P.part_ml + pi * 2 + 1);
+      w0 = ld_tv(pm);
+      w1 = ld_tv(pm + 1);
+      w2 = ld_tv(pm + 2);
+      w3 = ld_tv(pm + 3);
     }
-    mls[(h * n_act + s2) * 2] = tv_val(wm);
-    mls[(h * n_act + s2) * 2 + 1] = tv_val(wl);
+    mls[(h * n_act + s2) * 2] = tvd_val(w0, w1);
+    mls[(h * n_act + s2) * 2 + 1] = tvd_val(w2, w3);
   }
   __syncthreads();
   if (tid < G) {
     const int h = tid;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < n_act; ++s2) M = fmaxf(M, mls[(h * n_act + s2) * 2]);
-    float den = 0.f;
+    double M = -INFINITY;
+    for (int s2 = 0; s2 < n_act; ++s2) M = fmax(M, mls[(h * n_act + s2) * 2]);
+    double den = 0.0;
     for (int s2 = 0; s2 < n_act; ++s2) {
-      const float e = expf(mls[(h * n_act + s2) * 2] - M);
+      const double e = exp(mls[(h * n_act + s2) * 2] - M);
       scl[h * n_act + s2] = e;
       den += e * mls[(h * n_act + s2) * 2 + 1];
     }
@@ -860,25 +919,31 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   __syncthreads();
   for (int i = tid; i < G * D && ok_all; i += NT) {
     const int h = i / D, d = i - h * D;
-    float num = 0.f;
-    for (int c0 = 0; c0 < n_act && ok_all; c0 += 16) {
-      uint64_t wa[16];
+    double num = 0.0;
+    for (int c0 = 0; c0 < n_act && ok_all; c0 += 8) {
+      uint64_t wl[8], wh[8];
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (c0 + k < n_act) wa[k] = ld_tv(P.part_acc + ((b0 + c0 + k) * G + h) * D + d);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < 8; ++k)
         if (c0 + k < n_act) {
-          while (ok_all && !tv_ok(wa[k], tag)) {
+          const TV* pa = P.part_acc + ((((b0 + c0 + k) * G + h) * D + d) * 2);
+          wl[k] = ld_tv(pa);
+          wh[k] = ld_tv(pa + 1);
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (c0 + k < n_act) {
+          const TV* pa = P.part_acc + ((((b0 + c0 + k) * G + h) * D + d) * 2);
+          while (ok_all && !(tv_ok(wl[k], tag) && tv_ok(wh[k], tag))) {
             if (++polls > P.watchdog) ok_all = false;
             __builtin_amdgcn_s_sleep(1);
-            wa[k] = ld_tv(P.part_acc + ((b0 + c0 + k) * G + h) * D + d);
+            wl[k] = ld_tv(pa);
+            wh[k] = ld_tv(pa + 1);
           }
-          num += scl[h * n_act + c0 + k] * tv_val(wa[k]);
+          num += scl[h * n_act + c0 + k] * tvd_val(wl[k], wh[k]);
         }
       }
     }
-    if (ok_all) stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, num / m->ml[h][1]);
+    if (ok_all) stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, (float)(num / m->ml[h][1]));
   }
   if (!ok_all) {
     uint32_t zero = 0u;
@@ -930,7 +995,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   }
   if (blockIdx.x == 0) {
     // last step's token: wait for every LM tile of the final step
-    Misc* m = (Misc*)(lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+    Misc* m = (Misc*)(lds + P.misc_off);
     const uint32_t ev_lm = (uint32_t)(P.L * (P.Hkv + 4));
     if (!wait_event(P, ev_lm, P.epoch + (uint32_t)P.n_steps, 0xffffffffu, m)) return;
     reduce_tokens<NB>(P, m);
@@ -951,7 +1016,7 @@ __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
 
 template <int NB>
 __global__ __launch_bounds__(NT, 1) void mk_finish_tokens(KParams P) {
-  Misc* m = (Misc*)(g_lds + (size_t)P.xs_floats * 4 + RED_FLOATS * 4);
+  Misc* m = (Misc*)(g_lds + P.misc_off);
   reduce_tokens<NB>(P, m);
   if (threadIdx.x < NB) {
     if (P.out_tokens) stg(P.out_tokens + (size_t)P.step * P.B + threadIdx.x, m->tok[threadIdx.x]);
@@ -1015,7 +1080,7 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* 
 // ---------------------------------------------------------------------------
 // host-side launch helpers
 // ---------------------------------------------------------------------------
-size_t lds_bytes(const KParams& P) { return (size_t)P.xs_floats * 4 + RED_FLOATS * 4 + MISC_BYTES; }
+size_t lds_bytes(const KParams& P) { return (size_t)P.misc_off + MISC_BYTES; }
 
 template <int NB>
 static hipError_t launch_nb(int kind, const KParams& P, hipStream_t st) {

@@ -59,11 +59,12 @@ struct LmPart {
   int32_t idx;
 };
 
-// A value with the sequence tag of the step that wrote it, stored and loaded
-// as one 64-bit word: a reader that sees the expected tag also sees the
-// value written with it.  Tag of event ev at global step n: n * ntag + ev + 1.
+// 32 bits of a value with the sequence tag of the step that wrote it, stored
+// and loaded as one 64-bit word: a reader that sees the expected tag also sees
+// the bits written with it.  An fp64 value is two of these (low word, high
+// word).  Tag of event ev at global step n: n * ntag + ev + 1.
 struct TV {
-  float v;
+  uint32_t bits;
   uint32_t tag;
 };
 
@@ -74,17 +75,20 @@ constexpr uint32_t ERR_WATCHDOG = 1;
 struct KParams {
   // model shape
   int32_t L, H, Hq, Hkv, D, F, V, G, RG, QKVR, QD, B, max_seq, S, NS, qk_norm;
-  float eps, attn_scale;
+  float eps;          // RMSNorm epsilon (an fp32 value, widened to fp64 where used)
+  double attn_scale;  // 1 / sqrt(D)
   // tiling
   int32_t n_workers, n_qkv, n_wo, n_gu, n_down, n_lm;
-  int32_t xs_floats;  // activation staging capacity in LDS (floats)
+  // LDS layout of a worker: [activation staging: xs_doubles fp64][row sums: red_doubles fp64][misc]
+  int32_t xs_doubles, red_doubles;
+  int32_t red_off, misc_off;  // byte offsets
   // weights
   const LayerW* layers;
   const uint16_t* embed;
   const uint16_t* final_norm;
   const uint16_t* lm_head;
-  const float* rope_cos;  // [max_seq][D/2]
-  const float* rope_sin;
+  const double* rope_cos;  // [max_seq][D/2]
+  const double* rope_sin;
   // KV cache [L][B][Hkv][max_seq][D] bf16
   uint16_t* kc;
   uint16_t* vc;
@@ -93,8 +97,8 @@ struct KParams {
   float* qkv;       // [B][QKVR]
   float* o;         // [B][QD]
   float* a;         // [B][F]
-  TV* part_ml;      // [B][Hkv][NS][G][2] split max and sum, tagged
-  TV* part_acc;     // [B][Hkv][NS][G][D] split unnormalised P.V, tagged
+  TV* part_ml;      // [B][Hkv][NS][G][2][2] split max and sum (fp64 as two tagged words)
+  TV* part_acc;     // [B][Hkv][NS][G][D][2] split unnormalised P.V (fp64 as two tagged words)
   LmPart* lm_part;    // [B][n_lm]
   // tokens
   int32_t* pending;           // [B]

@@ -34,14 +34,25 @@ def compare_free_running(orc: "po.Oracle", seq: int, first_token: int, gpu_token
                          gpu_logits: np.ndarray | None, n_check: int | None = None, label: str = ""):
     """Oracle decodes on its own from first_token; compare step by step.
 
-    Returns the number of steps compared.  Raises AssertionError with details on a violation.
+    Returns the number of steps compared.  Raises AssertionError with details on a violation.  Prints the
+    largest per-step max and mean |logit error| seen (shown with pytest -s).
     """
     n = len(gpu_tokens) if n_check is None else min(n_check, len(gpu_tokens))
     tok = int(first_token)
+    worst = [0.0, 0.0]
+    try:
+        return _compare(orc, seq, tok, gpu_tokens, gpu_logits, n, label, worst)
+    finally:
+        if gpu_logits is not None:
+            print(f"[parity] {label}: worst step max|d| {worst[0]:.3e}, mean|d| {worst[1]:.3e}", flush=True)
+
+
+def _compare(orc, seq, tok, gpu_tokens, gpu_logits, n, label, worst):
     for i in range(n):
         lo = orc.step(seq, tok)
         if gpu_logits is not None:
             d = np.abs(gpu_logits[i].astype(np.float64) - lo.astype(np.float64))
+            worst[0], worst[1] = max(worst[0], float(d.max())), max(worst[1], float(d.mean()))
             assert np.all(np.isfinite(gpu_logits[i])), f"{label} step {i}: non-finite GPU logits"
             assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, \
                 f"{label} step {i}: max|d|={d.max():.3e} mean|d|={d.mean():.3e}"
