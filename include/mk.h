@@ -165,8 +165,9 @@ int mk_last_decode_ms(mk_ctx* ctx, float* ms);
 /* Tracing (diagnostics).  mk_set_trace(ctx, step) makes the next megakernel
  * mk_decode record, for decode step `step` of that call (0-based; -1
  * disables), four device wall-clock stamps per task of every worker: task
- * start, event satisfied, inputs staged (GEMV tasks), task end; 0 where a
- * point was not reached (e.g. attention splits beyond the current length).
+ * start, event satisfied, inputs staged (GEMV tasks) or split partial stored
+ * (attention tasks), task end; 0 where a point was not reached (e.g.
+ * attention splits beyond the current length).
  * mk_get_trace copies them as uint64 [n_workers][max_list][4] into out
  * (host, *len words; with out == NULL only the sizes are returned) and
  * reports the clock rate in kHz. */

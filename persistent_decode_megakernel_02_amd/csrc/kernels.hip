@@ -29,7 +29,7 @@ constexpr int NW = NT / 64;
 constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
 constexpr int DEPTH = 4;   // pipeline groups in flight per wave (16 KB per wave)
 constexpr int MISC_BYTES = 4096;
-constexpr int ATT_MAXL = 5;  // K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8))
+constexpr int ATT_MAXL = 5;  // most K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8))
 
 // Pointers kept inside the parameter block are generic; casting them to the
 // global address space lets the compiler emit global (not flat) memory
@@ -696,7 +696,8 @@ __device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
 }
 __device__ __forceinline__ double tvd_val(uint64_t lo, uint64_t hi) { return __hiloint2double((int)(uint32_t)hi, (int)(uint32_t)lo); }
 
-template <int G, int LPP>
+// NL: K/V 16-byte loads per thread (the split covers at most NL * PPB positions)
+template <int G, int LPP, int NL>
 __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                           uint64_t* tr) {
   constexpr int D = LPP * 8, PPB = NT / LPP;
@@ -716,15 +717,32 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   const uint32_t tag = (P.epoch + (uint32_t)s) * P.ntag + t.sig_ev + 1u;
 
   // cached K/V do not depend on this step: load them before waiting
-  uint4 kr[ATT_MAXL], vr[ATT_MAXL];
+  uint4 kr[NL], vr[NL];
 #pragma unroll
-  for (int i = 0; i < ATT_MAXL; ++i) {
+  for (int i = 0; i < NL; ++i) {
     const int j = j0 + po + i * PPB;
     if (po + i * PPB < S && j < jc) {
       kr[i] = ld16(Kh + (size_t)j * D + lp * 8);
       vr[i] = ld16(Vh + (size_t)j * D + lp * 8);
     } else {
       kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // so do this thread's RoPE factors (and QK-norm gains): item tid is (head tid / (D/2), pair tid % (D/2))
+  constexpr int half = D / 2;
+  const int nh = G + (has_cur ? 1 : 0);  // heads to rotate (q heads, then k)
+  const bool rot = tid < nh * half;
+  const int rh = tid / half, rk = tid - rh * half;
+  double rc = 0.0, rsn = 0.0, g0 = 1.0, g1 = 1.0;
+  if (rot) {
+    rc = ldg(P.rope_cos + (size_t)pos * half + rk);
+    rsn = ldg(P.rope_sin + (size_t)pos * half + rk);
+    if (P.qk_norm) {
+      const LayerW LW = ldg(P.layers + l);
+      const uint16_t* gm = rh < G ? LW.q_norm : LW.k_norm;
+      g0 = (double)bf1(ldg(gm + rk));
+      g1 = (double)bf1(ldg(gm + rk + half));
     }
   }
 
@@ -741,7 +759,6 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   const float* src = P.qkv + (size_t)b * P.QKVR + (size_t)g * P.RG;
   for (int i = tid * 4; i < (G + 2) * D; i += NT * 4) *(v4f*)(raw + i) = ldc4(src, (uint32_t)i);
   __syncthreads();
-  const int nh = G + (has_cur ? 1 : 0);  // heads to rotate (q heads, then k)
   if (P.qk_norm) {
     for (int h = w; h < nh; h += NW) {
       double ss = 0.0;
@@ -751,20 +768,14 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
     __syncthreads();
   }
-  constexpr int half = D / 2;
-  const double* cs = P.rope_cos + (size_t)pos * half;
-  const double* sn = P.rope_sin + (size_t)pos * half;
-  const LayerW LW = ldg(P.layers + l);
-  for (int i = tid; i < nh * half; i += NT) {
-    const int h = i / half, k = i - h * half;
+  if (rot) {
+    const int h = rh, k = rk;
     double x0 = raw[h * D + k], x1 = raw[h * D + k + half];
     if (P.qk_norm) {
-      const uint16_t* gm = h < G ? LW.q_norm : LW.k_norm;
-      x0 = (x0 * m->hr[h]) * (double)bf1(ldg(gm + k));
-      x1 = (x1 * m->hr[h]) * (double)bf1(ldg(gm + k + half));
+      x0 = (x0 * m->hr[h]) * g0;
+      x1 = (x1 * m->hr[h]) * g1;
     }
-    const double c = ldg(cs + k), sv = ldg(sn + k);
-    const double y0 = x0 * c - x1 * sv, y1 = x0 * sv + x1 * c;
+    const double y0 = x0 * rc - x1 * rsn, y1 = x0 * rsn + x1 * rc;
     if (h < G) {
       qrot[h * D + k] = y0;
       qrot[h * D + k + half] = y1;
@@ -788,7 +799,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[h][e] = qrot[h * D + lp * 8 + e];
 #pragma unroll
-  for (int i = 0; i < ATT_MAXL; ++i) {
+  for (int i = 0; i < NL; ++i) {
     if (i * PPB < S) {
       const int jr = po + i * PPB, j = j0 + jr;
       const uint4 kk = (has_cur && j == pos) ? *(const uint4*)(kcur + lp * 8) : kr[i];
@@ -833,7 +844,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0;
 #pragma unroll
-  for (int i = 0; i < ATT_MAXL; ++i) {
+  for (int i = 0; i < NL; ++i) {
     const int jr = po + i * PPB, j = j0 + jr;
     if (i * PPB < S && jr < S && j < j1) {
       const uint4 vv = (has_cur && j == pos) ? *(const uint4*)(vcur + lp * 8) : vr[i];
@@ -875,6 +886,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     st_tvd(P.part_ml + ((pbase + tid) * 2) * 2, m->ml[tid][0], tag);
     st_tvd(P.part_ml + ((pbase + tid) * 2 + 1) * 2, m->ml[tid][1], tag);
   }
+  if (tr && tid == 0) tr[2] = wall_clock64();  // partial stored
   if (!has_cur) {
     __syncthreads();
     return true;
@@ -959,21 +971,29 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   return ldc_u(P.status + ST_ABORT) == 0u;
 }
 
+template <int G, int LPP>
+__device__ __forceinline__ bool attn_nl(const KParams& P, const TaskRec& t, int s, bool mega, char* lds, uint64_t* tr) {
+  constexpr int PPB = NT / LPP;
+  if (P.S <= PPB) return task_attn<G, LPP, 1>(P, t, s, mega, lds, tr);
+  if (P.S <= 2 * PPB) return task_attn<G, LPP, 2>(P, t, s, mega, lds, tr);
+  return task_attn<G, LPP, ATT_MAXL>(P, t, s, mega, lds, tr);
+}
+
 template <int NB>
 __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                          uint64_t* tr = nullptr) {
   if (t.op == OP_ATTN) {
     if (P.D == 64) {
       switch (P.G) {
-        case 1: return task_attn<1, 8>(P, t, s, mega, lds, tr);
-        case 2: return task_attn<2, 8>(P, t, s, mega, lds, tr);
-        default: return task_attn<4, 8>(P, t, s, mega, lds, tr);
+        case 1: return attn_nl<1, 8>(P, t, s, mega, lds, tr);
+        case 2: return attn_nl<2, 8>(P, t, s, mega, lds, tr);
+        default: return attn_nl<4, 8>(P, t, s, mega, lds, tr);
       }
     }
     switch (P.G) {
-      case 1: return task_attn<1, 16>(P, t, s, mega, lds, tr);
-      case 2: return task_attn<2, 16>(P, t, s, mega, lds, tr);
-      default: return task_attn<4, 16>(P, t, s, mega, lds, tr);
+      case 1: return attn_nl<1, 16>(P, t, s, mega, lds, tr);
+      case 2: return attn_nl<2, 16>(P, t, s, mega, lds, tr);
+      default: return attn_nl<4, 16>(P, t, s, mega, lds, tr);
     }
   }
   return task_gemv<NB>(P, t, s, mega, lds, tr);
