@@ -1,31 +1,66 @@
-"""Build libmk.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc."""
+"""Build libmk.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+The kernels are compiled as six translation units of kernels.hip (one per batch size, plus probes and
+dispatch) in parallel, with api.cpp and graph.cpp, then linked into one shared library.
+"""
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
 SOURCES = ["kernels.hip", "api.cpp", "graph.cpp"]
 HEADERS = ["mk_internal.h", "graph.h"]
+BATCHES = [1, 2, 4, 8, 16]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
-FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17",
+FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = ["hipcc", *FLAGS, *extra, "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _units(tmp):
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    k = os.path.join(CSRC, "kernels.hip")
+    units = [(["-c", k], os.path.join(tmp, "kernels_common.o"))]
+    units += [([f"-DMK_NB={nb}", "-c", k], os.path.join(tmp, f"kernels_b{nb}.o")) for nb in BATCHES]
+    units += [(["-c", os.path.join(CSRC, f)], os.path.join(tmp, f + ".o")) for f in ("api.cpp", "graph.cpp")]
+    return [(["hipcc", *FLAGS, *inc, *args, "-o", out], out) for args, out in units]
+
+
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(line for line in r.stderr.splitlines() if "packed-fp32-ops" not in line)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
-    os.replace(LIB + ".tmp", LIB)
+    return r.returncode, " ".join(cmd), err
+
+
+def build(verbose: bool = False, extra=(), jobs: int = 0) -> str:
+    tmp = tempfile.mkdtemp(prefix="mkbuild_")
+    try:
+        units = _units(tmp)
+        units = [(cmd[:1] + list(extra) + cmd[1:], out) for cmd, out in units]
+        jobs = jobs or min(len(units), max(1, min(os.cpu_count() or 1, 16)))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(_run, [c for c, _ in units]))
+        for rc, cmd, err in results:
+            if verbose:
+                print(cmd, flush=True)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}): {cmd}\n{err}")
+            if verbose and err.strip():
+                print(err)
+        link = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o in units], "-o", LIB + ".tmp"]
+        rc, cmd, err = _run(link)
+        if verbose:
+            print(cmd, flush=True)
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}): {cmd}\n{err}")
+        os.replace(LIB + ".tmp", LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
     return LIB
 
 

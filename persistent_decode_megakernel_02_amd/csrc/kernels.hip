@@ -1045,6 +1045,55 @@ __global__ __launch_bounds__(NT, 1) void mk_finish_tokens(KParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// host-side launch helpers.  The kernels are instantiated for one batch size
+// per translation unit (MK_NB = 1, 2, 4, 8, 16), so that the units compile in
+// parallel; the unit built without MK_NB holds the probes and the dispatch.
+// ---------------------------------------------------------------------------
+static inline size_t worker_lds_bytes(const KParams& P) { return (size_t)P.misc_off + MISC_BYTES; }
+
+#define MK_CAT2(a, b) a##b
+#define MK_CAT(a, b) MK_CAT2(a, b)
+
+#ifdef MK_NB
+template <int NB>
+static hipError_t launch_nb(int kind, const KParams& P, hipStream_t st) {
+  const size_t sh = worker_lds_bytes(P);
+  KParams Q = P;
+  if (kind == 0) {
+    void* args[] = {&Q};
+    return hipLaunchCooperativeKernel((const void*)mk_persistent<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
+  } else if (kind == 1) {
+    hipLaunchKernelGGL(mk_per_op<NB>, dim3(P.n_workers), dim3(NT), sh, st, Q);
+  } else if (kind == 3) {
+    // cooperative: an attention merger polls partials written by other workgroups of the same launch
+    void* args[] = {&Q};
+    return hipLaunchCooperativeKernel((const void*)mk_per_op<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
+  } else {
+    hipLaunchKernelGGL(mk_finish_tokens<NB>, dim3(1), dim3(NT), sh, st, Q);
+  }
+  return hipGetLastError();
+}
+
+template <int NB>
+static hipError_t set_attrs() {
+  const int sh = 163840;
+  hipError_t e = hipFuncSetAttribute((const void*)mk_persistent<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)mk_per_op<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)mk_finish_tokens<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+}
+
+hipError_t MK_CAT(launch_b, MK_NB)(int kind, const KParams& P, hipStream_t st) { return launch_nb<MK_NB>(kind, P, st); }
+hipError_t MK_CAT(set_attrs_b, MK_NB)() { return set_attrs<MK_NB>(); }
+int MK_CAT(coresident_b, MK_NB)(size_t lds) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)mk_persistent<MK_NB>, NT, lds) != hipSuccess)
+    return -1;
+  return per_cu;
+}
+#else
+// ---------------------------------------------------------------------------
 // Plain streaming read of a buffer: the achievable HBM read rate with the same
 // loads the GEMV tasks use (16-byte non-temporal, one contiguous block per
 // workgroup), and a kernel of known traffic for calibrating byte counters.
@@ -1097,73 +1146,48 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* 
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// host-side launch helpers
-// ---------------------------------------------------------------------------
-size_t lds_bytes(const KParams& P) { return (size_t)P.misc_off + MISC_BYTES; }
+size_t lds_bytes(const KParams& P) { return worker_lds_bytes(P); }
 
-template <int NB>
-static hipError_t launch_nb(int kind, const KParams& P, hipStream_t st) {
-  const size_t sh = lds_bytes(P);
-  KParams Q = P;
-  if (kind == 0) {
-    void* args[] = {&Q};
-    return hipLaunchCooperativeKernel((const void*)mk_persistent<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
-  } else if (kind == 1) {
-    hipLaunchKernelGGL(mk_per_op<NB>, dim3(P.n_workers), dim3(NT), sh, st, Q);
-  } else if (kind == 3) {
-    // cooperative: an attention merger polls partials written by other workgroups of the same launch
-    void* args[] = {&Q};
-    return hipLaunchCooperativeKernel((const void*)mk_per_op<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
-  } else {
-    hipLaunchKernelGGL(mk_finish_tokens<NB>, dim3(1), dim3(NT), sh, st, Q);
-  }
-  return hipGetLastError();
-}
-
-template <int NB>
-static hipError_t set_attrs() {
-  const int sh = 163840;
-  hipError_t e = hipFuncSetAttribute((const void*)mk_persistent<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)mk_per_op<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)mk_finish_tokens<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
-}
+#define MK_DECL(nb)                                                         \
+  hipError_t launch_b##nb(int kind, const KParams& P, hipStream_t st); \
+  hipError_t set_attrs_b##nb();                                        \
+  int coresident_b##nb(size_t lds);
+MK_DECL(1)
+MK_DECL(2)
+MK_DECL(4)
+MK_DECL(8)
+MK_DECL(16)
 
 hipError_t prepare_kernels(int B) {
   switch (B) {
-    case 1: return set_attrs<1>();
-    case 2: return set_attrs<2>();
-    case 4: return set_attrs<4>();
-    case 8: return set_attrs<8>();
-    default: return set_attrs<16>();
+    case 1: return set_attrs_b1();
+    case 2: return set_attrs_b2();
+    case 4: return set_attrs_b4();
+    case 8: return set_attrs_b8();
+    default: return set_attrs_b16();
   }
 }
 
 // kind: 0 persistent (cooperative), 1 one operator instance, 2 final token, 3 attention operator instance
 hipError_t launch(int kind, const KParams& P, hipStream_t st) {
   switch (P.B) {
-    case 1: return launch_nb<1>(kind, P, st);
-    case 2: return launch_nb<2>(kind, P, st);
-    case 4: return launch_nb<4>(kind, P, st);
-    case 8: return launch_nb<8>(kind, P, st);
-    default: return launch_nb<16>(kind, P, st);
+    case 1: return launch_b1(kind, P, st);
+    case 2: return launch_b2(kind, P, st);
+    case 4: return launch_b4(kind, P, st);
+    case 8: return launch_b8(kind, P, st);
+    default: return launch_b16(kind, P, st);
   }
 }
 
 int max_coresident_workers(int B, size_t lds) {
-  int per_cu = 0;
-  const void* f = (const void*)mk_persistent<1>;
   switch (B) {
-    case 2: f = (const void*)mk_persistent<2>; break;
-    case 4: f = (const void*)mk_persistent<4>; break;
-    case 8: f = (const void*)mk_persistent<8>; break;
-    case 16: f = (const void*)mk_persistent<16>; break;
-    default: break;
+    case 1: return coresident_b1(lds);
+    case 2: return coresident_b2(lds);
+    case 4: return coresident_b4(lds);
+    case 8: return coresident_b8(lds);
+    default: return coresident_b16(lds);
   }
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, NT, lds) != hipSuccess) return -1;
-  return per_cu;
 }
+#endif
 
 }  // namespace mk
