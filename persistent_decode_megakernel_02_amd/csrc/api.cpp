@@ -26,6 +26,7 @@ size_t lds_bytes(const KParams& P);
 int max_coresident_workers(int B, size_t lds);
 constexpr int kLdsBytes = 163840;  // one worker per compute unit takes all of its LDS
 constexpr int kMiscBytes = 4096;   // per-worker scalars at the top of LDS (same size as in the kernels)
+constexpr int kMaxSlice = 1536;    // largest K slice of the matrix-core GEMV (same as in the kernels)
 constexpr uint32_t kDefaultWatchdog = 1u << 22;  // ~1-2 us per poll: several seconds, far above any healthy wait
 }  // namespace mk
 
@@ -35,6 +36,7 @@ using namespace mk;
 // space below misc for q/k/v, rotated queries, scores and per-wave P.V sums.
 struct LdsPlan {
   int xs_doubles, red_doubles, red_off, misc_off;
+  int mk_ks;  // batch >= 8: K slice of the matrix-core GEMV
 };
 
 struct mk_ctx {
@@ -129,13 +131,32 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
   const int worst = std::max({maxrows(cfg.hidden, g.n_wo), maxrows(cfg.ffn, g.n_gu) * 2, maxrows(cfg.hidden, g.n_down),
                               maxrows(cfg.vocab, g.n_lm), (G + 2) * D / g.qkv_tiles_per_group + 1});
   LdsPlan L;
-  L.red_doubles = (worst * B + 1) / 2 * 2;
-  L.misc_off = kLdsBytes - kMiscBytes;
-  L.red_off = L.misc_off - L.red_doubles * 8;
-  L.xs_doubles = L.red_off / 8;
-  if (L.xs_doubles / B < 512) {
-    *why = "a GEMV tile has too many rows for LDS at this batch (use more workers or a smaller batch)";
-    return MK_ERR_UNSUPPORTED;
+  L.mk_ks = 0;
+  if (B >= 8) {
+    // matrix-core GEMV: passes of up to 8 row tiles (128 rows), K staged in slices of three bf16 pieces
+    // (96 bytes per K element at 16 columns), each wave taking 1/8 of a slice in pairs of 32-element steps
+    if (cfg.hidden % 512 || cfg.ffn % 512 || (cfg.n_q_heads * D) % 512) {
+      *why = "batch >= 8 needs hidden, ffn and n_q_heads * head_dim to be multiples of 512";
+      return MK_ERR_UNSUPPORTED;
+    }
+    L.red_doubles = 128 * B;
+    L.misc_off = kLdsBytes - kMiscBytes;
+    L.red_off = L.misc_off - L.red_doubles * 8;
+    L.mk_ks = std::min(kMaxSlice, L.red_off / 96 / 512 * 512);
+    L.xs_doubles = L.red_off / 8;
+    if (L.mk_ks < 512 || 8 * 8 * 256 * 4 > L.red_off) {
+      *why = "LDS too small for the matrix-core GEMV";
+      return MK_ERR_UNSUPPORTED;
+    }
+  } else {
+    L.red_doubles = (worst * B + 1) / 2 * 2;
+    L.misc_off = kLdsBytes - kMiscBytes;
+    L.red_off = L.misc_off - L.red_doubles * 8;
+    L.xs_doubles = L.red_off / 8;
+    if (L.xs_doubles / B < 512) {
+      *why = "a GEMV tile has too many rows for LDS at this batch (use more workers or a smaller batch)";
+      return MK_ERR_UNSUPPORTED;
+    }
   }
   if (att_bytes > L.misc_off) {
     *why = "attention working set exceeds LDS";
@@ -423,6 +444,7 @@ static KParams make_params(mk_ctx* c) {
   P.red_doubles = c->lds.red_doubles;
   P.red_off = c->lds.red_off;
   P.misc_off = c->lds.misc_off;
+  P.mk_ks = c->lds.mk_ks;
   P.layers = c->d_layers;
   P.embed = c->embed;
   P.final_norm = c->final_norm;

@@ -670,6 +670,296 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 }
 
 // ---------------------------------------------------------------------------
+// GEMV task for B >= 8 sequences: a skinny GEMM on the matrix cores.
+//   Y[rows x 16] = W[rows x K] . X[K x 16]  with v_mfma_f32_16x16x32_bf16
+// (columns beyond B are zero).  Each fp32 activation is split exactly into
+// three bf16 pieces, x = x0 + x1 + x2, so every product W * x_p is exact; the
+// only rounding before the fp64 epilogue is the fp32 accumulation inside one
+// wave's share of K.  The eight waves split K and their partial sums are added
+// in fp64.  K is staged in LDS in slices of P.mk_ks elements (pieces laid out
+// [piece][8-element block][column][8 x bf16]), rows go in tiles of 16, and up
+// to MT tiles share one pass over K (more tiles take more passes).
+// Lane layout on gfx950: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]
+// and D[4(l/16)+r][l%16], e < 8, r < 4.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int MT = 8;        // row tiles per pass
+constexpr int MAX_KS = 1536; // largest K slice the host plans (a multiple of 512, as is K)
+constexpr int MSTEPS = MAX_KS / 8 / 32;  // 32-element steps per wave per slice, at most
+
+// x = bf16(p0) + bf16(p1) + bf16(p2) exactly (truncations of x and of the exact remainders)
+__device__ __forceinline__ void split3(float x, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+  const uint32_t u = __float_as_uint(x);
+  const float r1 = x - __uint_as_float(u & 0xffff0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+  p0 = u >> 16;
+  p1 = u1 >> 16;
+  p2 = __float_as_uint(r2) >> 16;
+}
+
+template <int NB>
+__device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
+                                               uint64_t* tr) {
+  const int op = (int)t.op, l = (int)t.layer;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  const int li = lane & 15, lq = lane >> 4;  // MFMA row / column index and K quarter of this lane
+  double* red = (double*)(lds + P.red_off);
+  Misc* m = (Misc*)(lds + P.misc_off);
+  const LayerW LW = ldg(P.layers + (op == OP_LM ? 0 : l));
+
+  const uint16_t* W0;
+  const uint16_t* W1 = nullptr;
+  const uint16_t* gamma = nullptr;
+  int K, RU = 1;
+  switch (op) {
+    case OP_QKV: W0 = LW.wqkv; K = P.H; gamma = LW.attn_norm; break;
+    case OP_WO: W0 = LW.wo; K = P.QD; break;
+    case OP_GU: W0 = LW.wg; W1 = LW.wu; K = P.H; RU = 2; gamma = LW.ffn_norm; break;
+    case OP_DOWN: W0 = LW.wd; K = P.F; break;
+    default: W0 = P.lm_head; K = P.H; gamma = P.final_norm; break;
+  }
+  const bool norm = gamma != nullptr;
+  const bool embed_src = (op == OP_QKV && l == 0);
+  const int u0 = (int)t.a0, nu = (int)t.a1 - (int)t.a0;
+  const int R = nu * RU, T = (R + 15) >> 4;
+  const int ks = P.mk_ks, CB = ks >> 3;
+  const int nsl = (K + ks - 1) / ks;
+  const int npass = (T + MT - 1) / MT;
+
+  auto rowptr = [&](int r) -> const uint16_t* {
+    r = min(r, R - 1);
+    const int ui = RU == 2 ? (r >> 1) : r;
+    const uint16_t* base = (RU == 2 && (r & 1)) ? W1 : W0;
+    return base + (size_t)(u0 + ui) * K;
+  };
+  // the step sequence of this wave: (pass, slice, 32-element step of the wave's share of the slice)
+  int cp = 0, csl = 0, cst = 0;
+  auto nsteps = [&](int sl) { return (min(ks, K - sl * ks) >> 3) >> 5; };
+  auto step_k = [&](int sl, int st) { return sl * ks + w * (min(ks, K - sl * ks) >> 3) + 32 * st; };
+  uint4 A[2][MT];
+  auto issue = [&](uint4 (&a)[MT], int pass, int sl, int st) {
+    const int kk = step_k(sl, st) + 8 * lq;
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt) {
+      const int tile = pass * MT + tt;
+      a[tt] = ldw(rowptr(min(tile, T - 1) * 16 + li) + kk);
+    }
+  };
+
+  // weights do not depend on the event: the first step's loads go out before the wait
+  issue(A[0], 0, 0, 0);
+
+  if (mega && !(s == 0 && t.wait_lag) &&
+      !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m, tr))
+    return false;
+
+  if (embed_src) {
+    if (P.force_tok) {
+      if (tid < NB) m->tok[tid] = ldg(P.force_tok + (size_t)s * P.B + tid);
+      __syncthreads();
+    } else if (s == 0) {
+      if (tid < NB) {
+        const int32_t tk = ldg(P.pending + tid);
+        m->tok[tid] = (tk >= 0 && tk < P.V) ? tk : 0;
+      }
+      __syncthreads();
+    } else {
+      reduce_tokens<NB>(P, m);
+      if (t.tile == 0 && P.out_tokens && tid < NB) stg(P.out_tokens + (size_t)(s - 1) * P.B + tid, m->tok[tid]);
+    }
+    const int h0 = (int)((int64_t)t.tile * P.H / P.n_qkv), h1 = (int)((int64_t)(t.tile + 1) * P.H / P.n_qkv);
+    for (int i = h0 + tid; i < h1; i += NT)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) stc(P.x + (size_t)b * P.H + i, bf1(ldg(P.embed + (size_t)m->tok[b] * P.H + i)));
+  }
+
+  const int jcol = tid & 15;  // every staging item of this thread belongs to column jcol
+  double ss = 0.0;            // sum of squares of column jcol (first pass)
+  float bv[NB];
+  int32_t bi[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    bv[b] = -INFINITY;
+    bi[b] = 0x7fffffff;
+  }
+  const float* src = op == OP_WO ? P.o : op == OP_DOWN ? P.a : P.x;
+  const int sstride = op == OP_WO ? P.QD : op == OP_DOWN ? P.F : P.H;
+
+  for (int pass = 0; pass < npass; ++pass) {
+    const int tp0 = pass * MT, ntp = min(MT, T - tp0);
+    v4f acc[MT];
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < nsl; ++sl) {
+      const int k0 = sl * ks, ksc = min(ks, K - k0);
+      // ---- stage this slice: x (* gamma) split into three bf16 pieces per column
+      __syncthreads();  // the previous slice (or pass) is no longer read
+      {
+        const int items = (ksc >> 3) * 16;
+        for (int it = tid; it < items; it += NT) {
+          const int c = it >> 4, kb = k0 + 8 * c;
+          float xv[8];
+          if (jcol < NB) {
+            if (embed_src) {
+              const uint4 q = ld16(P.embed + (size_t)m->tok[jcol] * P.H + kb);
+              const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                xv[2 * e] = bf_lo(qw[e]);
+                xv[2 * e + 1] = bf_hi(qw[e]);
+              }
+            } else {
+              const v4f a0 = ldc4(src + (size_t)jcol * sstride, (uint32_t)kb);
+              const v4f a1 = ldc4(src + (size_t)jcol * sstride, (uint32_t)kb + 4u);
+              xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+              xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+            }
+            if (norm) {
+              const uint4 gq = ld16(gamma + kb);
+              const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const double xd = xv[e];
+                if (pass == 0) ss += xd * xd;
+                xv[e] = (float)(xd * (double)((e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1])));
+              }
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[e] = 0.f;
+          }
+          uint32_t p0[8], p1[8], p2[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split3(xv[e], p0[e], p1[e], p2[e]);
+          char* xb = lds + (size_t)(c * 16 + jcol) * 16;
+          *(uint4*)(xb) = make_uint4(p0[0] | (p0[1] << 16), p0[2] | (p0[3] << 16), p0[4] | (p0[5] << 16), p0[6] | (p0[7] << 16));
+          *(uint4*)(xb + (size_t)CB * 256) = make_uint4(p1[0] | (p1[1] << 16), p1[2] | (p1[3] << 16), p1[4] | (p1[5] << 16), p1[6] | (p1[7] << 16));
+          *(uint4*)(xb + (size_t)CB * 512) = make_uint4(p2[0] | (p2[1] << 16), p2[2] | (p2[3] << 16), p2[4] | (p2[5] << 16), p2[6] | (p2[7] << 16));
+        }
+      }
+      __syncthreads();
+      if (tr && pass == 0 && sl == 0 && tid == 0) tr[2] = wall_clock64();
+      // ---- this wave's share of the slice, 32 elements per step, steps in pairs (a slice
+      // has an even number of them) so that the two weight buffers are indexed statically;
+      // each step requests the next step's weights before its own MFMAs
+      const int nst = nsteps(sl);
+      auto step = [&](uint4 (&cur)[MT], uint4 (&nxt)[MT], int st) {
+        int np = pass, nsl2 = sl, nst2 = st + 1;  // next step in (pass, slice, step) order
+        if (nst2 == nst) {
+          nst2 = 0;
+          if (++nsl2 == nsl) {
+            nsl2 = 0;
+            ++np;
+          }
+        }
+        if (np < npass) issue(nxt, np, nsl2, nst2);
+        const int cbase = ((step_k(sl, st) - k0) >> 3) + lq;
+        const char* xb = lds + (size_t)(cbase * 16 + li) * 16;
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *(const uint4*)(xb));
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *(const uint4*)(xb + (size_t)CB * 256));
+        const bf16x8 b2 = __builtin_bit_cast(bf16x8, *(const uint4*)(xb + (size_t)CB * 512));
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt) {
+          if (tt < ntp) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, cur[tt]);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, acc[tt], 0, 0, 0);
+          }
+        }
+      };
+      for (int st = 0; st < nst; st += 2) {
+        step(A[0], A[1], st);
+        step(A[1], A[0], st + 1);
+      }
+    }
+    // ---- add the eight waves' partial tiles in fp64 (the staging area is free now)
+    __syncthreads();
+    float* part = (float*)lds;  // [wave][tile][256]
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt)
+      if (tt < ntp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[((size_t)w * MT + tt) * 256 + (lq * 4 + r) * 16 + li] = acc[tt][r];
+    if (pass == 0 && norm) {  // per-wave sums of squares per column: lanes with equal (lane & 15) share a column
+      double v = ss;
+      v = xor16_pair_d(v);
+      v = xor32_pair_d(v);
+      if (lane < 16) m->wred[w][lane] = v;
+    }
+    __syncthreads();
+    const int rows = min(R - tp0 * 16, ntp * 16);
+    for (int i = tid; i < rows * NB; i += NT) {
+      const int rr = i / NB, b = i - rr * NB;
+      const int tt = rr >> 4, ri = rr & 15;
+      double v = 0.0;
+      for (int ww = 0; ww < NW; ++ww) v += (double)part[((size_t)ww * MT + tt) * 256 + ri * 16 + b];
+      red[rr * NB + b] = v;
+    }
+    __syncthreads();
+    // ---- epilogue for this pass's rows
+    double rs[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      double tot = 0.0;
+      for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][b];
+      rs[b] = norm ? 1.0 / sqrt(tot / (double)K + (double)P.eps) : 1.0;
+    }
+    const int pu0 = u0 + tp0 * 16 / RU, pnu = rows / RU;
+    if (op == OP_QKV) {
+      for (int i = tid; i < pnu * NB; i += NT) {
+        const int ul = i / NB, b = i - ul * NB;
+        stc(P.qkv + (size_t)b * P.QKVR + pu0 + ul, (float)(red[ul * NB + b] * rs[b]));
+      }
+    } else if (op == OP_WO || op == OP_DOWN) {
+      for (int i = tid; i < pnu * NB; i += NT) {
+        const int ul = i / NB, b = i - ul * NB;
+        float* xp = P.x + (size_t)b * P.H + pu0 + ul;
+        stc(xp, (float)((double)ldc(xp) + red[ul * NB + b]));
+      }
+    } else if (op == OP_GU) {
+      for (int i = tid; i < pnu * NB; i += NT) {
+        const int ul = i / NB, b = i - ul * NB;
+        const double gt = red[(ul * 2) * NB + b] * rs[b];
+        const double up = red[(ul * 2 + 1) * NB + b] * rs[b];
+        stc(P.a + (size_t)b * P.F + pu0 + ul, (float)(silu_d(gt) * up));
+      }
+    } else {  // OP_LM
+      for (int ul = tid; ul < pnu; ul += NT) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float logit = (float)(red[ul * NB + b] * rs[b]);
+          if (P.out_logits) stg(P.out_logits + ((size_t)s * P.B + b) * P.V + pu0 + ul, logit);
+          amax_merge(bv[b], bi[b], logit, pu0 + ul);
+        }
+      }
+    }
+  }
+  if (op == OP_LM) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      wave_amax(bv[b], bi[b]);
+      if (lane == 0) {
+        m->wval[w][b] = bv[b];
+        m->widx[w][b] = bi[b];
+      }
+    }
+    __syncthreads();
+    if (tid < NB) {
+      float v = m->wval[0][tid];
+      int32_t ix = m->widx[0][tid];
+      for (int ww = 1; ww < NW; ++ww) amax_merge(v, ix, m->wval[ww][tid], m->widx[ww][tid]);
+      LmPart* lp = P.lm_part + (size_t)tid * P.n_lm + t.tile;
+      stc(&lp->val, v);
+      stc_i(&lp->idx, ix);
+    }
+  }
+  signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 // Attention task (sequence b, KV head g, split sp): QK-norm + RoPE of the G
 // query heads (and of k when this split holds the current position, which it
 // then appends to the cache), scores over the split's positions, and the
@@ -996,7 +1286,8 @@ __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int
       default: return attn_nl<4, 16>(P, t, s, mega, lds, tr);
     }
   }
-  return task_gemv<NB>(P, t, s, mega, lds, tr);
+  if constexpr (NB >= 8) return task_gemv_mfma<NB>(P, t, s, mega, lds, tr);
+  else return task_gemv<NB>(P, t, s, mega, lds, tr);
 }
 
 // The megakernel: one launch runs n_steps decode steps of the whole model.

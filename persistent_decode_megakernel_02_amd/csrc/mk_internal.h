@@ -82,6 +82,7 @@ struct KParams {
   // LDS layout of a worker: [activation staging: xs_doubles fp64][row sums: red_doubles fp64][misc]
   int32_t xs_doubles, red_doubles;
   int32_t red_off, misc_off;  // byte offsets
+  int32_t mk_ks;              // B >= 8: K slice staged per pass of the matrix-core GEMV
   // weights
   const LayerW* layers;
   const uint16_t* embed;
