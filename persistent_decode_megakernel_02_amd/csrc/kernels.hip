@@ -142,6 +142,15 @@ __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
 }
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return ldg((const uint4*)p); }
 
+// The thread index seen through an empty asm.  Lane-dependent addresses are
+// then recomputed inside every task instead of being hoisted out of the
+// persistent loop, where they would stay live across all tasks (and spill).
+__device__ __forceinline__ int ltid() {
+  int v = threadIdx.x;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Cross-lane reductions in VALU (DPP row operations and the gfx950
 // permlane swaps), no LDS traffic.  Every lane of a group receives the same,
 // bit-identical result (each step adds the same two operands on all lanes).
@@ -250,8 +259,9 @@ __device__ __forceinline__ double silu_d(double z) { return z / (1.0 + exp(-z));
 __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32_t target, uint32_t task, Misc* m,
                                            uint64_t* tr = nullptr) {
   if (ev == EV_NONE) return true;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+  const int tid = ltid();
+  if (tid < 64) {
+    const int lane = tid;
     const EventRec e = ldg(P.events + ev);
     const uint32_t* f = P.flags + e.slot0;
     uint32_t polls = 0;
@@ -307,7 +317,7 @@ __device__ __forceinline__ void signal_event(const KParams& P, uint32_t ev, uint
 // ---------------------------------------------------------------------------
 template <int NB>
 __device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   float bv[NB];
   int32_t bi[NB];
 #pragma unroll
@@ -315,7 +325,7 @@ __device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
     bv[b] = -INFINITY;
     bi[b] = 0x7fffffff;
   }
-  for (int i = threadIdx.x; i < P.n_lm; i += NT) {
+  for (int i = tid; i < P.n_lm; i += NT) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const LmPart* lp = P.lm_part + (size_t)b * P.n_lm + i;
@@ -333,8 +343,8 @@ __device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
     }
   }
   __syncthreads();
-  if (threadIdx.x < NB) {
-    const int b = threadIdx.x;
+  if (tid < NB) {
+    const int b = tid;
     float v = m->wval[0][b];
     int32_t ix = m->widx[0][b];
     for (int ww = 1; ww < NW; ++ww) amax_merge(v, ix, m->wval[ww][b], m->widx[ww][b]);
@@ -353,7 +363,7 @@ template <int NB>
 __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                           uint64_t* tr) {
   const int op = (int)t.op, l = (int)t.layer;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   double* xs = (double*)lds;
   double* red = (double*)(lds + P.red_off);
   Misc* m = (Misc*)(lds + P.misc_off);
@@ -702,7 +712,7 @@ template <int NB>
 __device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                                uint64_t* tr) {
   const int op = (int)t.op, l = (int)t.layer;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;  // MFMA row / column index and K quarter of this lane
   double* red = (double*)(lds + P.red_off);
   Misc* m = (Misc*)(lds + P.misc_off);
@@ -996,7 +1006,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   const int pos = P.pos0 + s, N = pos + 1;
   const int n_act = (N + S - 1) / S;
   if (sp >= n_act) return true;  // split beyond the current length: nothing to do
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   const int j0 = sp * S, j1 = min(j0 + S, N);
   const bool has_cur = (j1 == N);  // this split holds the current position and merges
   const int jc = has_cur ? pos : j1;  // cached positions [j0, jc)
@@ -1082,25 +1092,24 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     stg((uint4*)(Vh + (size_t)pos * D + tid * 8), *(const uint4*)(vcur + tid * 8));
   }
 
-  // ---- scores t_j = (q_h . k_j) / sqrt(D); LPP lanes share one position
-  double q[G][8];
+  // ---- scores t_j = (q_h . k_j) / sqrt(D); LPP lanes share one position.  Heads go
+  // one at a time so that only one head's query slice and sums occupy registers.
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    double q[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[h][e] = qrot[h * D + lp * 8 + e];
+    for (int e = 0; e < 8; ++e) q[e] = qrot[h * D + lp * 8 + e];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    if (i * PPB < S) {
-      const int jr = po + i * PPB, j = j0 + jr;
-      const uint4 kk = (has_cur && j == pos) ? *(const uint4*)(kcur + lp * 8) : kr[i];
-      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
+    for (int i = 0; i < NL; ++i) {
+      if (i * PPB < S) {
+        const int jr = po + i * PPB, j = j0 + jr;
+        const uint4 kk = (has_cur && j == pos) ? *(const uint4*)(kcur + lp * 8) : kr[i];
+        const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
         double a = 0.0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a = fma(q[h][2 * e], (double)bf_lo(kw[e]), a);
-          a = fma(q[h][2 * e + 1], (double)bf_hi(kw[e]), a);
+          a = fma(q[2 * e], (double)bf_lo(kw[e]), a);
+          a = fma(q[2 * e + 1], (double)bf_hi(kw[e]), a);
         }
         a = group_sum_d<LPP>(a);
         if (jr < S && j < j1 && lp == 0) sc[h * S + jr] = a * P.attn_scale;
@@ -1127,43 +1136,35 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
   }
   __syncthreads();
-  // ---- unnormalised P.V
-  double acc[G][8];
+  // ---- unnormalised P.V, one head at a time; the sum over this wave's positions
+  // (lanes with the same lp) is written per wave
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    double acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int jr = po + i * PPB, j = j0 + jr;
-    if (i * PPB < S && jr < S && j < j1) {
-      const uint4 vv = (has_cur && j == pos) ? *(const uint4*)(vcur + lp * 8) : vr[i];
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
+    for (int i = 0; i < NL; ++i) {
+      const int jr = po + i * PPB, j = j0 + jr;
+      if (i * PPB < S && jr < S && j < j1) {
+        const uint4 vv = (has_cur && j == pos) ? *(const uint4*)(vcur + lp * 8) : vr[i];
+        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
         const double p = sc[h * S + jr];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[h][2 * e] = fma(p, (double)bf_lo(vw[e]), acc[h][2 * e]);
-          acc[h][2 * e + 1] = fma(p, (double)bf_hi(vw[e]), acc[h][2 * e + 1]);
+          acc[2 * e] = fma(p, (double)bf_lo(vw[e]), acc[2 * e]);
+          acc[2 * e + 1] = fma(p, (double)bf_hi(vw[e]), acc[2 * e + 1]);
         }
       }
     }
-  }
-  // sum over the positions of this wave: lanes with the same lp
-#pragma unroll
-  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      double v = acc[h][e];
+      double v = acc[e];
       if (LPP == 8) v += dpp_d<0x128>(v);  // row_ror:8 (lane i and i^8)
-      acc[h][e] = xor32_pair_d(xor16_pair_d(v));
+      v = xor32_pair_d(xor16_pair_d(v));
+      if (lane < LPP) accw[(w * G + h) * D + lp * 8 + e] = v;
     }
-  if (lane < LPP)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) accw[(w * G + h) * D + lp * 8 + e] = acc[h][e];
+  }
   __syncthreads();
   // ---- this split's partial, tagged with the step
   const size_t pbase = ((size_t)bg * P.NS + sp) * G;
