@@ -65,7 +65,7 @@ typedef struct mk_model_cfg {
   int32_t batch;      /* B independent sequences decoded together           */
   int32_t max_seq;    /* KV capacity in positions per sequence              */
   int32_t mode;       /* MK_MODE_*                                          */
-  int32_t split;      /* KV positions per attention task; 0 = default (64)  */
+  int32_t split;      /* KV positions per attention task; 0 = default rule   */
   int32_t n_workers;  /* persistent workgroups; 0 = one per compute unit    */
   uint32_t watchdog_polls; /* max polls of one event wait; 0 = default     */
   void* stream;       /* hipStream_t the library launches on, or NULL       */
@@ -90,8 +90,12 @@ typedef struct mk_tensor {
 
 /* Validate cfg, build the task graph (host only) and allocate every device
  * buffer: packed weights, KV cache [L][B][Hkv][max_seq][D] bf16 (K and V),
- * activations, event flags.  *out receives the context.  Errors:
- * INVALID_ARG, UNSUPPORTED (shape cannot be tiled), OOM, HIP. */
+ * activations, event flags.  *out receives the context.  With cfg.split == 0
+ * the attention split is S = min(20480 / head_dim, max(32, ceil(max_seq /
+ * max(1, workers / (batch * n_kv_heads))))) positions.  Batch 8 and 16 run the
+ * projections on the matrix cores and need hidden, ffn and n_q_heads *
+ * head_dim to be multiples of 512.  Errors: INVALID_ARG, UNSUPPORTED (shape
+ * cannot be tiled), OOM, HIP. */
 int mk_create(const mk_model_cfg* cfg, mk_ctx** out);
 
 /* Copy and repack all weights.  Exactly the canonical set must be given,

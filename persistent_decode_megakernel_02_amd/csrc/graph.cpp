@@ -43,8 +43,9 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   if (G > 8) return "at most 8 query heads per KV head";
   if (c.hidden % 8 || c.ffn % 8) return "hidden and ffn must be multiples of 8";
   // Default split: enough splits that the (sequence, KV head, split) tasks of a
-  // full cache fill the workers once, each split between 64 positions and the
-  // per-task register budget (5 * 4096 / D positions).
+  // full cache fill the workers once, each split between 32 positions and the
+  // per-task register budget (5 * 4096 / D positions).  Attention tasks are
+  // latency-bound at short contexts, so more, shorter splits finish sooner.
   const int smax = 5 * 4096 / D;
   int S = c.split;
   if (S <= 0) {

@@ -25,6 +25,6 @@ struct Graph {
 std::string build_graph(const mk_model_cfg& cfg, int n_workers, Graph* g);
 std::vector<uint8_t> serialize_graph(const mk_model_cfg& cfg, const Graph& g);
 
-constexpr int kDefaultSplit = 64;
+constexpr int kDefaultSplit = 32;  // smallest default split (positions per attention task)
 
 }  // namespace mk

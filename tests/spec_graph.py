@@ -11,7 +11,7 @@ Rules (one decode step; the persistent kernel repeats it every step):
     KV-head group of RG = (G + 2) D fused rows with TG = min(max(1, workers // Hkv), RG)
     tiles per group; group g's rows start at g * RG.
   * ATTN: one task per (split s, sequence b, KV head g), split-major, split s
-    covering positions [s S, (s + 1) S), S = 64 unless given, NS = ceil(max_seq / S).
+    covering positions [s S, (s + 1) S), S from the default rule unless given, NS = ceil(max_seq / S).
   * Task number k of an operator runs on worker k mod workers.
   * Events per layer: Hkv QKV-group events, ATT, O, A, X; then one LM event.
     Fan-ins: TG, B*Hkv, T_wo, T_gu, T_down, T_lm.  Slots are numbered
@@ -49,9 +49,9 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
     G = Hq // Hkv
     if split > 0:
         S = split
-    else:  # splits of a full cache fill the workers once; 64 <= S <= 5 * 4096 / D
+    else:  # splits of a full cache fill the workers once; 32 <= S <= 5 * 4096 / D
         ns_target = max(1, workers // max(1, B * Hkv))
-        S = min(5 * 4096 // D, max(64, -(-max_seq // ns_target)))
+        S = min(5 * 4096 // D, max(32, -(-max_seq // ns_target)))
     NS = -(-max_seq // S)
     RG = (G + 2) * D
     TG = min(max(1, workers // Hkv), RG)
