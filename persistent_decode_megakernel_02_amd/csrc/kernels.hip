@@ -509,6 +509,15 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       for (int b = 0; b < NB; ++b) stc(P.x + (size_t)b * P.H + i, bf1(ldg(P.embed + (size_t)m->tok[b] * P.H + i)));
   }
 
+  // The residual this task adds to (O-projection, down projection) is read now,
+  // after the wait, so the epilogue does not wait a round trip for it.
+  const bool resid = op == OP_WO || op == OP_DOWN;
+  float xpre = 0.f;
+  if (resid && tid < nu * NB) {
+    const int ul = tid / NB, b = tid - ul * NB;
+    xpre = ldc(P.x + (size_t)b * P.H + u0 + ul);
+  }
+
   for (int sl = 0; sl < nsl; ++sl) {
     sl_cur = sl;
     if (sl > 0) {
@@ -628,11 +637,11 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       const int ul = i / NB, b = i - ul * NB;
       stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, (float)(red[ul * NB + b] * rs[b]));
     }
-  } else if (op == OP_WO || op == OP_DOWN) {
+  } else if (resid) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
       float* xp = P.x + (size_t)b * P.H + u0 + ul;
-      stc(xp, (float)((double)ldc(xp) + red[ul * NB + b]));
+      stc(xp, (float)((double)(i == tid ? xpre : ldc(xp)) + red[ul * NB + b]));
     }
   } else if (op == OP_GU) {
     for (int i = tid; i < nu * NB; i += NT) {
@@ -988,6 +997,12 @@ __device__ __forceinline__ void st_tv(TV* p, uint32_t bits, uint32_t tag) {
 __device__ __forceinline__ uint64_t ld_tv(const TV* p) {
   return __hip_atomic_load((const GAS uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// the same coherent 8-byte load through a buffer resource: one 32-bit lane offset
+// and a scalar offset, so a burst of such loads holds no 64-bit addresses
+__device__ __forceinline__ uint64_t ld_tv_b(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 16 /* sc1 */);
+  return ((uint64_t)v.y << 32) | v.x;
+}
 __device__ __forceinline__ bool tv_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 // an fp64 value as two tagged words: p[0] low half, p[1] high half
 __device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
@@ -1054,10 +1069,17 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   uint16_t* kcur = (uint16_t*)(qrot + G * D);  // [D]
   uint16_t* vcur = kcur + D;                   // [D]
   double* sc = (double*)(vcur + D);            // [G S]
-  double* accw = sc + G * S;                   // [NW G D]
+  uint16_t* vsm = (uint16_t*)(sc + G * ((S + 1) & ~1));  // [S D] this split's values (bf16)
+  double* accw = (double*)(vsm + S * D);       // P.V partial sums, then the merge's scratch
 
   const float* src = P.qkv + (size_t)b * P.QKVR + (size_t)g * P.RG;
   for (int i = tid * 4; i < (G + 2) * D; i += NT * 4) *(v4f*)(raw + i) = ldc4(src, (uint32_t)i);
+  // the cached values, position-major, for the P.V pass
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int jr = po + i * PPB;
+    if (jr < S && j0 + jr < jc) *(uint4*)(vsm + jr * D + lp * 8) = vr[i];
+  }
   __syncthreads();
   if (P.qk_norm) {
     for (int h = w; h < nh; h += NW) {
@@ -1085,7 +1107,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
   }
   if (has_cur)
-    for (int i = tid; i < D; i += NT) vcur[i] = f2bf(raw[(G + 1) * D + i]);
+    for (int i = tid; i < D; i += NT) vcur[i] = vsm[(pos - j0) * D + i] = f2bf(raw[(G + 1) * D + i]);
   __syncthreads();
   if (has_cur && tid < LPP) {  // append this position's K/V to the cache
     stg((uint4*)(Kh + (size_t)pos * D + tid * 8), *(const uint4*)(kcur + tid * 8));
@@ -1136,43 +1158,29 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
   }
   __syncthreads();
-  // ---- unnormalised P.V, one head at a time; the sum over this wave's positions
-  // (lanes with the same lp) is written per wave
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    double acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int jr = po + i * PPB, j = j0 + jr;
-      if (i * PPB < S && jr < S && j < j1) {
-        const uint4 vv = (has_cur && j == pos) ? *(const uint4*)(vcur + lp * 8) : vr[i];
-        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-        const double p = sc[h * S + jr];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fma(p, (double)bf_lo(vw[e]), acc[2 * e]);
-          acc[2 * e + 1] = fma(p, (double)bf_hi(vw[e]), acc[2 * e + 1]);
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      double v = acc[e];
-      if (LPP == 8) v += dpp_d<0x128>(v);  // row_ror:8 (lane i and i^8)
-      v = xor32_pair_d(xor16_pair_d(v));
-      if (lane < LPP) accw[(w * G + h) * D + lp * 8 + e] = v;
-    }
+  // ---- unnormalised P.V: thread (h, d) of the group's G heads sums e^{t_j - m} v_j[d]
+  // over this split's positions in ascending order (RP interleaved partial sums,
+  // added in order, when G * D < NT)
+  constexpr int GD = G * D, RP = NT / GD;
+  double pv = 0.0;
+  {
+    const int e = tid % GD, r = tid / GD;
+    const int h = e / D, d = e - h * D;
+    const double* ph = sc + h * S;
+    double a = 0.0;
+    for (int jr = r; jr < n; jr += RP) a = fma(ph[jr], (double)bf1(vsm[jr * D + d]), a);
+    if constexpr (RP > 1) accw[r * GD + e] = a;
+    else pv = a;
   }
-  __syncthreads();
+  if constexpr (RP > 1) {
+    __syncthreads();
+    if (tid < GD)
+#pragma unroll
+      for (int r = 0; r < RP; ++r) pv += accw[r * GD + tid];
+  }
   // ---- this split's partial, tagged with the step
   const size_t pbase = ((size_t)bg * P.NS + sp) * G;
-  for (int i = tid; i < G * D; i += NT) {
-    double v = 0.0;
-    for (int ww = 0; ww < NW; ++ww) v += accw[ww * G * D + i];
-    st_tvd(P.part_acc + (pbase * D + i) * 2, v, tag);
-  }
+  if (tid < GD) st_tvd(P.part_acc + (pbase * D + tid) * 2, pv, tag);
   if (tid < G) {
     st_tvd(P.part_ml + ((pbase + tid) * 2) * 2, m->ml[tid][0], tag);
     st_tvd(P.part_ml + ((pbase + tid) * 2 + 1) * 2, m->ml[tid][1], tag);
