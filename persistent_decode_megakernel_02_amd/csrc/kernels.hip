@@ -152,11 +152,13 @@ __device__ __forceinline__ int ltid() {
 }
 
 // Cross-lane reductions in VALU (DPP row operations and the gfx950
-// permlane swaps), no LDS traffic.  Every lane of a group receives the same,
+// permlane swaps), no LDS traffic.  Only patterns within a row of 16 lanes are
+// used (quad permutes, row mirrors), so every lane reads a valid source and
+// the DPP moves need no fill value.  Every lane of a group receives the same,
 // bit-identical result (each step adds the same two operands on all lanes).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 __device__ __forceinline__ float xor16_pair(float v) {  // lanes i and i^16 both get v_i + v_{i^16}
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -194,8 +196,8 @@ __device__ __forceinline__ float wave_max(float v) {
 // fp64 versions: the two 32-bit halves move through the same lane permutation
 template <int CTRL>
 __device__ __forceinline__ double dpp_d(double v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xf, 0xf, false);
   return __hiloint2double(hi, lo);
 }
 __device__ __forceinline__ double xor16_pair_d(double v) {
@@ -225,6 +227,20 @@ __device__ __forceinline__ double group_sum_d(double v) {
   if (N >= 8) v += dpp_d<0x141>(v);
   if (N >= 16) v += dpp_d<0x140>(v);
   return v;
+}
+// group_sum_d over NV independent values at once (each step on all of them)
+template <int N, int NV>
+__device__ __forceinline__ void group_sum_d_n(double* v) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] += dpp_d<0xB1>(v[k]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] += dpp_d<0x4E>(v[k]);
+  if (N >= 8)
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] += dpp_d<0x141>(v[k]);
+  if (N >= 16)
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] += dpp_d<0x140>(v[k]);
 }
 __device__ __forceinline__ double wave_sum_d(double v) { return xor32_pair_d(xor16_pair_d(group_sum_d<16>(v))); }
 __device__ __forceinline__ double wave_max_d(double v) {
@@ -1109,13 +1125,18 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   if (has_cur)
     for (int i = tid; i < D; i += NT) vcur[i] = vsm[(pos - j0) * D + i] = f2bf(raw[(G + 1) * D + i]);
   __syncthreads();
-  if (has_cur && tid < LPP) {  // append this position's K/V to the cache
-    stg((uint4*)(Kh + (size_t)pos * D + tid * 8), *(const uint4*)(kcur + tid * 8));
-    stg((uint4*)(Vh + (size_t)pos * D + tid * 8), *(const uint4*)(vcur + tid * 8));
-  }
 
   // ---- scores t_j = (q_h . k_j) / sqrt(D); LPP lanes share one position.  Heads go
   // one at a time so that only one head's query slice and sums occupy registers.
+  // The current position's key (rotated above) joins the cached ones first.
+  const int n = j1 - j0;
+  if (has_cur)
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      if (j0 + po + i * PPB == pos) kr[i] = *(const uint4*)(kcur + lp * 8);
+  // Dot products of every (head, position block) first, then their 16-lane sums
+  // side by side, so the reduction chains overlap instead of running head after head.
+  double dots[G][NL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     double q[8];
@@ -1123,24 +1144,26 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     for (int e = 0; e < 8; ++e) q[e] = qrot[h * D + lp * 8 + e];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      if (i * PPB < S) {
-        const int jr = po + i * PPB, j = j0 + jr;
-        const uint4 kk = (has_cur && j == pos) ? *(const uint4*)(kcur + lp * 8) : kr[i];
-        const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-        double a = 0.0;
+      const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+      double a = 0.0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a = fma(q[2 * e], (double)bf_lo(kw[e]), a);
-          a = fma(q[2 * e + 1], (double)bf_hi(kw[e]), a);
-        }
-        a = group_sum_d<LPP>(a);
-        if (jr < S && j < j1 && lp == 0) sc[h * S + jr] = a * P.attn_scale;
+      for (int e = 0; e < 4; ++e) {
+        a = fma(q[2 * e], (double)bf_lo(kw[e]), a);
+        a = fma(q[2 * e + 1], (double)bf_hi(kw[e]), a);
       }
+      dots[h][i] = a;
     }
   }
+  group_sum_d_n<LPP, G * NL>(&dots[0][0]);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int jr = po + i * PPB;
+      if (jr < n && lp == 0) sc[h * S + jr] = dots[h][i] * P.attn_scale;
+    }
   __syncthreads();
   // ---- split softmax statistics per head
-  const int n = j1 - j0;
   for (int h = w; h < G; h += NW) {
     double mx = -INFINITY;
     for (int jr = lane; jr < n; jr += 64) mx = fmax(mx, sc[h * S + jr]);
@@ -1168,7 +1191,18 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     const int h = e / D, d = e - h * D;
     const double* ph = sc + h * S;
     double a = 0.0;
-    for (int jr = r; jr < n; jr += RP) a = fma(ph[jr], (double)bf1(vsm[jr * D + d]), a);
+    for (int j8 = r; j8 < n; j8 += 8 * RP) {  // 8 positions' LDS reads in flight, then the sums in order
+      double pp[8], vv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jr = min(j8 + u * RP, n - 1);
+        pp[u] = ph[jr];
+        vv[u] = (double)bf1(vsm[jr * D + d]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j8 + u * RP < n) a = fma(pp[u], vv[u], a);
+    }
     if constexpr (RP > 1) accw[r * GD + e] = a;
     else pv = a;
   }
@@ -1255,6 +1289,14 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
       }
     }
     if (ok_all) stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, (float)(num / m->ml[h][1]));
+  }
+  // Append this position's K/V to the cache.  Only later steps read it, after
+  // the signal below; issued here, the stores complete alongside those of o
+  // instead of stalling the scores (a store's registers are reusable only
+  // once it has completed).
+  if (tid < LPP) {
+    stg((uint4*)(Kh + (size_t)pos * D + tid * 8), *(const uint4*)(kcur + tid * 8));
+    stg((uint4*)(Vh + (size_t)pos * D + tid * 8), *(const uint4*)(vcur + tid * 8));
   }
   if (!ok_all) {
     uint32_t zero = 0u;
