@@ -27,7 +27,8 @@ namespace mk {
 constexpr int NT = 512;  // threads per worker
 constexpr int NW = NT / 64;
 constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
-constexpr int DEPTH = 4;   // pipeline groups in flight per wave (16 KB per wave)
+constexpr int DEPTH = 2;   // pipeline groups in flight per wave (8 KB per wave): a wave's loads complete in
+                          // order, so a deeper queue delays the activation and flag loads behind it
 constexpr int MISC_BYTES = 4096;
 constexpr int ATT_MAXL = 5;  // most K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8))
 
