@@ -26,7 +26,7 @@ size_t lds_bytes(const KParams& P);
 int max_coresident_workers(int B, size_t lds);
 constexpr int kLdsBytes = 163840;  // one worker per compute unit takes all of its LDS
 constexpr int kMiscBytes = 4096;   // per-worker scalars at the top of LDS (same size as in the kernels)
-constexpr int kMaxSlice = 1536;    // largest K slice of the matrix-core GEMV (same as in the kernels)
+constexpr int kMkSlice = 2048;     // K slice of the matrix-core GEMV (same as in the kernels)
 constexpr uint32_t kDefaultWatchdog = 1u << 22;  // ~1-2 us per poll: several seconds, far above any healthy wait
 }  // namespace mk
 
@@ -136,8 +136,8 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
   LdsPlan L;
   L.mk_ks = 0;
   if (B >= 8) {
-    // matrix-core GEMV: passes of up to 8 row tiles (128 rows), K staged in slices of three bf16 pieces
-    // (96 bytes per K element at 16 columns), each wave taking 1/8 of a slice in pairs of 32-element steps
+    // matrix-core GEMV: passes of up to 8 row tiles (128 rows), K staged in slices of kMkSlice elements
+    // as fp32 at 16 columns (64 bytes per K element), each wave taking 1/8 of a slice
     if (cfg.hidden % 512 || cfg.ffn % 512 || (cfg.n_q_heads * D) % 512) {
       *why = "batch >= 8 needs hidden, ffn and n_q_heads * head_dim to be multiples of 512";
       return MK_ERR_UNSUPPORTED;
@@ -145,9 +145,9 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
     L.red_doubles = 128 * B;
     L.misc_off = kLdsBytes - kMiscBytes;
     L.red_off = L.misc_off - L.red_doubles * 8;
-    L.mk_ks = std::min(kMaxSlice, L.red_off / 96 / 512 * 512);
+    L.mk_ks = kMkSlice;
     L.xs_doubles = L.red_off / 8;
-    if (L.mk_ks < 512 || 8 * 8 * 256 * 4 > L.red_off) {
+    if ((int64_t)kMkSlice * 64 > L.red_off) {
       *why = "LDS too small for the matrix-core GEMV";
       return MK_ERR_UNSUPPORTED;
     }

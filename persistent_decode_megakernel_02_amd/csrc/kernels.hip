@@ -49,6 +49,9 @@ struct Misc {
   double hr[16];        // QK-norm scales
   double ml[8][2];      // attention (max, sum) per head
   int32_t flag;
+  double rsd[16];       // matrix-core GEMV: RMSNorm scale per sequence
+  float lmv[16];        // matrix-core LM head: running (max, index) per sequence
+  int32_t lmi[16];
 };
 static_assert(sizeof(Misc) <= MISC_BYTES, "misc");
 
@@ -711,17 +714,23 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 // (columns beyond B are zero).  Each fp32 activation is split exactly into
 // three bf16 pieces, x = x0 + x1 + x2, so every product W * x_p is exact; the
 // only rounding before the fp64 epilogue is the fp32 accumulation inside one
-// wave's share of K.  The eight waves split K and their partial sums are added
-// in fp64.  K is staged in LDS in slices of P.mk_ks elements (pieces laid out
-// [piece][8-element block][column][8 x bf16]), rows go in tiles of 16, and up
-// to MT tiles share one pass over K (more tiles take more passes).
+// wave's share of K.  The eight waves split every K slice and their partial
+// sums are added in fp64.
+// K goes through LDS in slices of MK_KS elements, staged as fp32 x * gamma
+// (layout [8-element block][column][8 x fp32]) and split into the three pieces
+// when a step reads them.  K is padded to whole slices: the padding's
+// activations are zero and its weight loads re-read the row's last chunk.
+// Each wave takes MK_KS / 8 elements (MK_SPS steps of 32) of every slice.  Rows
+// go in tiles of 16, up to MT tiles per pass over K.  The weights stream
+// through NBUF register buffers of NTB tile slots (NBUF * NTB = 16, at most 8
+// buffers): with few tiles, more steps are in flight.
 // Lane layout on gfx950: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]
 // and D[4(l/16)+r][l%16], e < 8, r < 4.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-constexpr int MT = 8;        // row tiles per pass
-constexpr int MAX_KS = 1536; // largest K slice the host plans (a multiple of 512, as is K)
-constexpr int MSTEPS = MAX_KS / 8 / 32;  // 32-element steps per wave per slice, at most
+constexpr int MT = 8;                    // row tiles per pass
+constexpr int MK_KS = 2048;              // K elements per staged slice (the host plans the same)
+constexpr int MK_SPS = MK_KS / NW / 32;  // 32-element steps per wave per slice
 
 // x = bf16(p0) + bf16(p1) + bf16(p2) exactly (truncations of x and of the exact remainders)
 __device__ __forceinline__ void split3(float x, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
@@ -734,57 +743,114 @@ __device__ __forceinline__ void split3(float x, uint32_t& p0, uint32_t& p1, uint
   p2 = __float_as_uint(r2) >> 16;
 }
 
+// Stage K elements [k0, k0 + MK_KS) of the B activation rows as fp32 x * gamma
+// (zero beyond K).  Thread tid takes column tid % 16 and 8-element blocks
+// tid / 16, tid / 16 + NT / 16, ...; IB blocks' loads are in flight together.
+// src is the activation array (row stride `stride`), read with device-coherent
+// loads; layer-0 Q/K/V reads the embedding rows instead.  src is a plain,
+// uniform argument: a buffer resource built from a per-lane pointer would need
+// a loop over its distinct values.
 template <int NB>
-__device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
-                                               uint64_t* tr) {
-  const int op = (int)t.op, l = (int)t.layer;
+__device__ __forceinline__ void mfma_stage(const KParams& P, const float* src, int stride, bool embed_src,
+                                           const uint16_t* gamma, const Misc* m, int k0, int K, bool sumsq,
+                                           char* lds, double& ss) {
+  const int tid = ltid(), jcol = tid & 15;
+  const bool norm = gamma != nullptr;
+  const uint32_t scol = (uint32_t)jcol * (uint32_t)stride;  // this column's row, as a per-lane offset
+  constexpr int items = (MK_KS / 8) * 16;
+  constexpr int IB = 4;
+  static_assert(items % (NT * IB) == 0, "staging items");
+#pragma unroll 1
+  for (int it0 = tid; it0 < items; it0 += NT * IB) {
+    uint4 raw[IB][2], gqa[IB];
+#pragma unroll
+    for (int q = 0; q < IB; ++q) {
+      const int kb = k0 + 8 * ((it0 + q * NT) >> 4);
+      if (jcol < NB && kb < K) {
+        if (embed_src) {
+          raw[q][0] = ld16(P.embed + (size_t)m->tok[jcol] * P.H + kb);
+        } else {
+          raw[q][0] = __builtin_bit_cast(uint4, ldc4(src, scol + (uint32_t)kb));
+          raw[q][1] = __builtin_bit_cast(uint4, ldc4(src, scol + (uint32_t)kb + 4u));
+        }
+        if (norm) gqa[q] = ld16(gamma + kb);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < IB; ++q) {
+      const int it = it0 + q * NT, c = it >> 4, kb = k0 + 8 * c;
+      float xv[8];
+      if (jcol < NB && kb < K) {
+        if (embed_src) {
+          const uint32_t qw[4] = {raw[q][0].x, raw[q][0].y, raw[q][0].z, raw[q][0].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xv[2 * e] = bf_lo(qw[e]);
+            xv[2 * e + 1] = bf_hi(qw[e]);
+          }
+        } else {
+          const uint32_t xw[8] = {raw[q][0].x, raw[q][0].y, raw[q][0].z, raw[q][0].w,
+                                  raw[q][1].x, raw[q][1].y, raw[q][1].z, raw[q][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xv[e] = __uint_as_float(xw[e]);
+        }
+        if (norm) {
+          const uint32_t gw[4] = {gqa[q].x, gqa[q].y, gqa[q].z, gqa[q].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double xd = xv[e];
+            if (sumsq) ss += xd * xd;
+            xv[e] = (float)(xd * (double)((e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1])));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = 0.f;
+      }
+      char* xb = lds + (size_t)(c * 16 + jcol) * 32;
+      *(v4f*)(xb) = v4f{xv[0], xv[1], xv[2], xv[3]};
+      *(v4f*)(xb + 16) = v4f{xv[4], xv[5], xv[6], xv[7]};
+    }
+  }
+}
+
+template <int NB, int NTB>
+__device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, int s, bool mega, char* lds, uint64_t* tr,
+                                          int op, const uint16_t* W0, const uint16_t* W1, const uint16_t* gamma, int K,
+                                          int RU) {
+  constexpr int NBUF = (16 / NTB) > 8 ? 8 : 16 / NTB;
+  static_assert(MK_SPS % NBUF == 0, "buffers per slice");
+  const int l = (int)t.layer;
   const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lq = lane >> 4;  // MFMA row / column index and K quarter of this lane
   double* red = (double*)(lds + P.red_off);
   Misc* m = (Misc*)(lds + P.misc_off);
-  const LayerW LW = ldg(P.layers + (op == OP_LM ? 0 : l));
-
-  const uint16_t* W0;
-  const uint16_t* W1 = nullptr;
-  const uint16_t* gamma = nullptr;
-  int K, RU = 1;
-  switch (op) {
-    case OP_QKV: W0 = LW.wqkv; K = P.H; gamma = LW.attn_norm; break;
-    case OP_WO: W0 = LW.wo; K = P.QD; break;
-    case OP_GU: W0 = LW.wg; W1 = LW.wu; K = P.H; RU = 2; gamma = LW.ffn_norm; break;
-    case OP_DOWN: W0 = LW.wd; K = P.F; break;
-    default: W0 = P.lm_head; K = P.H; gamma = P.final_norm; break;
-  }
   const bool norm = gamma != nullptr;
   const bool embed_src = (op == OP_QKV && l == 0);
   const int u0 = (int)t.a0, nu = (int)t.a1 - (int)t.a0;
   const int R = nu * RU, T = (R + 15) >> 4;
-  const int ks = P.mk_ks, CB = ks >> 3;
-  const int nsl = (K + ks - 1) / ks;
+  const int nsl = (K + MK_KS - 1) / MK_KS;
   const int npass = (T + MT - 1) / MT;
+  const int gsteps = npass * nsl * MK_SPS;  // this wave's steps, over every pass and slice
 
-  auto rowptr = [&](int r) -> const uint16_t* {
-    r = min(r, R - 1);
-    const int ui = RU == 2 ? (r >> 1) : r;
-    const uint16_t* base = (RU == 2 && (r & 1)) ? W1 : W0;
-    return base + (size_t)(u0 + ui) * K;
-  };
-  // the step sequence of this wave: (pass, slice, 32-element step of the wave's share of the slice)
-  int cp = 0, csl = 0, cst = 0;
-  auto nsteps = [&](int sl) { return (min(ks, K - sl * ks) >> 3) >> 5; };
-  auto step_k = [&](int sl, int st) { return sl * ks + w * (min(ks, K - sl * ks) >> 3) + 32 * st; };
-  uint4 A[2][MT];
-  auto issue = [&](uint4 (&a)[MT], int pass, int sl, int st) {
-    const int kk = step_k(sl, st) + 8 * lq;
+  // the weights of this wave's step g (pass, slice, step), one 16-byte chunk per tile slot
+  auto issue = [&](uint4 (&a)[NTB], int g) {
+    if (g >= gsteps) return;
+    const int pass = g / (nsl * MK_SPS), r = g - pass * nsl * MK_SPS;
+    const int sl = r / MK_SPS, st = r - sl * MK_SPS;
+    const int kk = min(sl * MK_KS + w * (MK_KS / NW) + 32 * st + 8 * lq, K - 8);
 #pragma unroll
-    for (int tt = 0; tt < MT; ++tt) {
-      const int tile = pass * MT + tt;
-      a[tt] = ldw(rowptr(min(tile, T - 1) * 16 + li) + kk);
+    for (int tt = 0; tt < NTB; ++tt) {
+      const int row = min((min(pass * MT + tt, T - 1)) * 16 + li, R - 1);
+      const int ui = RU == 2 ? (row >> 1) : row;
+      const uint16_t* base = (RU == 2 && (row & 1)) ? W1 : W0;
+      a[tt] = ldw(base + (size_t)(u0 + ui) * K + kk);
     }
   };
-
-  // weights do not depend on the event: the first step's loads go out before the wait
-  issue(A[0], 0, 0, 0);
+  uint4 A[NBUF][NTB];
+  // weights do not depend on the event: the first NBUF steps go out before the wait
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) issue(A[b], b);
 
   if (mega && !(s == 0 && t.wait_lag) &&
       !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m, tr))
@@ -810,111 +876,61 @@ __device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& 
       for (int b = 0; b < NB; ++b) stc(P.x + (size_t)b * P.H + i, bf1(ldg(P.embed + (size_t)m->tok[b] * P.H + i)));
   }
 
-  const int jcol = tid & 15;  // every staging item of this thread belongs to column jcol
-  double ss = 0.0;            // sum of squares of column jcol (first pass)
-  float bv[NB];
-  int32_t bi[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    bv[b] = -INFINITY;
-    bi[b] = 0x7fffffff;
+  double ss = 0.0;  // sum of squares of column tid % 16 (first pass)
+  if (op == OP_LM && tid < NB) {
+    m->lmv[tid] = -INFINITY;
+    m->lmi[tid] = 0x7fffffff;
   }
-  const float* src = op == OP_WO ? P.o : op == OP_DOWN ? P.a : P.x;
-  const int sstride = op == OP_WO ? P.QD : op == OP_DOWN ? P.F : P.H;
 
+  int g = 0;  // this wave's next step
   for (int pass = 0; pass < npass; ++pass) {
     const int tp0 = pass * MT, ntp = min(MT, T - tp0);
-    v4f acc[MT];
+    v4f acc[NTB];
 #pragma unroll
-    for (int tt = 0; tt < MT; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NTB; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int sl = 0; sl < nsl; ++sl) {
-      const int k0 = sl * ks, ksc = min(ks, K - k0);
-      // ---- stage this slice: x (* gamma) split into three bf16 pieces per column
+      const int k0 = sl * MK_KS;
       __syncthreads();  // the previous slice (or pass) is no longer read
-      {
-        const int items = (ksc >> 3) * 16;
-        for (int it = tid; it < items; it += NT) {
-          const int c = it >> 4, kb = k0 + 8 * c;
-          float xv[8];
-          if (jcol < NB) {
-            if (embed_src) {
-              const uint4 q = ld16(P.embed + (size_t)m->tok[jcol] * P.H + kb);
-              const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+      const bool sumsq = norm && pass == 0;
+      if (op == OP_WO) mfma_stage<NB>(P, P.o, P.QD, false, nullptr, m, k0, K, false, lds, ss);
+      else if (op == OP_DOWN) mfma_stage<NB>(P, P.a, P.F, false, nullptr, m, k0, K, false, lds, ss);
+      else mfma_stage<NB>(P, P.x, P.H, embed_src, gamma, m, k0, K, sumsq, lds, ss);
+      __syncthreads();
+      if (tr && pass == 0 && sl == 0 && tid == 0) tr[2] = wall_clock64();
+      // ---- this wave's MK_SPS steps of the slice; each consumes buffer b, then refills it
+      // with the step NBUF ahead (which may belong to the next slice or pass)
+      for (int st0 = 0; st0 < MK_SPS; st0 += NBUF) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                xv[2 * e] = bf_lo(qw[e]);
-                xv[2 * e + 1] = bf_hi(qw[e]);
-              }
-            } else {
-              const v4f a0 = ldc4(src + (size_t)jcol * sstride, (uint32_t)kb);
-              const v4f a1 = ldc4(src + (size_t)jcol * sstride, (uint32_t)kb + 4u);
-              xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
-              xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
-            }
-            if (norm) {
-              const uint4 gq = ld16(gamma + kb);
-              const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w};
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const double xd = xv[e];
-                if (pass == 0) ss += xd * xd;
-                xv[e] = (float)(xd * (double)((e & 1) ? bf_hi(gw[e >> 1]) : bf_lo(gw[e >> 1])));
-              }
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xv[e] = 0.f;
-          }
+        for (int b = 0; b < NBUF; ++b) {
+          const int cblk = (w * (MK_KS / NW) + 32 * (st0 + b)) / 8 + lq;  // 8-element block of this lane
+          const char* xb = lds + (size_t)(cblk * 16 + li) * 32;
+          const v4f xa = *(const v4f*)(xb), xc = *(const v4f*)(xb + 16);
+          const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xc.x, xc.y, xc.z, xc.w};
           uint32_t p0[8], p1[8], p2[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) split3(xv[e], p0[e], p1[e], p2[e]);
-          char* xb = lds + (size_t)(c * 16 + jcol) * 16;
-          *(uint4*)(xb) = make_uint4(p0[0] | (p0[1] << 16), p0[2] | (p0[3] << 16), p0[4] | (p0[5] << 16), p0[6] | (p0[7] << 16));
-          *(uint4*)(xb + (size_t)CB * 256) = make_uint4(p1[0] | (p1[1] << 16), p1[2] | (p1[3] << 16), p1[4] | (p1[5] << 16), p1[6] | (p1[7] << 16));
-          *(uint4*)(xb + (size_t)CB * 512) = make_uint4(p2[0] | (p2[1] << 16), p2[2] | (p2[3] << 16), p2[4] | (p2[5] << 16), p2[6] | (p2[7] << 16));
-        }
-      }
-      __syncthreads();
-      if (tr && pass == 0 && sl == 0 && tid == 0) tr[2] = wall_clock64();
-      // ---- this wave's share of the slice, 32 elements per step, steps in pairs (a slice
-      // has an even number of them) so that the two weight buffers are indexed statically;
-      // each step requests the next step's weights before its own MFMAs
-      const int nst = nsteps(sl);
-      auto step = [&](uint4 (&cur)[MT], uint4 (&nxt)[MT], int st) {
-        int np = pass, nsl2 = sl, nst2 = st + 1;  // next step in (pass, slice, step) order
-        if (nst2 == nst) {
-          nst2 = 0;
-          if (++nsl2 == nsl) {
-            nsl2 = 0;
-            ++np;
-          }
-        }
-        if (np < npass) issue(nxt, np, nsl2, nst2);
-        const int cbase = ((step_k(sl, st) - k0) >> 3) + lq;
-        const char* xb = lds + (size_t)(cbase * 16 + li) * 16;
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *(const uint4*)(xb));
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *(const uint4*)(xb + (size_t)CB * 256));
-        const bf16x8 b2 = __builtin_bit_cast(bf16x8, *(const uint4*)(xb + (size_t)CB * 512));
+          const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(p0[0] | (p0[1] << 16), p0[2] | (p0[3] << 16), p0[4] | (p0[5] << 16), p0[6] | (p0[7] << 16)));
+          const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(p1[0] | (p1[1] << 16), p1[2] | (p1[3] << 16), p1[4] | (p1[5] << 16), p1[6] | (p1[7] << 16)));
+          const bf16x8 b2 = __builtin_bit_cast(bf16x8, make_uint4(p2[0] | (p2[1] << 16), p2[2] | (p2[3] << 16), p2[4] | (p2[5] << 16), p2[6] | (p2[7] << 16)));
 #pragma unroll
-        for (int tt = 0; tt < MT; ++tt) {
-          if (tt < ntp) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, cur[tt]);
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[tt], 0, 0, 0);
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[tt], 0, 0, 0);
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, acc[tt], 0, 0, 0);
+          for (int tt = 0; tt < NTB; ++tt) {
+            if (tt < ntp) {
+              const bf16x8 a = __builtin_bit_cast(bf16x8, A[b][tt]);
+              acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[tt], 0, 0, 0);
+              acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[tt], 0, 0, 0);
+              acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, acc[tt], 0, 0, 0);
+            }
           }
+          issue(A[b], g + NBUF);
+          ++g;
         }
-      };
-      for (int st = 0; st < nst; st += 2) {
-        step(A[0], A[1], st);
-        step(A[1], A[0], st + 1);
       }
     }
     // ---- add the eight waves' partial tiles in fp64 (the staging area is free now)
     __syncthreads();
     float* part = (float*)lds;  // [wave][tile][256]
 #pragma unroll
-    for (int tt = 0; tt < MT; ++tt)
+    for (int tt = 0; tt < NTB; ++tt)
       if (tt < ntp)
 #pragma unroll
         for (int r = 0; r < 4; ++r) part[((size_t)w * MT + tt) * 256 + (lq * 4 + r) * 16 + li] = acc[tt][r];
@@ -933,15 +949,14 @@ __device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& 
       for (int ww = 0; ww < NW; ++ww) v += (double)part[((size_t)ww * MT + tt) * 256 + ri * 16 + b];
       red[rr * NB + b] = v;
     }
-    __syncthreads();
-    // ---- epilogue for this pass's rows
-    double rs[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    // ---- epilogue for this pass's rows (the RMSNorm scale per sequence, formed once, in LDS)
+    if (tid < NB) {
       double tot = 0.0;
-      for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][b];
-      rs[b] = norm ? 1.0 / sqrt(tot / (double)K + (double)P.eps) : 1.0;
+      for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][tid];
+      m->rsd[tid] = norm ? 1.0 / sqrt(tot / (double)K + (double)P.eps) : 1.0;
     }
+    __syncthreads();
+    const double* rs = m->rsd;
     const int pu0 = u0 + tp0 * 16 / RU, pnu = rows / RU;
     if (op == OP_QKV) {
       for (int i = tid; i < pnu * NB; i += NT) {
@@ -962,37 +977,68 @@ __device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& 
         stc(P.a + (size_t)b * P.F + pu0 + ul, (float)(silu_d(gt) * up));
       }
     } else {  // OP_LM
-      for (int ul = tid; ul < pnu; ul += NT) {
+      if (P.out_logits)
+        for (int ul = tid; ul < pnu; ul += NT)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float logit = (float)(red[ul * NB + b] * rs[b]);
-          if (P.out_logits) stg(P.out_logits + ((size_t)s * P.B + b) * P.V + pu0 + ul, logit);
-          amax_merge(bv[b], bi[b], logit, pu0 + ul);
-        }
+          for (int b = 0; b < NB; ++b)
+            stg(P.out_logits + ((size_t)s * P.B + b) * P.V + pu0 + ul, (float)(red[ul * NB + b] * rs[b]));
+      // this pass's (max, lowest index) per sequence: thread (b, c) scans rows c, c + TPB, ... of
+      // sequence b, then the TPB threads of b (adjacent lanes of one wave) combine theirs
+      constexpr int TPB = NT / NB;
+      const int b = tid / TPB, c = tid - b * TPB;
+      float v = -INFINITY;
+      int32_t ix = 0x7fffffff;
+      for (int ul = c; ul < pnu; ul += TPB) amax_merge(v, ix, (float)(red[ul * NB + b] * rs[b]), pu0 + ul);
+#pragma unroll
+      for (int o = TPB / 2; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(v, o, 64);
+        const int32_t i2 = __shfl_xor(ix, o, 64);
+        amax_merge(v, ix, v2, i2);
+      }
+      if (c == 0) {
+        float rv = m->lmv[b];
+        int32_t ri = m->lmi[b];
+        amax_merge(rv, ri, v, ix);
+        m->lmv[b] = rv;
+        m->lmi[b] = ri;
       }
     }
   }
   if (op == OP_LM) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      wave_amax(bv[b], bi[b]);
-      if (lane == 0) {
-        m->wval[w][b] = bv[b];
-        m->widx[w][b] = bi[b];
-      }
-    }
     __syncthreads();
     if (tid < NB) {
-      float v = m->wval[0][tid];
-      int32_t ix = m->widx[0][tid];
-      for (int ww = 1; ww < NW; ++ww) amax_merge(v, ix, m->wval[ww][tid], m->widx[ww][tid]);
       LmPart* lp = P.lm_part + (size_t)tid * P.n_lm + t.tile;
-      stc(&lp->val, v);
-      stc_i(&lp->idx, ix);
+      stc(&lp->val, m->lmv[tid]);
+      stc_i(&lp->idx, m->lmi[tid]);
     }
   }
   signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
   return true;
+}
+
+// The weight buffers are shaped by the tile count of the task's first pass.
+template <int NB>
+__device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
+                                               uint64_t* tr) {
+  const int op = (int)t.op, l = (int)t.layer;
+  const LayerW LW = ldg(P.layers + (op == OP_LM ? 0 : l));
+  const uint16_t* W0;
+  const uint16_t* W1 = nullptr;
+  const uint16_t* gamma = nullptr;
+  int K, RU = 1;
+  switch (op) {
+    case OP_QKV: W0 = LW.wqkv; K = P.H; gamma = LW.attn_norm; break;
+    case OP_WO: W0 = LW.wo; K = P.QD; break;
+    case OP_GU: W0 = LW.wg; W1 = LW.wu; K = P.H; RU = 2; gamma = LW.ffn_norm; break;
+    case OP_DOWN: W0 = LW.wd; K = P.F; break;
+    default: W0 = P.lm_head; K = P.H; gamma = P.final_norm; break;
+  }
+  const int T = (((int)t.a1 - (int)t.a0) * RU + 15) >> 4;
+  static_assert(MT == 8, "the buffer shapes below cover up to eight tiles per pass");
+  if (T <= 1) return gemv_mfma<NB, 1>(P, t, s, mega, lds, tr, op, W0, W1, gamma, K, RU);
+  if (T <= 2) return gemv_mfma<NB, 2>(P, t, s, mega, lds, tr, op, W0, W1, gamma, K, RU);
+  if (T <= 4) return gemv_mfma<NB, 4>(P, t, s, mega, lds, tr, op, W0, W1, gamma, K, RU);
+  return gemv_mfma<NB, 8>(P, t, s, mega, lds, tr, op, W0, W1, gamma, K, RU);
 }
 
 // ---------------------------------------------------------------------------
