@@ -1272,70 +1272,103 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     return true;
   }
   // ---- merge every split of (b, g) in ascending order, polling the others' partials.
-  // Pass 1 gathers every (m_s, l_s) into LDS in one round trip; pass 2 issues
-  // the accumulator loads of up to 8 splits at once.
+  // The (m_s, l_s) words and this thread's first MCH accumulator words are
+  // requested together, so the merge costs one round trip; the weights
+  // e^{m_s - M} are formed once per (head, split), in parallel.
   const size_t b0 = (size_t)bg * P.NS;
   uint32_t polls = 0;
   bool ok_all = true;
   __syncthreads();                    // every thread is done reading the P.V scratch and m->ml
   double* mls = accw;                 // [G][n_act][2], reuses the P.V scratch
   double* scl = accw + 2 * G * n_act; // [G][n_act] weights e^{m_s - M}
-  for (int i = tid; i < G * n_act; i += NT) {
+  constexpr int MCH = 8;              // accumulator splits in flight per thread
+  constexpr uint32_t SSTR = G * D * 16;  // bytes between consecutive splits of one accumulator element
+  const int npair = G * n_act;
+  const bool mine = tid < G * D;      // this thread merges element tid of the group's G heads
+  const int h_me = tid / D;
+  // byte offsets: accumulator element tid of split s2 at tid * 16 + s2 * SSTR (lo word, then hi);
+  // (m, l) of (head h, split s2) at (s2 * G + h) * 32 (m lo, m hi, l lo, l hi)
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(P.part_acc + b0 * G * D * 2), (short)0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(P.part_ml + b0 * G * 4), (short)0, 0x7fffffff, 0x00020000);
+  const uint32_t va = (uint32_t)tid * 16u;
+  auto pair_off = [&](int i) -> uint32_t {
     const int h = i / n_act, s2 = i - h * n_act;
-    const TV* pm = P.part_ml + (((b0 + s2) * G + h) * 2) * 2;  // m: pm[0..1], l: pm[2..3]
-    uint64_t w0 = ld_tv(pm), w1 = ld_tv(pm + 1), w2 = ld_tv(pm + 2), w3 = ld_tv(pm + 3);
-    while (ok_all && !(tv_ok(w0, tag) && tv_ok(w1, tag) && tv_ok(w2, tag) && tv_ok(w3, tag))) {
+    return (uint32_t)(s2 * G + h) * 32u;
+  };
+  uint64_t pw[4] = {0, 0, 0, 0};
+  if (tid < npair) {
+    const uint32_t vo = pair_off(tid);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pw[k] = ld_tv_b(rm, vo, 8u * k);
+  }
+  uint64_t wl[MCH], wh[MCH];
+#pragma unroll
+  for (int k = 0; k < MCH; ++k)
+    if (mine && k < n_act) {
+      wl[k] = ld_tv_b(ra, va, k * SSTR);
+      wh[k] = ld_tv_b(ra, va + 8u, k * SSTR);
+    }
+  for (int i = tid; i < npair; i += NT) {
+    const uint32_t vo = pair_off(i);
+    if (i != tid)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pw[k] = ld_tv_b(rm, vo, 8u * k);
+    while (ok_all && !(tv_ok(pw[0], tag) && tv_ok(pw[1], tag) && tv_ok(pw[2], tag) && tv_ok(pw[3], tag))) {
       if (++polls > P.watchdog) ok_all = false;
       __builtin_amdgcn_s_sleep(1);
-      w0 = ld_tv(pm);
-      w1 = ld_tv(pm + 1);
-      w2 = ld_tv(pm + 2);
-      w3 = ld_tv(pm + 3);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pw[k] = ld_tv_b(rm, vo, 8u * k);
     }
-    mls[(h * n_act + s2) * 2] = tvd_val(w0, w1);
-    mls[(h * n_act + s2) * 2 + 1] = tvd_val(w2, w3);
+    mls[i * 2] = tvd_val(pw[0], pw[1]);
+    mls[i * 2 + 1] = tvd_val(pw[2], pw[3]);
   }
+  // checks the tags of a burst of accumulator words, re-reading those not yet written
+  auto settle = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < MCH; ++k)
+      if (mine && c0 + k < n_act)
+        while (ok_all && !(tv_ok(wl[k], tag) && tv_ok(wh[k], tag))) {
+          if (++polls > P.watchdog) ok_all = false;
+          __builtin_amdgcn_s_sleep(1);
+          wl[k] = ld_tv_b(ra, va, (c0 + k) * SSTR);
+          wh[k] = ld_tv_b(ra, va + 8u, (c0 + k) * SSTR);
+        }
+  };
+  settle(0);
+  double av[MCH];  // the first MCH accumulators
+#pragma unroll
+  for (int k = 0; k < MCH; ++k) av[k] = tvd_val(wl[k], wh[k]);
   __syncthreads();
-  if (tid < G) {
-    const int h = tid;
+  for (int i = tid; i < npair; i += NT) {
+    const int h = i / n_act;
     double M = -INFINITY;
     for (int s2 = 0; s2 < n_act; ++s2) M = fmax(M, mls[(h * n_act + s2) * 2]);
-    double den = 0.0;
-    for (int s2 = 0; s2 < n_act; ++s2) {
-      const double e = exp(mls[(h * n_act + s2) * 2] - M);
-      scl[h * n_act + s2] = e;
-      den += e * mls[(h * n_act + s2) * 2 + 1];
-    }
-    m->ml[h][1] = den;
+    scl[i] = exp(mls[i * 2] - M);
   }
   __syncthreads();
-  for (int i = tid; i < G * D && ok_all; i += NT) {
-    const int h = i / D, d = i - h * D;
+  if (mine) {
+    const double* sw = scl + h_me * n_act;
+    double den = 0.0;
+    for (int s2 = 0; s2 < n_act; ++s2) den += sw[s2] * mls[(h_me * n_act + s2) * 2 + 1];
     double num = 0.0;
-    for (int c0 = 0; c0 < n_act && ok_all; c0 += 8) {
-      uint64_t wl[8], wh[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (c0 + k < n_act) {
-          const TV* pa = P.part_acc + ((((b0 + c0 + k) * G + h) * D + d) * 2);
-          wl[k] = ld_tv(pa);
-          wh[k] = ld_tv(pa + 1);
-        }
+    for (int k = 0; k < MCH; ++k)
+      if (k < n_act) num += sw[k] * av[k];
+    for (int c0 = MCH; c0 < n_act && ok_all; c0 += MCH) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < MCH; ++k)
         if (c0 + k < n_act) {
-          const TV* pa = P.part_acc + ((((b0 + c0 + k) * G + h) * D + d) * 2);
-          while (ok_all && !(tv_ok(wl[k], tag) && tv_ok(wh[k], tag))) {
-            if (++polls > P.watchdog) ok_all = false;
-            __builtin_amdgcn_s_sleep(1);
-            wl[k] = ld_tv(pa);
-            wh[k] = ld_tv(pa + 1);
-          }
-          num += scl[h * n_act + c0 + k] * tvd_val(wl[k], wh[k]);
+          wl[k] = ld_tv_b(ra, va, (c0 + k) * SSTR);
+          wh[k] = ld_tv_b(ra, va + 8u, (c0 + k) * SSTR);
         }
-      }
+      settle(c0);
+#pragma unroll
+      for (int k = 0; k < MCH; ++k)
+        if (c0 + k < n_act) num += sw[c0 + k] * tvd_val(wl[k], wh[k]);
     }
-    if (ok_all) stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + i, (float)(num / m->ml[h][1]));
+    if (ok_all) stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + tid, (float)(num / den));
   }
   // Append this position's K/V to the cache.  Only later steps read it, after
   // the signal below; issued here, the stores complete alongside those of o
