@@ -126,10 +126,9 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
     return MK_ERR_UNSUPPORTED;
   }
   // attention: raw q/k/v, rotated q, current k/v, scores, the split's values (bf16), then
-  // the P.V partial sums (when fewer than 512 outputs) or the merge's (m, l) and weights
-  const int rp = 512 / (G * D);
+  // the P.V partial sums (4 per thread) or the merge's (m, l) and weights
   const int64_t att_bytes = (int64_t)(G + 2) * D * 4 + (int64_t)G * D * 8 + 2 * D * 2 + (int64_t)G * ((S + 1) & ~1) * 8 +
-                            (int64_t)S * D * 2 + (int64_t)std::max(rp > 1 ? rp * G * D : 0, 3 * G * g.n_splits) * 8;
+                            (int64_t)S * D * 2 + (int64_t)std::max(4 * 512, 3 * G * g.n_splits) * 8;
   auto maxrows = [](int R, int T) { return (R + T - 1) / T; };
   const int worst = std::max({maxrows(cfg.hidden, g.n_wo), maxrows(cfg.ffn, g.n_gu) * 2, maxrows(cfg.hidden, g.n_down),
                               maxrows(cfg.vocab, g.n_lm), (G + 2) * D / g.qkv_tiles_per_group + 1});

@@ -1228,37 +1228,43 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
   }
   __syncthreads();
-  // ---- unnormalised P.V: thread (h, d) of the group's G heads sums e^{t_j - m} v_j[d]
-  // over this split's positions in ascending order (RP interleaved partial sums,
-  // added in order, when G * D < NT)
-  constexpr int GD = G * D, RP = NT / GD;
+  // ---- unnormalised P.V: thread (q, r) sums e^{t_j - m} v_j[d] for the four outputs
+  // d = 4q..4q+3 of the group's G heads (one 8-byte read of the split's values per position)
+  // over positions j = r, r + RPV, ... in ascending order; the RPV partial sums of an output
+  // are then added in order of r.
+  constexpr int GD = G * D, NQ = GD / 4, RPV = NT / NQ;
+  static_assert(NQ * RPV == NT, "P.V thread layout");
   double pv = 0.0;
   {
-    const int e = tid % GD, r = tid / GD;
-    const int h = e / D, d = e - h * D;
+    const int q = tid % NQ, r = tid / NQ;
+    const int h = (4 * q) / D, d0 = 4 * q - h * D;
     const double* ph = sc + h * S;
-    double a = 0.0;
-    for (int j8 = r; j8 < n; j8 += 8 * RP) {  // 8 positions' LDS reads in flight, then the sums in order
-      double pp[8], vv[8];
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    for (int j4 = r; j4 < n; j4 += 4 * RPV) {  // 4 positions' LDS reads in flight
+      double pp[4];
+      uint2 vv[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int jr = min(j8 + u * RP, n - 1);
+      for (int u = 0; u < 4; ++u) {
+        const int jr = min(j4 + u * RPV, n - 1);
         pp[u] = ph[jr];
-        vv[u] = (double)bf1(vsm[jr * D + d]);
+        vv[u] = *(const uint2*)(vsm + jr * D + d0);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j8 + u * RP < n) a = fma(pp[u], vv[u], a);
+      for (int u = 0; u < 4; ++u)
+        if (j4 + u * RPV < n) {
+          a0 = fma(pp[u], (double)bf_lo(vv[u].x), a0);
+          a1 = fma(pp[u], (double)bf_hi(vv[u].x), a1);
+          a2 = fma(pp[u], (double)bf_lo(vv[u].y), a2);
+          a3 = fma(pp[u], (double)bf_hi(vv[u].y), a3);
+        }
     }
-    if constexpr (RP > 1) accw[r * GD + e] = a;
-    else pv = a;
+    *(v2d*)(accw + r * GD + 4 * q) = v2d{a0, a1};
+    *(v2d*)(accw + r * GD + 4 * q + 2) = v2d{a2, a3};
   }
-  if constexpr (RP > 1) {
-    __syncthreads();
-    if (tid < GD)
+  __syncthreads();
+  if (tid < GD)
 #pragma unroll
-      for (int r = 0; r < RP; ++r) pv += accw[r * GD + tid];
-  }
+    for (int r = 0; r < RPV; ++r) pv += accw[r * GD + tid];
   // ---- this split's partial, tagged with the step
   const size_t pbase = ((size_t)bg * P.NS + sp) * G;
   if (tid < GD) st_tvd(P.part_acc + (pbase * D + tid) * 2, pv, tag);
