@@ -1347,17 +1347,26 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
 #pragma unroll
   for (int k = 0; k < MCH; ++k) av[k] = tvd_val(wl[k], wh[k]);
   __syncthreads();
-  for (int i = tid; i < npair; i += NT) {
-    const int h = i / n_act;
+  // per head h, wave h (lanes over splits): M = max_s m_s, the weights e^{m_s - M}, and
+  // den = sum_s e^{m_s - M} l_s (a fixed tree, the same on every lane)
+  if (w < G) {
+    const int h = w;
     double M = -INFINITY;
-    for (int s2 = 0; s2 < n_act; ++s2) M = fmax(M, mls[(h * n_act + s2) * 2]);
-    scl[i] = exp(mls[i * 2] - M);
+    for (int s2 = lane; s2 < n_act; s2 += 64) M = fmax(M, mls[(h * n_act + s2) * 2]);
+    M = wave_max_d(M);
+    double dsum = 0.0;
+    for (int s2 = lane; s2 < n_act; s2 += 64) {
+      const double e = exp(mls[(h * n_act + s2) * 2] - M);
+      scl[h * n_act + s2] = e;
+      dsum += e * mls[(h * n_act + s2) * 2 + 1];
+    }
+    dsum = wave_sum_d(dsum);
+    if (lane == 0) m->ml[h][1] = dsum;
   }
   __syncthreads();
   if (mine) {
     const double* sw = scl + h_me * n_act;
-    double den = 0.0;
-    for (int s2 = 0; s2 < n_act; ++s2) den += sw[s2] * mls[(h_me * n_act + s2) * 2 + 1];
+    const double den = m->ml[h_me][1];
     double num = 0.0;
 #pragma unroll
     for (int k = 0; k < MCH; ++k)
