@@ -91,8 +91,10 @@ typedef struct mk_tensor {
 /* Validate cfg, build the task graph (host only) and allocate every device
  * buffer: packed weights, KV cache [L][B][Hkv][max_seq][D] bf16 (K and V),
  * activations, event flags.  *out receives the context.  With cfg.split == 0
- * the attention split is S = min(20480 / head_dim, max(32, ceil(max_seq /
- * max(1, workers / (batch * n_kv_heads))))) positions.  Batch 8 and 16 run the
+ * the attention split is S = min(Smax, max(32, ceil(max_seq / max(1, workers /
+ * (batch * n_kv_heads))))) positions, Smax = 20480 / head_dim (32768 /
+ * head_dim with one query head per KV head).  An explicit split above Smax is
+ * UNSUPPORTED.  Batch 8 and 16 run the
  * projections on the matrix cores and need hidden, ffn and n_q_heads *
  * head_dim to be multiples of 512.  Errors: INVALID_ARG, UNSUPPORTED (shape
  * cannot be tiled), OOM, HIP. */

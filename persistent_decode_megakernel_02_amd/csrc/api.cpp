@@ -121,8 +121,8 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
   const int D = cfg.head_dim, G = cfg.n_q_heads / cfg.n_kv_heads, B = cfg.batch;
   const int S = g.split;
   const int lpp = D / 8, ppb = 512 / lpp;
-  if (S > 5 * ppb) {
-    *why = "split too large for head_dim (at most 20480 / head_dim)";
+  if (S > (G == 1 ? 8 : 5) * ppb) {
+    *why = "split too large for head_dim (at most 20480 / head_dim, 32768 / head_dim with one query head per KV head)";
     return MK_ERR_UNSUPPORTED;
   }
   // attention: raw q/k/v, rotated q, current k/v, scores, the split's values (bf16), then

@@ -44,15 +44,16 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   if (c.hidden % 8 || c.ffn % 8) return "hidden and ffn must be multiples of 8";
   // Default split: enough splits that the (sequence, KV head, split) tasks of a
   // full cache fill the workers once, each split between 32 positions and the
-  // per-task register budget (5 * 4096 / D positions).  Attention tasks are
+  // per-task register budget (5 * 4096 / D positions, 8 * 4096 / D with one query
+  // head per KV head).  Attention tasks are
   // latency-bound at short contexts, so more, shorter splits finish sooner.
-  const int smax = 5 * 4096 / D;
+  const int smax = (G == 1 ? 8 : 5) * 4096 / D;
   int S = c.split;
   if (S <= 0) {
     const int ns_target = std::max(1, n_workers / std::max(1, c.batch * Hkv));
     S = std::min(smax, std::max(kDefaultSplit, (c.max_seq + ns_target - 1) / ns_target));
   }
-  if (S > smax) return "split must be <= 5 * 4096 / head_dim";
+  if (S > smax) return "split must be <= 5 * 4096 / head_dim (8 * 4096 / head_dim with one query head per KV head)";
   g.n_workers = n_workers;
   g.split = S;
   g.n_splits = (c.max_seq + S - 1) / S;

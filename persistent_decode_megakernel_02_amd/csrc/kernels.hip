@@ -30,7 +30,8 @@ constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
 constexpr int DEPTH = 2;   // pipeline groups in flight per wave (8 KB per wave): a wave's loads complete in
                           // order, so a deeper queue delays the activation and flag loads behind it
 constexpr int MISC_BYTES = 4096;
-constexpr int ATT_MAXL = 5;  // most K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8))
+constexpr int ATT_MAXL = 5;   // most K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8)) ...
+constexpr int ATT_MAXL1 = 8;  // ... or 8 with one query head per KV head (split <= 8 * 512 / (D / 8))
 
 // Pointers kept inside the parameter block are generic; casting them to the
 // global address space lets the compiler emit global (not flat) memory
@@ -1412,6 +1413,8 @@ __device__ __forceinline__ bool attn_nl(const KParams& P, const TaskRec& t, int 
   constexpr int PPB = NT / LPP;
   if (P.S <= PPB) return task_attn<G, LPP, 1>(P, t, s, mega, lds, tr);
   if (P.S <= 2 * PPB) return task_attn<G, LPP, 2>(P, t, s, mega, lds, tr);
+  if constexpr (G == 1)  // longer splits only where one head's scores are in registers
+    if (P.S > ATT_MAXL * PPB) return task_attn<G, LPP, ATT_MAXL1>(P, t, s, mega, lds, tr);
   return task_attn<G, LPP, ATT_MAXL>(P, t, s, mega, lds, tr);
 }
 

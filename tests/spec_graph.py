@@ -49,9 +49,9 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
     G = Hq // Hkv
     if split > 0:
         S = split
-    else:  # splits of a full cache fill the workers once; 32 <= S <= 5 * 4096 / D
+    else:  # splits of a full cache fill the workers once; 32 <= S <= 5 * 4096 / D (8 * 4096 / D when G = 1)
         ns_target = max(1, workers // max(1, B * Hkv))
-        S = min(5 * 4096 // D, max(32, -(-max_seq // ns_target)))
+        S = min((8 if G == 1 else 5) * 4096 // D, max(32, -(-max_seq // ns_target)))
     NS = -(-max_seq // S)
     RG = (G + 2) * D
     TG = min(max(1, workers // Hkv), RG)
