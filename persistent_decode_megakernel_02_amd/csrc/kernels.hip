@@ -416,7 +416,11 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     return base + (size_t)(u0 + w + NW * ui) * K;
   };
 
-  // pipeline state for one slice
+  // pipeline state for one slice.  With four or more sequences the activations
+  // read from LDS for a chunk serve RPG rows (a group holds CG / RPG chunks of each
+  // of RPG rows): at one row per read the reads would outrun LDS bandwidth.
+  constexpr int RPG = NB >= 4 ? 2 : 1, CGE = CG / RPG;
+  const int my_groups = (my_rows + RPG - 1) / RPG;  // row groups (a last odd row is paired with itself)
   uint4 buf[DEPTH][CG];
   int ir = 0, ig = 0, cr = 0, cgi = 0;
   int k0 = 0, nch8 = 0, GPR = 1;
@@ -425,18 +429,21 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     const int ks = min(kc, K - k0);
     nch8 = ks / 8;
     const int nch = (nch8 + 63) / 64;
-    GPR = (nch + CG - 1) / CG;
+    GPR = (nch + CGE - 1) / CGE;
     ir = ig = cr = cgi = 0;
   };
   // Loads are never predicated: lanes past the row end re-read the row's last
   // chunk (a clamped, in-bounds address) and are zeroed when consumed, so the
   // steady-state loop is branch-free and its waits count outstanding loads.
   auto issue_nocheck = [&](uint4 (&b)[CG]) {
-    const uint16_t* p = rowptr(ir) + k0;
 #pragma unroll
-    for (int c = 0; c < CG; ++c) {
-      const int j = min((ig * CG + c) * 64 + lane, nch8 - 1);
-      b[c] = ldw(p + (size_t)j * 8);
+    for (int rr = 0; rr < RPG; ++rr) {
+      const uint16_t* p = rowptr(RPG == 1 ? ir : min(ir * RPG + rr, my_rows - 1)) + k0;
+#pragma unroll
+      for (int c = 0; c < CGE; ++c) {
+        const int j = min((ig * CGE + c) * 64 + lane, nch8 - 1);
+        b[rr * CGE + c] = ldw(p + (size_t)j * 8);
+      }
     }
     if (++ig == GPR) {
       ig = 0;
@@ -444,25 +451,31 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     }
   };
   auto issue = [&](uint4 (&b)[CG]) {
-    if (ir < my_rows) issue_nocheck(b);
+    if (ir < my_groups) issue_nocheck(b);
   };
 
-  double acc[NB];
+  double acc[RPG][NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.0;
+  for (int rr = 0; rr < RPG; ++rr)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[rr][b] = 0.0;
   int sl_cur = 0;
   auto consume = [&](const uint4 (&bw)[CG]) {
 #pragma unroll
-    for (int c = 0; c < CG; ++c) {
-      const int jr = (cgi * CG + c) * 64 + lane;
+    for (int c = 0; c < CGE; ++c) {
+      const int jr = (cgi * CGE + c) * 64 + lane;
       const bool ok = jr < nch8;
       const int j = ok ? jr : nch8 - 1;
-      const uint32_t wv[4] = {ok ? bw[c].x : 0u, ok ? bw[c].y : 0u, ok ? bw[c].z : 0u, ok ? bw[c].w : 0u};
-      double wd[8];
+      double wd[RPG][8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wd[2 * e] = (double)bf_lo(wv[e]);
-        wd[2 * e + 1] = (double)bf_hi(wv[e]);
+      for (int rr = 0; rr < RPG; ++rr) {
+        const uint4 q = bw[rr * CGE + c];
+        const uint32_t wv[4] = {ok ? q.x : 0u, ok ? q.y : 0u, ok ? q.z : 0u, ok ? q.w : 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wd[rr][2 * e] = (double)bf_lo(wv[e]);
+          wd[rr][2 * e + 1] = (double)bf_hi(wv[e]);
+        }
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -472,27 +485,34 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
         const v2d x1 = *(const v2d*)(xb + ps);
         const v2d x2 = *(const v2d*)(xb + 2 * ps);
         const v2d x3 = *(const v2d*)(xb + 3 * ps);
-        double a = acc[b];
-        a = fma(wd[0], x0.x, a);
-        a = fma(wd[1], x0.y, a);
-        a = fma(wd[2], x1.x, a);
-        a = fma(wd[3], x1.y, a);
-        a = fma(wd[4], x2.x, a);
-        a = fma(wd[5], x2.y, a);
-        a = fma(wd[6], x3.x, a);
-        a = fma(wd[7], x3.y, a);
-        acc[b] = a;
+#pragma unroll
+        for (int rr = 0; rr < RPG; ++rr) {
+          double a = acc[rr][b];
+          a = fma(wd[rr][0], x0.x, a);
+          a = fma(wd[rr][1], x0.y, a);
+          a = fma(wd[rr][2], x1.x, a);
+          a = fma(wd[rr][3], x1.y, a);
+          a = fma(wd[rr][4], x2.x, a);
+          a = fma(wd[rr][5], x2.y, a);
+          a = fma(wd[rr][6], x3.x, a);
+          a = fma(wd[rr][7], x3.y, a);
+          acc[rr][b] = a;
+        }
       }
     }
     if (++cgi == GPR) {
       cgi = 0;
-      const int ui = RU == 2 ? (cr >> 1) : cr;
-      const int rl = (w + NW * ui) * RU + (RU == 2 ? (cr & 1) : 0);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const double v = wave_sum_d(acc[b]);
-        if (lane == 0) red[rl * NB + b] = sl_cur == 0 ? v : red[rl * NB + b] + v;
-        acc[b] = 0.0;
+      for (int rr = 0; rr < RPG; ++rr) {
+        const int r = cr * RPG + rr;  // the wave's row
+        const int ui = RU == 2 ? (r >> 1) : r;
+        const int rl = (w + NW * ui) * RU + (RU == 2 ? (r & 1) : 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const double v = wave_sum_d(acc[rr][b]);
+          if (lane == 0 && (RPG == 1 || r < my_rows)) red[rl * NB + b] = sl_cur == 0 ? v : red[rl * NB + b] + v;
+          acc[rr][b] = 0.0;
+        }
       }
       ++cr;
     }
@@ -621,7 +641,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     // exact count to start from, so the loop below waits only for the oldest
     // group instead of draining every load.
     __builtin_amdgcn_s_waitcnt(0);
-    const int total = my_rows * GPR;
+    const int total = my_groups * GPR;
     int g = 0;
     for (; g + 2 * DEPTH <= total; g += DEPTH) {  // steady state: DEPTH groups always in flight
 #pragma unroll
