@@ -287,15 +287,22 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
     const uint32_t* f = P.flags + e.slot0;
     uint32_t polls = 0;
     int ok = 0;
+    // a pass reads the slots in bursts of PW per lane, all in flight together (a slot index past
+    // the fan-in re-reads the last slot), so one pass over up to 64 PW slots costs one round trip
+    constexpr uint32_t PW = 4;
     for (;;) {
       bool mine = true;
       uint32_t seen = target;
-      for (uint32_t i = lane; i < e.fanin; i += 64) {
-        uint32_t v = ldc_u(f + i);
-        if ((int32_t)(v - target) < 0) {
-          mine = false;
-          seen = v;
-        }
+      for (uint32_t i0 = 0; i0 < e.fanin; i0 += 64 * PW) {
+        uint32_t v[PW];
+#pragma unroll
+        for (uint32_t k = 0; k < PW; ++k) v[k] = ldc_u(f + min(i0 + lane + 64 * k, e.fanin - 1));
+#pragma unroll
+        for (uint32_t k = 0; k < PW; ++k)
+          if ((int32_t)(v[k] - target) < 0) {
+            mine = false;
+            seen = v[k];
+          }
       }
       if (__all(mine)) {
         ok = 1;
