@@ -126,9 +126,11 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
     return MK_ERR_UNSUPPORTED;
   }
   // attention: raw q/k/v, rotated q, current k/v, scores, the split's values (bf16), then
-  // the P.V partial sums (4 per thread) or the merge's (m, l) and weights
+  // the P.V partial sums (4 per thread) or the merge's (m, l), weights and slice of accumulators
+  // (at most G D + n_splits items)
+  const int64_t merge_doubles = (int64_t)3 * G * g.n_splits + (int64_t)G * D + g.n_splits;
   const int64_t att_bytes = (int64_t)(G + 2) * D * 4 + (int64_t)G * D * 8 + 2 * D * 2 + (int64_t)G * ((S + 1) & ~1) * 8 +
-                            (int64_t)S * D * 2 + (int64_t)std::max(4 * 512, 3 * G * g.n_splits) * 8;
+                            (int64_t)S * D * 2 + std::max<int64_t>(4 * 512, merge_doubles) * 8;
   auto maxrows = [](int R, int T) { return (R + T - 1) / T; };
   const int worst = std::max({maxrows(cfg.hidden, g.n_wo), maxrows(cfg.ffn, g.n_gu) * 2, maxrows(cfg.hidden, g.n_down),
                               maxrows(cfg.vocab, g.n_lm), (G + 2) * D / g.qkv_tiles_per_group + 1});

@@ -66,6 +66,10 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   g.n_down = std::min(n_workers, c.hidden);
   g.n_lm = std::min(n_workers, c.vocab);
   if ((int64_t)g.n_qkv > n_workers) return "internal: too many QKV tiles";
+  // When every attention task of a layer has a worker of its own, all of a head's splits run
+  // at once and each merges a slice of the outputs, signalling its own slot; otherwise the
+  // split holding the current position merges everything and signals for its (sequence, head).
+  const bool dist = (int64_t)g.n_splits * c.batch * Hkv <= n_workers;
 
   // events: per layer [QKV group 0..Hkv-1, ATT, O, A, X], then LM
   const int per_layer = Hkv + 4;
@@ -78,7 +82,7 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   g.events.resize(ev_lm + 1);
   for (int l = 0; l < c.n_layers; ++l) {
     for (int gg = 0; gg < Hkv; ++gg) g.events[ev_qkv(l, gg)].fanin = TG;
-    g.events[ev_att(l)].fanin = c.batch * Hkv;
+    g.events[ev_att(l)].fanin = dist ? g.n_splits * c.batch * Hkv : c.batch * Hkv;
     g.events[ev_o(l)].fanin = g.n_wo;
     g.events[ev_a(l)].fanin = g.n_gu;
     g.events[ev_x(l)].fanin = g.n_down;
@@ -127,7 +131,7 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
       for (int b = 0; b < c.batch; ++b)
         for (int gg = 0; gg < Hkv; ++gg, ++idx)
           push(OP_ATTN, l, idx, (uint32_t)(b * Hkv + gg), (uint32_t)s, ev_qkv(l, gg), 0, ev_att(l),
-               (uint32_t)(b * Hkv + gg), idx);
+               dist ? idx : (uint32_t)(b * Hkv + gg), idx);
     range_end(f);
     f = range_begin();
     for (int i = 0; i < g.n_wo; ++i)

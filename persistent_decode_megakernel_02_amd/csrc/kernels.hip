@@ -277,14 +277,37 @@ __device__ __forceinline__ double silu_d(double z) { return z / (1.0 + exp(-z));
 // ---------------------------------------------------------------------------
 // events
 // ---------------------------------------------------------------------------
+// Attention merge forms.  dist: a worker for every attention task of the layer, so the splits
+// of a head run together and the attention event has one slot per task, split-major (slot
+// sp B Hkv + b Hkv + g).  Then, past ATT_MCH active splits (more than one burst of accumulator
+// loads for a single merger), every active split merges a slice of its head group's outputs and
+// signals; otherwise the split holding the current position merges them all and alone signals
+// (without dist, in slot b Hkv + g, and a split may wait only on splits listed before it).
+constexpr int ATT_MCH = 8;
+__device__ __forceinline__ bool att_dist(const KParams& P) { return P.NS * P.B * P.Hkv <= P.n_workers; }
+__device__ __forceinline__ int att_active(const KParams& P, int s) { return (P.pos0 + s + 1 + P.S - 1) / P.S; }
+
+// att: ev is a layer's attention event
 __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32_t target, uint32_t task, Misc* m,
-                                           uint64_t* tr = nullptr) {
+                                           uint64_t* tr = nullptr, bool att = false) {
   if (ev == EV_NONE) return true;
   const int tid = ltid();
   if (tid < 64) {
     const int lane = tid;
     const EventRec e = ldg(P.events + ev);
     const uint32_t* f = P.flags + e.slot0;
+    uint32_t fanin = e.fanin;
+    // a dist attention event: only the slots of the step's signalling splits
+    if (att && att_dist(P)) {
+      const int n_act = att_active(P, (int)(target - P.epoch) - 1);
+      const uint32_t bh = (uint32_t)(P.B * P.Hkv);
+      if (n_act > ATT_MCH) {
+        fanin = (uint32_t)n_act * bh;
+      } else {
+        f += (uint32_t)(n_act - 1) * bh;
+        fanin = bh;
+      }
+    }
     uint32_t polls = 0;
     int ok = 0;
     // a pass reads the slots in bursts of PW per lane, all in flight together (a slot index past
@@ -293,10 +316,10 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
     for (;;) {
       bool mine = true;
       uint32_t seen = target;
-      for (uint32_t i0 = 0; i0 < e.fanin; i0 += 64 * PW) {
+      for (uint32_t i0 = 0; i0 < fanin; i0 += 64 * PW) {
         uint32_t v[PW];
 #pragma unroll
-        for (uint32_t k = 0; k < PW; ++k) v[k] = ldc_u(f + min(i0 + lane + 64 * k, e.fanin - 1));
+        for (uint32_t k = 0; k < PW; ++k) v[k] = ldc_u(f + min(i0 + lane + 64 * k, fanin - 1));
 #pragma unroll
         for (uint32_t k = 0; k < PW; ++k)
           if ((int32_t)(v[k] - target) < 0) {
@@ -532,7 +555,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 
   // a wait on the previous step is met by the launch boundary at the first step of a call
   if (mega && !(s == 0 && t.wait_lag) &&
-      !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m, tr))
+      !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m, tr, t.op == OP_WO))
     return false;
 
   // layer-0 Q/K/V reads the embedding of this step's token
@@ -881,7 +904,7 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
   for (int b = 0; b < NBUF; ++b) issue(A[b], b);
 
   if (mega && !(s == 0 && t.wait_lag) &&
-      !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m, tr))
+      !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u - t.wait_lag, t.tile, m, tr, t.op == OP_WO))
     return false;
 
   if (embed_src) {
@@ -1110,11 +1133,13 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   const int Hkv = P.Hkv, S = P.S;
   const int bg = (int)t.a0, b = bg / Hkv, g = bg - b * Hkv, sp = (int)t.a1, l = (int)t.layer;
   const int pos = P.pos0 + s, N = pos + 1;
-  const int n_act = (N + S - 1) / S;
+  const int n_act = att_active(P, s);
+  constexpr int MCH = ATT_MCH;  // single merger: accumulator splits in flight per thread
+  const bool slice = att_dist(P) && n_act > MCH;
   if (sp >= n_act) return true;  // split beyond the current length: nothing to do
   const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   const int j0 = sp * S, j1 = min(j0 + S, N);
-  const bool has_cur = (j1 == N);  // this split holds the current position and merges
+  const bool has_cur = (j1 == N);  // this split holds the current position (and appends it)
   const int jc = has_cur ? pos : j1;  // cached positions [j0, jc)
   const int lp = tid % LPP, po = tid / LPP;
   const size_t head = ((size_t)(l * P.B + b) * Hkv + g) * P.max_seq;
@@ -1301,24 +1326,31 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     st_tvd(P.part_ml + ((pbase + tid) * 2 + 1) * 2, m->ml[tid][1], tag);
   }
   if (tr && tid == 0) tr[2] = wall_clock64();  // partial stored
-  if (!has_cur) {
+  if (!has_cur && !slice) {  // the merger checks this split's partial by its tags
     __syncthreads();
     return true;
   }
-  // ---- merge every split of (b, g) in ascending order, polling the others' partials.
-  // The (m_s, l_s) words and this thread's first MCH accumulator words are
-  // requested together, so the merge costs one round trip; the weights
-  // e^{m_s - M} are formed once per (head, split), in parallel.
+  // ---- merge the splits of (b, g), polling the others' partials:
+  //   slice: this split merges outputs [e0, e0 + ne) of the group's G D, item i of its
+  //   slice being (split i / ne, output e0 + i % ne), at most MI items per thread in flight;
+  //   otherwise: thread tid merges output tid, MCH splits in flight at a time.
+  // The (m_s, l_s) words and the first accumulator words are requested together, so the
+  // merge costs one round trip; the weights e^{m_s - M} are formed once per (head, split).
+  // Either way output e is sum_s e^{m_s - M} acc_s[e] / den, summed in ascending s.
   const size_t b0 = (size_t)bg * P.NS;
   uint32_t polls = 0;
+  const uint32_t wdog = P.watchdog;
   bool ok_all = true;
   __syncthreads();                    // every thread is done reading the P.V scratch and m->ml
   double* mls = accw;                 // [G][n_act][2], reuses the P.V scratch
   double* scl = accw + 2 * G * n_act; // [G][n_act] weights e^{m_s - M}
-  constexpr int MCH = 8;              // accumulator splits in flight per thread
+  double* accs = scl + G * n_act;     // slice: [n_act][ne] the slice's accumulators
+  constexpr int MI = 2;               // slice: items in flight per thread
   constexpr uint32_t SSTR = G * D * 16;  // bytes between consecutive splits of one accumulator element
   const int npair = G * n_act;
-  const bool mine = tid < G * D;      // this thread merges element tid of the group's G heads
+  const int e0 = slice ? sp * GD / n_act : 0, ne = slice ? (sp + 1) * GD / n_act - e0 : GD;
+  const int tot = ne * n_act;
+  const bool mine = !slice && tid < G * D;  // this thread merges element tid of the group's G heads
   const int h_me = tid / D;
   // byte offsets: accumulator element tid of split s2 at tid * 16 + s2 * SSTR (lo word, then hi);
   // (m, l) of (head h, split s2) at (s2 * G + h) * 32 (m lo, m hi, l lo, l hi)
@@ -1338,19 +1370,34 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     for (int k = 0; k < 4; ++k) pw[k] = ld_tv_b(rm, vo, 8u * k);
   }
   uint64_t wl[MCH], wh[MCH];
+  // slice: byte offset of item i
+  auto item_off = [&](int i) -> uint32_t {
+    const int s2 = i / ne, el = i - s2 * ne;
+    return (uint32_t)s2 * SSTR + (uint32_t)(e0 + el) * 16u;
+  };
+  if (slice) {
 #pragma unroll
-  for (int k = 0; k < MCH; ++k)
-    if (mine && k < n_act) {
-      wl[k] = ld_tv_b(ra, va, k * SSTR);
-      wh[k] = ld_tv_b(ra, va + 8u, k * SSTR);
-    }
+    for (int k = 0; k < MI; ++k)
+      if (tid + k * NT < tot) {
+        const uint32_t vo = item_off(tid + k * NT);
+        wl[k] = ld_tv_b(ra, vo, 0u);
+        wh[k] = ld_tv_b(ra, vo + 8u, 0u);
+      }
+  } else {
+#pragma unroll
+    for (int k = 0; k < MCH; ++k)
+      if (mine && k < n_act) {
+        wl[k] = ld_tv_b(ra, va, k * SSTR);
+        wh[k] = ld_tv_b(ra, va + 8u, k * SSTR);
+      }
+  }
   for (int i = tid; i < npair; i += NT) {
     const uint32_t vo = pair_off(i);
     if (i != tid)
 #pragma unroll
       for (int k = 0; k < 4; ++k) pw[k] = ld_tv_b(rm, vo, 8u * k);
     while (ok_all && !(tv_ok(pw[0], tag) && tv_ok(pw[1], tag) && tv_ok(pw[2], tag) && tv_ok(pw[3], tag))) {
-      if (++polls > P.watchdog) ok_all = false;
+      if (++polls > wdog) ok_all = false;
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) pw[k] = ld_tv_b(rm, vo, 8u * k);
@@ -1364,16 +1411,44 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     for (int k = 0; k < MCH; ++k)
       if (mine && c0 + k < n_act)
         while (ok_all && !(tv_ok(wl[k], tag) && tv_ok(wh[k], tag))) {
-          if (++polls > P.watchdog) ok_all = false;
+          if (++polls > wdog) ok_all = false;
           __builtin_amdgcn_s_sleep(1);
           wl[k] = ld_tv_b(ra, va, (c0 + k) * SSTR);
           wh[k] = ld_tv_b(ra, va + 8u, (c0 + k) * SSTR);
         }
   };
-  settle(0);
   double av[MCH];  // the first MCH accumulators
+  if (slice) {
+    // the slice's items in bursts of MI per thread, each checked and parked in LDS
+    for (int c0 = 0; c0 < tot; c0 += MI * NT) {
+      if (c0 > 0)
 #pragma unroll
-  for (int k = 0; k < MCH; ++k) av[k] = tvd_val(wl[k], wh[k]);
+        for (int k = 0; k < MI; ++k)
+          if (c0 + tid + k * NT < tot) {
+            const uint32_t vo = item_off(c0 + tid + k * NT);
+            wl[k] = ld_tv_b(ra, vo, 0u);
+            wh[k] = ld_tv_b(ra, vo + 8u, 0u);
+          }
+#pragma unroll
+      for (int k = 0; k < MI; ++k) {
+        const int i = c0 + tid + k * NT;
+        if (i < tot) {
+          const uint32_t vo = item_off(i);
+          while (ok_all && !(tv_ok(wl[k], tag) && tv_ok(wh[k], tag))) {
+            if (++polls > wdog) ok_all = false;
+            __builtin_amdgcn_s_sleep(1);
+            wl[k] = ld_tv_b(ra, vo, 0u);
+            wh[k] = ld_tv_b(ra, vo + 8u, 0u);
+          }
+          accs[i] = tvd_val(wl[k], wh[k]);
+        }
+      }
+    }
+  } else {
+    settle(0);
+#pragma unroll
+    for (int k = 0; k < MCH; ++k) av[k] = tvd_val(wl[k], wh[k]);
+  }
   __syncthreads();
   // per head h, wave h (lanes over splits): M = max_s m_s, the weights e^{m_s - M}, and
   // den = sum_s e^{m_s - M} l_s (a fixed tree, the same on every lane)
@@ -1392,6 +1467,14 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     if (lane == 0) m->ml[h][1] = dsum;
   }
   __syncthreads();
+  if (slice && tid < ne) {
+    const int e = e0 + tid;
+    const double* sw = scl + (e / D) * n_act;
+    double num = 0.0;
+#pragma unroll 8
+    for (int s2 = 0; s2 < n_act; ++s2) num += sw[s2] * accs[s2 * ne + tid];
+    if (ok_all) stc(P.o + (size_t)b * P.QD + (size_t)(g * G) * D + e, (float)(num / m->ml[e / D][1]));
+  }
   if (mine) {
     const double* sw = scl + h_me * n_act;
     const double den = m->ml[h_me][1];
@@ -1417,7 +1500,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   // the signal below; issued here, the stores complete alongside those of o
   // instead of stalling the scores (a store's registers are reusable only
   // once it has completed).
-  if (tid < LPP) {
+  if (has_cur && tid < LPP) {
     stg((uint4*)(Kh + (size_t)pos * D + tid * 8), *(const uint4*)(kcur + tid * 8));
     stg((uint4*)(Vh + (size_t)pos * D + tid * 8), *(const uint4*)(vcur + tid * 8));
   }

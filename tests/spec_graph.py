@@ -14,12 +14,16 @@ Rules (one decode step; the persistent kernel repeats it every step):
     covering positions [s S, (s + 1) S), S from the default rule unless given, NS = ceil(max_seq / S).
   * Task number k of an operator runs on worker k mod workers.
   * Events per layer: Hkv QKV-group events, ATT, O, A, X; then one LM event.
-    Fan-ins: TG, B*Hkv, T_wo, T_gu, T_down, T_lm.  Slots are numbered
-    consecutively in event order.
+    Fan-ins: TG, F_att, T_wo, T_gu, T_down, T_lm.  Slots are numbered
+    consecutively in event order.  The attention tasks are "distributed" when
+    NS*B*Hkv <= workers (each on a worker of its own); then F_att = NS*B*Hkv,
+    else F_att = B*Hkv.
   * Waits: QKV(0) waits LM of the previous step (lag 1); QKV(l>0) waits X(l-1);
     ATTN waits its group's QKV event; WO waits ATT; GU waits O; DOWN waits A;
     LM waits X(L-1).  Signals: QKV tile i of group g -> QKV(l, g) slot i;
-    ATTN (b, g, s) -> ATT slot b*Hkv+g (only the merging split notifies);
+    ATTN task k = (s, b, g) -> ATT slot k when distributed (every split merges a slice
+    and notifies; splits beyond the current length notify at once), else slot b*Hkv+g
+    (only the split holding the current position merges and notifies);
     GEMV tile i -> its event, slot i.
 """
 from __future__ import annotations
@@ -57,6 +61,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
     TG = min(max(1, workers // Hkv), RG)
     n_wo, n_gu, n_down, n_lm = min(workers, H), min(workers, F), min(workers, H), min(workers, V)
     per_layer = Hkv + 4
+    dist = NS * B * Hkv <= workers
 
     def ev(layer, k):
         return layer * per_layer + k
@@ -64,7 +69,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
     ev_lm = L * per_layer
     fanin = []
     for _ in range(L):
-        fanin += [TG] * Hkv + [B * Hkv, n_wo, n_gu, n_down]
+        fanin += [TG] * Hkv + [NS * B * Hkv if dist else B * Hkv, n_wo, n_gu, n_down]
     fanin.append(n_lm)
 
     def lo(i, R, T):
@@ -83,7 +88,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
             for b in range(B):
                 for g in range(Hkv):
                     tasks.append(Task(OP_ATTN, layer, k, b * Hkv + g, s, ev(layer, g), 0, ev(layer, Hkv),
-                                      b * Hkv + g, k % workers))
+                                      k if dist else b * Hkv + g, k % workers))
                     k += 1
         for op, R, T, wait, sig in ((OP_WO, H, n_wo, Hkv, Hkv + 1), (OP_GU, F, n_gu, Hkv + 1, Hkv + 2),
                                     (OP_DOWN, H, n_down, Hkv + 2, Hkv + 3)):

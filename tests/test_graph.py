@@ -95,18 +95,40 @@ def test_graph_invariants(shape, B, max_seq, workers, split):
 
 
 def simulate(g, shape, B, steps, start_pos, seed, drop=None):
-    """Run every worker's list under random interleaving with the event rules; returns True if all
-    steps complete, False on deadlock.  Attention splits beyond the current length are skipped and
-    only the split holding the current position notifies (after every active split of its head)."""
+    """Run every worker's list under random interleaving with the event rules, one flag per slot
+    holding the number of steps its producer signalled; returns True if all steps complete, False
+    on deadlock.  Attention splits beyond the current length do nothing.  A merging split stores
+    its partial, stays on its worker until every active split of its head has stored, then
+    signals; a split that does not merge stores and moves on without signalling.  The split
+    holding the current position merges; with the attention tasks distributed (one slot per task)
+    and more than 8 active splits, every active split merges a slice, and a wait on the attention
+    event reads only the slots of the step's merging splits."""
     rnd = random.Random(seed)
     tasks, events = g["tasks"], g["events"]
-    workers = g["workers"]
+    workers, S, Hkv = g["workers"], g["split"], shape.n_kv_heads
+    per_layer = Hkv + 4
+    dist = g["ns"] * B * Hkv <= workers
     lists = [[t for t in tasks if t[11] == w] for w in range(workers)]
-    count = [0] * len(events)      # monotone counters
-    done_split = {}                # (step, layer, bg) -> active splits finished
+    flags = {}                     # (event, slot) -> steps signalled
+    done_split = {}                # (step, layer, bg) -> active splits that stored their partial
+    stored = [False] * workers     # a merging split has stored and waits for its head's others
     pos = [0] * workers            # (step * len(list) + index)
-    S = g["split"]
     total = [steps * len(lst) for lst in lists]
+
+    def n_active(step):
+        return -(-(start_pos + step + 1) // S)
+
+    def slots(ev, step):
+        fanin = events[ev][1]
+        if dist and ev < shape.n_layers * per_layer and ev % per_layer == Hkv:
+            n_act = n_active(step)
+            return range(n_act * B * Hkv) if n_act > 8 else range((n_act - 1) * B * Hkv, n_act * B * Hkv)
+        return range(fanin)
+
+    def merges(t, step):
+        n_act = n_active(step)
+        return t[5] == n_act - 1 or (dist and n_act > 8)
+
     while True:
         ready = []
         for w in range(workers):
@@ -114,39 +136,53 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None):
                 continue
             step, i = divmod(pos[w], len(lists[w]))
             t = lists[w][i]
-            N = start_pos + step + 1
-            if t[1] == OP_ATTN and t[5] * S >= N:
+            if t[1] == OP_ATTN and t[5] >= n_active(step):
                 ready.append(w)
-                continue
-            need = (step + 1 - t[8]) * events[t[6]][1]
-            if count[t[6]] >= need:
-                ready.append(w)
+            elif stored[w]:
+                if done_split.get((step, t[2], t[4]), 0) == n_active(step):
+                    ready.append(w)
+            else:
+                target = step + 1 - t[8]
+                if target <= 0 or all(flags.get((t[6], sl), 0) >= target for sl in slots(t[6], step - t[8])):
+                    ready.append(w)
         if not ready:
             return all(pos[w] >= total[w] for w in range(workers))
         w = rnd.choice(ready)
         step, i = divmod(pos[w], len(lists[w]))
         t = lists[w][i]
-        pos[w] += 1
-        if drop is not None and t[0] == drop:
-            continue
+        signal = True
         if t[1] == OP_ATTN:
-            N = start_pos + step + 1
-            n_act = -(-N // S)
-            if t[5] >= n_act:
-                continue
-            key = (step, t[2], t[4])
-            done_split[key] = done_split.get(key, 0) + 1
-            if done_split[key] == n_act:
-                count[t[9]] += 1
-            continue
-        count[t[9]] += 1
+            if t[5] >= n_active(step):
+                signal = False
+            elif not stored[w]:
+                key = (step, t[2], t[4])
+                done_split[key] = done_split.get(key, 0) + 1
+                if merges(t, step):
+                    stored[w] = True
+                    continue
+                signal = False
+            else:
+                stored[w] = False
+        pos[w] += 1
+        if signal and not (drop is not None and t[0] == drop):
+            assert flags.get((t[9], t[10]), 0) <= step, "slot signalled twice in a step"
+            flags[(t[9], t[10])] = step + 1
 
 
-@pytest.mark.parametrize("workers,split,seed", [(8, 16, 0), (13, 8, 1), (37, 32, 2)])
+@pytest.mark.parametrize("workers,split,seed", [(8, 16, 0), (13, 8, 1), (37, 32, 2), (40, 8, 4), (20, 8, 5)])
 def test_event_protocol_completes_under_random_interleavings(workers, split, seed):
     shape = ModelShape(2, 128, 4, 2, 64, 96, 100)
     g = parse(mk.mk_build_graph(cfg_of(shape, 2, 40, split), workers))
     assert simulate(g, shape, 2, steps=3, start_pos=5, seed=seed)
+
+
+@pytest.mark.parametrize("steps,start_pos,seed", [(3, 12, 6), (4, 30, 7)])
+def test_event_protocol_with_slice_merges(steps, start_pos, seed):
+    # 2-position splits: 7 to 17 active splits per head, so both merge forms occur
+    shape = ModelShape(2, 128, 4, 2, 64, 96, 100)
+    g = parse(mk.mk_build_graph(cfg_of(shape, 2, 40, 2), 96))
+    assert g["ns"] * 2 * shape.n_kv_heads <= 96
+    assert simulate(g, shape, 2, steps=steps, start_pos=start_pos, seed=seed)
 
 
 def test_dropped_signal_deadlocks_in_simulation():
