@@ -53,6 +53,7 @@ struct Misc {
   double rsd[16];       // matrix-core GEMV: RMSNorm scale per sequence
   float lmv[16];        // matrix-core LM head: running (max, index) per sequence
   int32_t lmi[16];
+  uint32_t cev, ctgt;   // the last (event, target) this worker's wait saw complete
 };
 static_assert(sizeof(Misc) <= MISC_BYTES, "misc");
 
@@ -287,10 +288,18 @@ constexpr int ATT_MCH = 8;
 __device__ __forceinline__ bool att_dist(const KParams& P) { return P.NS * P.B * P.Hkv <= P.n_workers; }
 __device__ __forceinline__ int att_active(const KParams& P, int s) { return (P.pos0 + s + 1 + P.S - 1) / P.S; }
 
-// att: ev is a layer's attention event
+// att: ev is a layer's attention event; cached: an attention task's wait, which first checks
+// whether this worker's previous attention task already saw the same event complete
 __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32_t target, uint32_t task, Misc* m,
-                                           uint64_t* tr = nullptr, bool att = false) {
+                                           uint64_t* tr = nullptr, bool att = false, bool cached = false) {
   if (ev == EV_NONE) return true;
+  // the worker's attention tasks of a layer usually share one (sequence, KV head) and so one
+  // event; slots only grow, so an event seen complete for this target still is
+  if (cached && m->cev == ev && m->ctgt == target) {
+    __syncthreads();
+    if (tr && threadIdx.x == 0) tr[1] = wall_clock64();
+    return true;
+  }
   const int tid = ltid();
   if (tid < 64) {
     const int lane = tid;
@@ -350,7 +359,13 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (lane == 0) m->flag = ok;
+    if (lane == 0) {
+      m->flag = ok;
+      if (ok && cached) {
+        m->cev = ev;
+        m->ctgt = target;
+      }
+    }
   }
   __syncthreads();
   if (tr && threadIdx.x == 0) tr[1] = wall_clock64();
@@ -1135,7 +1150,8 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   const int pos = P.pos0 + s, N = pos + 1;
   const int n_act = att_active(P, s);
   constexpr int MCH = ATT_MCH;  // single merger: accumulator splits in flight per thread
-  const bool slice = att_dist(P) && n_act > MCH;
+  const bool dist = att_dist(P);
+  const bool slice = dist && n_act > MCH;
   if (sp >= n_act) return true;  // split beyond the current length: nothing to do
   const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   const int j0 = sp * S, j1 = min(j0 + S, N);
@@ -1178,7 +1194,8 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   }
 
   Misc* m = (Misc*)(lds + P.misc_off);
-  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr)) return false;
+  // (with dist a worker holds at most one attention task of a layer: nothing to reuse)
+  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr, false, !dist)) return false;
 
   float* raw = (float*)lds;                    // [(G+2) D]: q heads, k, v as stored (fp32)
   double* qrot = (double*)(raw + (G + 2) * D); // [G D]
@@ -1554,6 +1571,8 @@ template <int NB>
 __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   char* lds = g_lds;
   const uint32_t off = ldg(P.list_off + blockIdx.x), n = ldg(P.list_len + blockIdx.x);
+  if (threadIdx.x == 0) ((Misc*)(lds + P.misc_off))->cev = EV_NONE;
+  __syncthreads();
   for (int s = 0; s < P.n_steps; ++s) {
     for (uint32_t i = 0; i < n; ++i) {
       const TaskRec t = ldg(P.tasks + ldg(P.cu_tasks + off + i));
