@@ -54,6 +54,7 @@ struct Misc {
   float lmv[16];        // matrix-core LM head: running (max, index) per sequence
   int32_t lmi[16];
   uint32_t cev, ctgt;   // the last (event, target) this worker's wait saw complete
+  uint32_t qk_step, qk_id;  // step tag and (layer, sequence, KV head) of the rotated queries in LDS
 };
 static_assert(sizeof(Misc) <= MISC_BYTES, "misc");
 
@@ -1141,7 +1142,8 @@ __device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
 __device__ __forceinline__ double tvd_val(uint64_t lo, uint64_t hi) { return __hiloint2double((int)(uint32_t)hi, (int)(uint32_t)lo); }
 
 // NL: K/V 16-byte loads per thread (the split covers at most NL * PPB positions)
-template <int G, int LPP, int NL>
+// QR: compiled with the reuse of rotated queries (left out where registers are scarce)
+template <int G, int LPP, int NL, bool QR>
 __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                           uint64_t* tr) {
   constexpr int D = LPP * 8, PPB = NT / LPP;
@@ -1176,10 +1178,17 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
   }
 
+  // Without dist, a worker's attention tasks of a layer are consecutive in its list and share
+  // one (sequence, KV head): a split that does not hold the current position reuses the rotated
+  // queries that the worker's previous task left in LDS.
+  Misc* m = (Misc*)(lds + P.misc_off);
+  const uint32_t qk_step = P.epoch + (uint32_t)s + 1u, qk_id = (uint32_t)(l * P.B * Hkv + bg);
+  const bool reuse = QR && !dist && !has_cur && m->qk_step == qk_step && m->qk_id == qk_id;
+
   // so do this thread's RoPE factors (and QK-norm gains): item tid is (head tid / (D/2), pair tid % (D/2))
   constexpr int half = D / 2;
   const int nh = G + (has_cur ? 1 : 0);  // heads to rotate (q heads, then k)
-  const bool rot = tid < nh * half;
+  const bool rot = !reuse && tid < nh * half;
   const int rh = tid / half, rk = tid - rh * half;
   double rc = 0.0, rsn = 0.0, g0 = 1.0, g1 = 1.0;
   if (rot) {
@@ -1193,7 +1202,6 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     }
   }
 
-  Misc* m = (Misc*)(lds + P.misc_off);
   // (with dist a worker holds at most one attention task of a layer: nothing to reuse)
   if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr, false, !dist)) return false;
 
@@ -1206,7 +1214,8 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   double* accw = (double*)(vsm + S * D);       // P.V partial sums, then the merge's scratch
 
   const float* src = P.qkv + (size_t)b * P.QKVR + (size_t)g * P.RG;
-  for (int i = tid * 4; i < (G + 2) * D; i += NT * 4) *(v4f*)(raw + i) = ldc4(src, (uint32_t)i);
+  if (!reuse)
+    for (int i = tid * 4; i < (G + 2) * D; i += NT * 4) *(v4f*)(raw + i) = ldc4(src, (uint32_t)i);
   // the cached values, position-major, for the P.V pass
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
@@ -1214,7 +1223,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     if (jr < S && j0 + jr < jc) *(uint4*)(vsm + jr * D + lp * 8) = vr[i];
   }
   __syncthreads();
-  if (P.qk_norm) {
+  if (P.qk_norm && !reuse) {
     for (int h = w; h < nh; h += NW) {
       double ss = 0.0;
       for (int d = lane; d < D; d += 64) ss += (double)raw[h * D + d] * (double)raw[h * D + d];
@@ -1241,6 +1250,10 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   }
   if (has_cur)
     for (int i = tid; i < D; i += NT) vcur[i] = vsm[(pos - j0) * D + i] = f2bf(raw[(G + 1) * D + i]);
+  if (QR && tid == 0) {
+    m->qk_step = qk_step;
+    m->qk_id = qk_id;
+  }
   __syncthreads();
 
   // ---- scores t_j = (q_h . k_j) / sqrt(D); LPP lanes share one position.  Heads go
@@ -1535,31 +1548,32 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   return ldc_u(P.status + ST_ABORT) == 0u;
 }
 
-template <int G, int LPP>
+template <int G, int LPP, bool QR>
 __device__ __forceinline__ bool attn_nl(const KParams& P, const TaskRec& t, int s, bool mega, char* lds, uint64_t* tr) {
   constexpr int PPB = NT / LPP;
-  if (P.S <= PPB) return task_attn<G, LPP, 1>(P, t, s, mega, lds, tr);
-  if (P.S <= 2 * PPB) return task_attn<G, LPP, 2>(P, t, s, mega, lds, tr);
+  if (P.S <= PPB) return task_attn<G, LPP, 1, QR>(P, t, s, mega, lds, tr);
+  if (P.S <= 2 * PPB) return task_attn<G, LPP, 2, QR>(P, t, s, mega, lds, tr);
   if constexpr (G == 1)  // longer splits only where one head's scores are in registers
-    if (P.S > ATT_MAXL * PPB) return task_attn<G, LPP, ATT_MAXL1>(P, t, s, mega, lds, tr);
-  return task_attn<G, LPP, ATT_MAXL>(P, t, s, mega, lds, tr);
+    if (P.S > ATT_MAXL * PPB) return task_attn<G, LPP, ATT_MAXL1, QR>(P, t, s, mega, lds, tr);
+  return task_attn<G, LPP, ATT_MAXL, QR>(P, t, s, mega, lds, tr);
 }
 
 template <int NB>
 __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                          uint64_t* tr = nullptr) {
   if (t.op == OP_ATTN) {
+    constexpr bool QR = NB < 8;  // at B >= 8 the matrix-core GEMV leaves no registers for it
     if (P.D == 64) {
       switch (P.G) {
-        case 1: return attn_nl<1, 8>(P, t, s, mega, lds, tr);
-        case 2: return attn_nl<2, 8>(P, t, s, mega, lds, tr);
-        default: return attn_nl<4, 8>(P, t, s, mega, lds, tr);
+        case 1: return attn_nl<1, 8, QR>(P, t, s, mega, lds, tr);
+        case 2: return attn_nl<2, 8, QR>(P, t, s, mega, lds, tr);
+        default: return attn_nl<4, 8, QR>(P, t, s, mega, lds, tr);
       }
     }
     switch (P.G) {
-      case 1: return attn_nl<1, 16>(P, t, s, mega, lds, tr);
-      case 2: return attn_nl<2, 16>(P, t, s, mega, lds, tr);
-      default: return attn_nl<4, 16>(P, t, s, mega, lds, tr);
+      case 1: return attn_nl<1, 16, QR>(P, t, s, mega, lds, tr);
+      case 2: return attn_nl<2, 16, QR>(P, t, s, mega, lds, tr);
+      default: return attn_nl<4, 16, QR>(P, t, s, mega, lds, tr);
     }
   }
   if constexpr (NB >= 8) return task_gemv_mfma<NB>(P, t, s, mega, lds, tr);
@@ -1571,7 +1585,11 @@ template <int NB>
 __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   char* lds = g_lds;
   const uint32_t off = ldg(P.list_off + blockIdx.x), n = ldg(P.list_len + blockIdx.x);
-  if (threadIdx.x == 0) ((Misc*)(lds + P.misc_off))->cev = EV_NONE;
+  if (threadIdx.x == 0) {
+    Misc* m = (Misc*)(lds + P.misc_off);
+    m->cev = EV_NONE;
+    if constexpr (NB < 8) m->qk_step = 0u;  // no rotated queries in LDS yet
+  }
   __syncthreads();
   for (int s = 0; s < P.n_steps; ++s) {
     for (uint32_t i = 0; i < n; ++i) {
@@ -1599,6 +1617,10 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
 template <int NB>
 __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
   char* lds = g_lds;
+  if constexpr (NB < 8) {
+    if (threadIdx.x == 0) ((Misc*)(lds + P.misc_off))->qk_step = 0u;  // no rotated queries in LDS yet
+    __syncthreads();
+  }
   for (int i = P.op_first; i < P.op_first + P.op_count; ++i)
     if (ldg(P.task_cu + i) == blockIdx.x) run_task<NB>(P, ldg(P.tasks + i), P.step, false, lds);
 }
