@@ -13,8 +13,9 @@
 // device-coherent accesses (sc1: they bypass the non-coherent per-XCD L2
 // state).  A producer drains its stores (s_waitcnt), joins its workgroup at a
 // barrier and then one lane stores the step number into its own slot of the
-// event; a consumer's wave 0 polls every slot of the event, then the
-// workgroup barrier releases the other waves.  Weights and the KV cache are
+// event; a consumer's wave 0 polls the event's slots (every slot, except that
+// a wait on a distributed attention event reads only the step's merging
+// splits), then the workgroup barrier releases the other waves.  Weights and the KV cache are
 // never written by one worker and read by another inside a launch (a KV
 // position is always re-read by the worker that wrote it), so they use plain
 // or non-temporal loads.
@@ -1115,10 +1116,12 @@ __device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& 
 // split's softmax partial: max m, sum l = sum_j e^{t_j - m}, and the
 // unnormalised acc = sum_j e^{t_j - m} v_j (FlashDecoding-style split-KV, as
 // in the Mirage article's attention search space).  Everything is evaluated
-// in fp64; partials are stored as tagged fp64 words.  The split holding the
-// current position merges all splits in ascending order:
-//   M = max_s m_s;  den = sum_s e^{m_s - M} l_s;  o = sum_s e^{m_s - M} acc_s / den,
-// and rounds o once to fp32.
+// in fp64; partials are stored as tagged fp64 words.  The merge
+//   M = max_s m_s;  den = sum_s e^{m_s - M} l_s;  o = sum_s e^{m_s - M} acc_s / den
+// adds the splits in ascending order and rounds o once to fp32.  It is done by
+// the split holding the current position, or, past ATT_MCH active splits with
+// a worker per attention task, by every active split for a slice of the
+// outputs (the forms are described with att_dist).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void st_tv(TV* p, uint32_t bits, uint32_t tag) {
   const uint64_t w = ((uint64_t)tag << 32) | bits;
