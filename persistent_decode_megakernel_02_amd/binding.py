@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(HERE, "libmk.so")
 
 MK_OK = 0
 MK_ERR = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OOM", -4: "HIP", -5: "CAPACITY", -6: "TIMEOUT", -7: "STATE"}
+(MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_OOM, MK_ERR_HIP, MK_ERR_CAPACITY, MK_ERR_TIMEOUT,
+ MK_ERR_STATE) = range(-1, -8, -1)
 MK_MODE_MEGAKERNEL = 0
 MK_MODE_PER_OP = 1
 

@@ -56,6 +56,7 @@ struct Misc {
   int32_t lmi[16];
   uint32_t cev, ctgt;   // the last (event, target) this worker's wait saw complete
   uint32_t qk_step, qk_id;  // step tag and (layer, sequence, KV head) of the rotated queries in LDS
+  int32_t att_fail;         // sticky: an attention merge of this worker exceeded its poll budget
 };
 static_assert(sizeof(Misc) <= MISC_BYTES, "misc");
 
@@ -1546,9 +1547,12 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
       stc_u(P.status + ST_EVENT, t.sig_ev);
     }
     stc_u(P.status + ST_ABORT, 1u);
+    m->att_fail = 1;
   }
   signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
-  return ldc_u(P.status + ST_ABORT) == 0u;
+  // the same verdict for every thread (read after the signal's barrier; never cleared within a
+  // launch); other workers' aborts are seen at this worker's next wait
+  return m->att_fail == 0;
 }
 
 template <int G, int LPP, bool QR>
@@ -1591,6 +1595,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   if (threadIdx.x == 0) {
     Misc* m = (Misc*)(lds + P.misc_off);
     m->cev = EV_NONE;
+    m->att_fail = 0;
     if constexpr (NB < 8) m->qk_step = 0u;  // no rotated queries in LDS yet
   }
   __syncthreads();
@@ -1620,10 +1625,12 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
 template <int NB>
 __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
   char* lds = g_lds;
-  if constexpr (NB < 8) {
-    if (threadIdx.x == 0) ((Misc*)(lds + P.misc_off))->qk_step = 0u;  // no rotated queries in LDS yet
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    Misc* m = (Misc*)(lds + P.misc_off);
+    m->att_fail = 0;
+    if constexpr (NB < 8) m->qk_step = 0u;  // no rotated queries in LDS yet
   }
+  __syncthreads();
   for (int i = P.op_first; i < P.op_first + P.op_count; ++i)
     if (ldg(P.task_cu + i) == blockIdx.x) run_task<NB>(P, ldg(P.tasks + i), P.step, false, lds);
 }

@@ -33,3 +33,12 @@ def test_error_reporting_without_context():
         mk.mk_build_graph(mk.make_cfg(__import__("persistent_decode_megakernel_02_amd.configs").configs.TINY, 5, 64), 8)
     assert e.value.code == -1
     assert "batch" in mk.mk_last_error(None)
+
+
+def test_binding_error_codes_match_the_header():
+    hdr = open(os.path.join(ROOT, "include", "mk.h")).read()
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MK_ERR_[A-Z_]+) \((-?\d+)\)", hdr)}
+    assert len(codes) == 7
+    for name, val in codes.items():
+        assert getattr(mk, name) == val, name
+        assert mk.MK_ERR[val] == name[len("MK_ERR_"):]
