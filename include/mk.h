@@ -93,8 +93,11 @@ typedef struct mk_tensor {
  * activations, event flags.  *out receives the context.  With cfg.split == 0
  * the attention split is S = min(Smax, max(32, ceil(max_seq / max(1, workers /
  * (batch * n_kv_heads))))) positions, Smax = 20480 / head_dim (32768 /
- * head_dim with one query head per KV head).  An explicit split above Smax is
- * UNSUPPORTED.  Batch 8 and 16 run the
+ * head_dim with one query head per KV head).  Where Smax caps it and the
+ * attention tasks then come to at most 3 per worker, the split shrinks to
+ * max(32, ceil(max_seq / n)), n the largest split count that keeps that
+ * per-worker count.  An explicit split above Smax is UNSUPPORTED.  Batch 8 and
+ * 16 run the
  * projections on the matrix cores and need hidden, ffn and n_q_heads *
  * head_dim to be multiples of 512.  Errors: INVALID_ARG, UNSUPPORTED (shape
  * cannot be tiled), OOM, HIP. */

@@ -50,8 +50,20 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   const int smax = (G == 1 ? 8 : 5) * 4096 / D;
   int S = c.split;
   if (S <= 0) {
-    const int ns_target = std::max(1, n_workers / std::max(1, c.batch * Hkv));
+    const int per = std::max(1, c.batch * Hkv);  // attention tasks per split
+    const int ns_target = std::max(1, n_workers / per);
     S = std::min(smax, std::max(kDefaultSplit, (c.max_seq + ns_target - 1) / ns_target));
+    // Capped by smax, the splits spill over into several tasks per worker.  Up to three per
+    // worker, take as many (shorter) splits as keep that count: the critical worker then runs
+    // the same number of shorter tasks.
+    const int ns_min = (c.max_seq + smax - 1) / smax;
+    if (ns_min > ns_target) {
+      const int64_t per_worker = ((int64_t)ns_min * per + n_workers - 1) / n_workers;
+      if (per_worker <= 3) {
+        const int ns = std::max<int64_t>(ns_min, per_worker * n_workers / per);
+        S = std::max(kDefaultSplit, (c.max_seq + ns - 1) / ns);
+      }
+    }
   }
   if (S > smax) return "split must be <= 5 * 4096 / head_dim (8 * 4096 / head_dim with one query head per KV head)";
   g.n_workers = n_workers;

@@ -12,6 +12,9 @@ Rules (one decode step; the persistent kernel repeats it every step):
     tiles per group; group g's rows start at g * RG.
   * ATTN: one task per (split s, sequence b, KV head g), split-major, split s
     covering positions [s S, (s + 1) S), S from the default rule unless given, NS = ceil(max_seq / S).
+    Default rule: S = min(Smax, max(32, ceil(max_seq / (workers // (B Hkv))))); when Smax caps it and
+    the resulting tasks come to at most 3 per worker, S = max(32, ceil(max_seq / ns)) with ns the
+    largest split count that keeps that per-worker count (and at least ceil(max_seq / Smax)).
   * Task number k of an operator runs on worker k mod workers.
   * Events per layer: Hkv QKV-group events, ATT, O, A, X; then one LM event.
     Fan-ins: TG, F_att, T_wo, T_gu, T_down, T_lm.  Slots are numbered
@@ -53,9 +56,16 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
     G = Hq // Hkv
     if split > 0:
         S = split
-    else:  # splits of a full cache fill the workers once; 32 <= S <= 5 * 4096 / D (8 * 4096 / D when G = 1)
-        ns_target = max(1, workers // max(1, B * Hkv))
-        S = min((8 if G == 1 else 5) * 4096 // D, max(32, -(-max_seq // ns_target)))
+    else:  # splits of a full cache fill the workers once; 32 <= S <= Smax = 5 * 4096 / D (8 * 4096 / D when G = 1)
+        per = max(1, B * Hkv)
+        ns_target = max(1, workers // per)
+        smax = (8 if G == 1 else 5) * 4096 // D
+        S = min(smax, max(32, -(-max_seq // ns_target)))
+        ns_min = -(-max_seq // smax)
+        if ns_min > ns_target:  # capped: at most 3 tasks per worker -> as many splits as keep that count
+            per_worker = -(-(ns_min * per) // workers)
+            if per_worker <= 3:
+                S = max(32, -(-max_seq // max(ns_min, per_worker * workers // per)))
     NS = -(-max_seq // S)
     RG = (G + 2) * D
     TG = min(max(1, workers // Hkv), RG)
