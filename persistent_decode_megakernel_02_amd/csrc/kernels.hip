@@ -1631,8 +1631,12 @@ __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
     if constexpr (NB < 8) m->qk_step = 0u;  // no rotated queries in LDS yet
   }
   __syncthreads();
-  for (int i = P.op_first; i < P.op_first + P.op_count; ++i)
+  // task k of an operator runs on worker k mod workers, so a worker steps through its own tasks
+  // (in list order) instead of scanning the operator's whole list
+  for (int k = blockIdx.x; k < P.op_count; k += P.n_workers) {
+    const int i = P.op_first + k;
     if (ldg(P.task_cu + i) == blockIdx.x) run_task<NB>(P, ldg(P.tasks + i), P.step, false, lds);
+  }
 }
 
 template <int NB>

@@ -88,6 +88,8 @@ def test_graph_invariants(shape, B, max_seq, workers, split):
     att = [t for t in tasks if t[1] == OP_ATTN and t[2] == 0]
     assert len(att) == g["ns"] * B * shape.n_kv_heads
     assert g["ns"] == -(-max_seq // g["split"])
+    # task k of an operator runs on worker k mod workers (the per-operator kernel steps by it)
+    assert all(t[11] == t[3] % g["workers"] for t in tasks)
     # QKV tiles never straddle a KV-head group
     for t in tasks:
         if t[1] == OP_QKV:
