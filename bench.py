@@ -53,33 +53,44 @@ def measured_traffic(workload, n_steps):
     return rec["traffic_bytes_per_step"] * n_steps
 
 
-def cpu_baseline(shape, host_weights, sample_layers=4):
-    """The oracle as it stands, single-threaded, on a bounded sample of the same shape.
+def host_info():
+    """Core count, CPU model and RAM of the host the oracle runs on."""
+    model, ram_gb = None, None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram_gb = round(int(line.split()[1]) / 2**20, 1)
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model, "host_ram_GiB": ram_gb}
 
-    One full 8B-shape step takes ~30 s on one core, so the sample is one decode step of two truncations of
-    the model that keep every matrix size: 0 layers (embedding, final norm, LM head) and `sample_layers`
-    layers.  Per-token time = t0 + n_layers * (t_k - t0) / k (every layer has the same shape; attention
-    over the workload's few hundred positions adds < 1% and is left out)."""
-    from dataclasses import replace
 
-    from persistent_decode_megakernel_02_amd import synth
+def cpu_baseline(shape, host_weights, tokens, n_threads, budget_s=20.0, max_steps=8):
+    """The oracle as it stands, on the full model of the workload, timed on this host.
+
+    It decodes the workload's first tokens from an empty cache: one untimed step, then up to max_steps
+    timed steps or about budget_s seconds, whichever comes first.  Attention over these few positions is a
+    negligible share of a step at this shape (the weight matrices dominate), so the per-step time stands
+    for the workload's steps.  Returns (ms per step, steps timed)."""
     from tests.parity import oracle_for
 
-    per_layer = len(synth.canonical_names(replace(shape, n_layers=1))) - 3
-
-    def one_step(n_layers):
-        sub = replace(shape, n_layers=n_layers)
-        ws = host_weights[:1 + n_layers * per_layer] + host_weights[-2:]
-        orc = oracle_for(sub, ws, max_seq=1, n_seq=1, n_threads=1)
+    orc = oracle_for(shape, host_weights, max_seq=max_steps + 1, n_seq=1, n_threads=n_threads)
+    try:
+        orc.step(0, int(tokens[0]))
         t0 = time.perf_counter()
-        orc.step(0, 1)
+        n = 0
+        while n < max_steps and (time.perf_counter() - t0) < budget_s:
+            orc.step(0, int(tokens[(n + 1) % len(tokens)]))
+            n += 1
         dt = time.perf_counter() - t0
+    finally:
         orc.close()
-        return dt
-
-    t0 = one_step(0)
-    tk = one_step(sample_layers)
-    return (t0 + shape.n_layers * (tk - t0) / sample_layers) * 1000.0
+    return dt / n * 1000.0, n
 
 
 def main():
@@ -112,107 +123,134 @@ def main():
     log(f"workload {w.name}: generating weights on cuda:0")
     weights = synth.make_weights(shape, seed=w.seed, device="cuda")
     seqs = synth.make_sequences(shape, B, w.prompt_len, w.kv_prefill, seed=w.seed, device="cuda")
-    eng = mk.Engine(shape, batch=B, max_seq=max_seq, split=args.split)
-    eng.load_weights(weights)
     host_weights = None
-    if not args.no_cpu:
-        log("copying weights to host for the CPU baseline")
-        host_weights = [(n, t.cpu()) for n, t in weights]
-    del weights
-    torch.cuda.empty_cache()
+    eng = None
+    toks = logits = mega_toks = mega_logits = None
+    out = None
+    # Every device object is released on every path before the interpreter exits: the context is
+    # destroyed (mk_destroy synchronises its stream and frees its memory) in the finally clause, not by
+    # a finaliser during interpreter shutdown.
+    try:
+        eng = mk.Engine(shape, batch=B, max_seq=max_seq, split=args.split)
+        eng.load_weights(weights)
+        if not args.no_cpu:
+            log("copying weights to host for the CPU baseline")
+            host_weights = [(n, t.cpu()) for n, t in weights]
+        del weights
+        torch.cuda.empty_cache()
 
-    def restore():
-        if w.prompt_len > 0:
-            eng.prefill(seqs["prompts"].cpu().numpy())
-        else:
-            for b in range(B):
-                eng.load_kv(b, seqs["k"][b], seqs["v"][b], int(seqs["pending"][b]))
+        def restore():
+            if w.prompt_len > 0:
+                eng.prefill(seqs["prompts"].cpu().numpy())
+            else:
+                for b in range(B):
+                    eng.load_kv(b, seqs["k"][b], seqs["v"][b], int(seqs["pending"][b]))
 
-    toks = torch.empty((max(K, W), B), dtype=torch.int32, device="cuda")
-    logits = torch.empty((max(K, W), B, shape.vocab), dtype=torch.float32, device="cuda")
+        toks = torch.empty((max(K, W), B), dtype=torch.int32, device="cuda")
+        logits = torch.empty((max(K, W), B, shape.vocab), dtype=torch.float32, device="cuda")
 
-    def timed(mode, n):
-        eng.set_mode(mode)
-        restore()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        mk.mk_decode(eng.ctx, n, toks, logits)
-        e1.record()
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1000.0
-        return e0.elapsed_time(e1), eng.last_ms(), wall
+        def timed(mode, n):
+            """HIP events on torch's current stream, which is the stream the library launches on."""
+            eng.set_mode(mode)
+            restore()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record()
+            mk.mk_decode(eng.ctx, n, toks, logits)
+            e1.record()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) * 1000.0
+            return e0.elapsed_time(e1), eng.last_ms(), wall
 
-    log(f"warmup: {W} steps (megakernel)")
-    if W > 0:
-        timed(mk.MK_MODE_MEGAKERNEL, W)
-    log(f"timed: {K} steps in one persistent launch")
-    ms_torch, ms_kernel, ms_wall = timed(mk.MK_MODE_MEGAKERNEL, K)
-    first_tokens = toks[: min(K, 8), 0].cpu().tolist()
-    mega_toks, mega_logits = toks[:K].clone(), logits[:K].clone()
-    ms_per_step = ms_torch / K
-    nbytes = algorithmic_bytes(shape, B, w.start_pos, K)
-    achieved = nbytes / (ms_kernel * 1e-3) / 1e9
-    roofline_ms = nbytes / K / (PEAK_GBS * 1e9) * 1e3
-    log(f"megakernel: {ms_per_step:.4f} ms/token ({ms_kernel:.2f} ms kernel, {ms_wall:.2f} ms wall), "
-        f"{achieved:.1f} GB/s, roofline {roofline_ms:.4f} ms/token, first tokens {first_tokens}")
+        log(f"warmup: {W} steps (megakernel)")
+        if W > 0:
+            timed(mk.MK_MODE_MEGAKERNEL, W)
+        log(f"timed: {K} steps in one persistent launch")
+        ms_torch, ms_kernel, ms_wall = timed(mk.MK_MODE_MEGAKERNEL, K)
+        first_tokens = toks[: min(K, 8), 0].cpu().tolist()
+        mega_toks, mega_logits = toks[:K].clone(), logits[:K].clone()
+        ms_per_step = ms_torch / K
+        nbytes = algorithmic_bytes(shape, B, w.start_pos, K)
+        # value and the roofline fraction come from the same timer (HIP events around the launch)
+        achieved = nbytes / (ms_torch * 1e-3) / 1e9
+        roofline_ms = nbytes / K / (PEAK_GBS * 1e9) * 1e3
+        log(f"megakernel: {ms_per_step:.4f} ms/token ({ms_torch:.2f} ms events on the launch stream, "
+            f"{ms_kernel:.2f} ms library events, {ms_wall:.2f} ms wall), {achieved:.1f} GB/s, "
+            f"roofline {roofline_ms:.4f} ms/token, first tokens {first_tokens}")
 
-    ablation, identical = None, None
-    if not args.no_ablation:
-        log(f"ablation: {K} steps, one launch per operator")
-        a_torch, a_kernel, _ = timed(mk.MK_MODE_PER_OP, K)
-        ablation = a_torch / K
-        identical = bool(torch.equal(mega_toks, toks[:K]) and
-                         torch.equal(mega_logits.view(torch.int32), logits[:K].view(torch.int32)))
-        log(f"per-operator: {ablation:.4f} ms/token; bit-identical to the megakernel: {identical}")
-        eng.set_mode(mk.MK_MODE_MEGAKERNEL)
-
-    probe = None
-    if args.probe_gib > 0:
+        ablation, identical = None, None
+        if not args.no_ablation:
+            log(f"ablation: {K} steps, one launch per operator")
+            a_torch, a_kernel, _ = timed(mk.MK_MODE_PER_OP, K)
+            ablation = a_torch / K
+            identical = bool(torch.equal(mega_toks, toks[:K]) and
+                             torch.equal(mega_logits.view(torch.int32), logits[:K].view(torch.int32)))
+            log(f"per-operator: {ablation:.4f} ms/token; bit-identical to the megakernel: {identical}")
+            eng.set_mode(mk.MK_MODE_MEGAKERNEL)
+        prompt_tokens = (seqs["prompts"][0].cpu().tolist() if w.prompt_len > 0 else first_tokens)
         eng.close()
-        nb = int(args.probe_gib * (1 << 30))
-        probe = {"read_GBps": round(mk.mk_read_bandwidth(nb, 3), 1), "copy_GBps": round(mk.mk_copy_bandwidth(nb, 3), 1),
-                 "bytes": nb}
-        log(f"plain read probe: {probe['read_GBps']} GB/s, copy probe: {probe['copy_GBps']} GB/s")
+        eng = None
+        del toks, logits, mega_toks, mega_logits, seqs
+        toks = logits = mega_toks = mega_logits = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
-    cpu = None
-    if host_weights is not None:
-        log("CPU baseline: oracle, 1 thread, one step of 0- and 4-layer truncations of the same shape")
-        eng.close()
-        ms_cpu = cpu_baseline(shape, host_weights, sample_layers=4)
-        cpu = {"value": round(ms_cpu, 1), "unit": "ms/token", "cores": 1, "kind": "oracle",
-               "sample": f"one decode step of 0-layer and 4-layer truncations of the {w.name} shape (same matrix "
-                         f"sizes), extrapolated linearly to {shape.n_layers} layers; single thread"}
-        log(f"CPU oracle: {ms_cpu:.1f} ms/token")
+        probe = None
+        if args.probe_gib > 0:
+            nb = int(args.probe_gib * (1 << 30))
+            probe = {"read_GBps": round(mk.mk_read_bandwidth(nb, 3), 1),
+                     "copy_GBps": round(mk.mk_copy_bandwidth(nb, 3), 1), "bytes": nb}
+            log(f"plain read probe: {probe['read_GBps']} GB/s, copy probe: {probe['copy_GBps']} GB/s")
 
-    traffic = measured_traffic(w.name, K)
-    out = {
-        "metric": METRIC,
-        "value": round(ms_per_step, 5),
-        "unit": "ms/token",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "prompt_tokens": w.prompt_len, "kv_prefill": w.kv_prefill,
-                   "decode_steps": K, "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
-                   "activations": "f32", "mode": "persistent megakernel, one launch"},
-        "tokens_per_s": round(B * 1000.0 / ms_per_step, 2),
-        "ablation_per_op_ms_per_step": round(ablation, 5) if ablation else None,
-        "ablation_bit_identical": identical,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                     "roofline_ms_per_step": round(roofline_ms, 5), "algorithmic_bytes_per_launch": nbytes},
-        "cpu_baseline": cpu,
-        "stream_probe": probe,
-        "frac_of_measured_read_peak": round(achieved / probe["read_GBps"], 4) if probe else None,
-    }
+        cpu = None
+        if host_weights is not None:
+            info = host_info()
+            threads = max(1, min(16, info["nproc"] or 1))
+            log(f"CPU baseline: oracle, {threads} threads, full {w.name} model ({info['cpu_model']}, "
+                f"nproc {info['nproc']})")
+            ms_cpu, n_cpu = cpu_baseline(shape, host_weights, prompt_tokens, threads)
+            host_weights = None
+            cpu = {"value": round(ms_cpu, 1), "unit": "ms/token", "cores": threads, "kind": "oracle",
+                   "sample": f"{n_cpu} decode steps of the full {w.name} model (batch 1, all {shape.n_layers} "
+                             f"layers and the LM head) after one untimed step, from an empty cache; "
+                             f"{threads} threads splitting each matrix's rows",
+                   **info}
+            log(f"CPU oracle: {ms_cpu:.1f} ms/token over {n_cpu} steps")
+
+        traffic = measured_traffic(w.name, K)
+        out = {
+            "metric": METRIC,
+            "value": round(ms_per_step, 5),
+            "unit": "ms/token",
+            "n_gpus": 1,
+            "steps": K,
+            "warmup": W,
+            "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": False,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": w.name, "batch": B, "prompt_tokens": w.prompt_len, "kv_prefill": w.kv_prefill,
+                       "decode_steps": K, "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
+                       "activations": "f32", "mode": "persistent megakernel, one launch"},
+            "tokens_per_s": round(B * 1000.0 / ms_per_step, 2),
+            "kernel_ms_library_events": round(ms_kernel, 3),
+            "ablation_per_op_ms_per_step": round(ablation, 5) if ablation else None,
+            "ablation_bit_identical": identical,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
+                         "roofline_ms_per_step": round(roofline_ms, 5), "algorithmic_bytes_per_launch": nbytes},
+            "cpu_baseline": cpu,
+            "stream_probe": probe,
+            "frac_of_measured_read_peak": round(achieved / probe["read_GBps"], 4) if probe else None,
+        }
+    finally:
+        if eng is not None:
+            eng.close()
+        del toks, logits, mega_toks, mega_logits
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 

@@ -1,7 +1,10 @@
 """Compile the CPU oracle (plain C) into oracle/liboracle.so.
 
 Test infrastructure only.  Flags keep the arithmetic exactly as written:
-no FMA contraction, no fast-math reassociation.
+no FMA contraction, no fast-math reassociation.  -O3 with AVX2 lets the
+compiler put the four rows a matvec walks side by side into one vector
+register; each row's sum still runs sequentially in ascending index, so the
+results are the same bits as a scalar build (a pin checks this).
 """
 import os
 import subprocess
@@ -13,7 +16,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 def build(verbose: bool = False) -> str:
     src = os.path.join(HERE, "oracle.c")
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
+    cmd = ["gcc", "-O3", "-mavx2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
            "-fopenmp", "-fPIC", "-shared", src, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))

@@ -1,10 +1,12 @@
 """GPU parity at the full Llama-3-8B and Chameleon-7B shapes, in the launch configuration the benchmark
 times (one worker per compute unit, default split, max_seq = start position + decode steps).
 
-The oracle (16 threads) recomputes the first decode steps one by one.  What it cannot reach at the full
-length is covered by properties that hold at any length: every token is the argmax of its own logits,
-every logit is finite, and the per-operator launches and a run split over two launches reproduce the
-single persistent launch bit for bit.
+The oracle (16 threads) recomputes the first 32 decode steps of every sequence one by one, teacher-forced
+on the GPU's tokens, and every one of those steps must meet the logit tolerances and the token rule.  At
+batch 8 and 16 the first and the last sequence get 32 steps and the others 2.  What the oracle cannot
+reach at the full length is covered by properties that hold at any length: every token is the argmax of
+its own logits, every logit is finite, and the per-operator launches and a run split over two launches
+reproduce the single persistent launch bit for bit.
 
 Every case prints its name before touching the GPU.
 """
@@ -16,12 +18,13 @@ torch = pytest.importorskip("torch")
 from persistent_decode_megakernel_02_amd import binding as mk  # noqa: E402
 from persistent_decode_megakernel_02_amd import synth  # noqa: E402
 from persistent_decode_megakernel_02_amd.configs import WORKLOADS  # noqa: E402
-from tests.parity import compare_free_running, oracle_for  # noqa: E402
+from tests.parity import STRICT_STEPS, compare_teacher_forced, oracle_for  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
 ORACLE_THREADS = 16
-N_ORACLE_STEPS = 3
+N_ORACLE_STEPS = STRICT_STEPS  # per checked sequence
+N_OTHER_SEQ_STEPS = 2          # batch >= 8: sequences other than the first and the last
 
 
 def say(msg):
@@ -76,11 +79,20 @@ def check_properties(toks, logits, label):
     assert toks.min() >= 0 and toks.max() < logits.shape[-1]
 
 
-def oracle_check(model, w, seqs, toks, logits, n_check, label):
+def steps_for(w, b):
+    if w.batch >= 8 and b not in (0, w.batch - 1):
+        return N_OTHER_SEQ_STEPS
+    return N_ORACLE_STEPS
+
+
+def oracle_check(model, w, seqs, toks, logits, label):
     B = w.batch
-    orc = oracle_for(model.shape, model.host(), max_seq=w.start_pos + n_check, n_seq=B, n_threads=ORACLE_THREADS)
+    n_max = max(steps_for(w, b) for b in range(B))
+    orc = oracle_for(model.shape, model.host(), max_seq=w.start_pos + n_max, n_seq=B, n_threads=ORACLE_THREADS)
     try:
         for b in range(B):
+            n_check = steps_for(w, b)
+            say(f"{label}: oracle, sequence {b}, {n_check} steps")
             if w.prompt_len > 0:
                 prompt = seqs["prompts"][b].cpu().numpy()
                 for t in prompt[:-1]:
@@ -91,7 +103,9 @@ def oracle_check(model, w, seqs, toks, logits, n_check, label):
                 v = synth.bf16_bits(seqs["v"][b])
                 orc.set_kv(b, k, v)
                 first = int(seqs["pending"][b])
-            compare_free_running(orc, b, first, toks[:, b], logits[:, b], n_check=n_check, label=f"{label} seq {b}")
+            rep = compare_teacher_forced(orc, b, first, toks[:, b], logits[:, b], n_check=n_check,
+                                         label=f"{label} seq {b}")
+            assert rep.steps == n_check
     finally:
         orc.close()
 
@@ -129,8 +143,7 @@ def test_llama8b_prompt512_matches_oracle_and_modes(llama):
         del tp, lp
     finally:
         eng.close()
-    say(f"{w.name}: oracle, first {N_ORACLE_STEPS} steps")
-    oracle_check(llama, w, seqs, t_mega, l_mega, N_ORACLE_STEPS, w.name)
+    oracle_check(llama, w, seqs, t_mega, l_mega, w.name)
 
 
 @pytest.mark.parametrize("name", ["llama8b_ctx4096", "llama8b_b1_ctx1024", "llama8b_b4_ctx1024",
@@ -150,8 +163,7 @@ def test_llama8b_prefilled_kv_matches_oracle(llama, name):
     finally:
         eng.close()
     check_properties(t, lg, name)
-    say(f"{name}: oracle, first {N_ORACLE_STEPS if w.batch == 1 else 2} steps")
-    oracle_check(llama, w, seqs, t, lg, N_ORACLE_STEPS if w.batch == 1 else 2, name)
+    oracle_check(llama, w, seqs, t, lg, name)
 
 
 def test_chameleon7b_ctx4096_matches_oracle(llama):
@@ -172,7 +184,6 @@ def test_chameleon7b_ctx4096_matches_oracle(llama):
         finally:
             eng.close()
         check_properties(t, lg, w.name)
-        say(f"{w.name}: oracle, first {N_ORACLE_STEPS} steps")
-        oracle_check(model, w, seqs, t, lg, N_ORACLE_STEPS, w.name)
+        oracle_check(model, w, seqs, t, lg, w.name)
     finally:
         model.free()

@@ -10,7 +10,7 @@ torch = pytest.importorskip("torch")
 from persistent_decode_megakernel_02_amd import binding as mk  # noqa: E402
 from persistent_decode_megakernel_02_amd import synth  # noqa: E402
 from persistent_decode_megakernel_02_amd.configs import TINY, ModelShape  # noqa: E402
-from tests.parity import compare_free_running, oracle_for  # noqa: E402
+from tests.parity import compare_teacher_forced, oracle_for  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,9 @@ def check_against_oracle(shape, weights, seqs, toks, logits, n_steps, label, n_t
         prompt = seqs["prompts"][b].numpy()
         for t in prompt[:-1]:
             orc.step(b, int(t), want_logits=False)
-        compare_free_running(orc, b, int(prompt[-1]), toks[:, b], logits[:, b], label=f"{label} seq {b}")
+        rep = compare_teacher_forced(orc, b, int(prompt[-1]), toks[:, b], logits[:, b], n_check=n_steps,
+                                     label=f"{label} seq {b}")
+        assert rep.steps == n_steps
     orc.close()
 
 
@@ -131,7 +133,9 @@ def test_prefilled_kv_matches_oracle():
     orc = oracle_for(shape, weights, max_seq=n_pos + n_steps, n_seq=B)
     for b in range(B):
         orc.set_kv(b, synth.bf16_bits(seqs["k"][b]), synth.bf16_bits(seqs["v"][b]))
-        compare_free_running(orc, b, int(seqs["pending"][b]), toks[:, b], logits[:, b], label=f"kv seq {b}")
+        rep = compare_teacher_forced(orc, b, int(seqs["pending"][b]), toks[:, b], logits[:, b], n_check=n_steps,
+                                     label=f"kv seq {b}")
+        assert rep.steps == n_steps
 
 
 @pytest.mark.parametrize("batch,prompt,steps", [(8, 9, 24), (16, 5, 20)])

@@ -61,6 +61,23 @@ def test_matvec_brute_force_within_higham_bound(rows, cols):
     assert y2[3] == 0.0 and np.array_equal(np.delete(y2, 3), np.delete(y, 3))
 
 
+def test_matvec_is_the_sequential_fp64_sum_of_each_row():
+    # every row is summed k = 0, 1, ... in fp64 with each product and each sum rounded once, whatever
+    # the compiler's vectorisation across rows (rows 0-7 go in blocks of four, row 8 alone)
+    rng = np.random.default_rng(11)
+    rows, cols = 9, 300
+    W16 = bits(rng.standard_normal((rows, cols)) * 0.02)
+    x = rng.standard_normal(cols)
+    W = bf16_bits_to_f64(W16)
+    want = []
+    for r in range(rows):
+        acc = 0.0
+        for k in range(cols):
+            acc = acc + float(W[r, k]) * float(x[k])
+        want.append(acc)
+    assert np.array_equal(po.matvec(W16, x), np.array(want))
+
+
 def test_matvec_threads_bit_identical():
     rng = np.random.default_rng(5)
     W16 = bits(rng.standard_normal((300, 512)) * 0.02)
