@@ -116,6 +116,7 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* tensors, int n);
  * (len > max_seq), STATE (no weights), HIP. */
 int mk_prefill(mk_ctx* ctx, const int32_t* prompts, int len);
 
+
 /* Install a pre-filled KV cache for sequence seq: k and v are bf16
  * [L][n_pos][Hkv*D] (keys already rotated), host memory or device memory
  * (on_device != 0).  pending is the token decode step 0 consumes at
@@ -140,6 +141,11 @@ int mk_set_mode(mk_ctx* ctx, int mode);
 /* Current position (shared by all sequences) and, if pending != NULL,
  * host int32 [B] pending tokens. */
 int mk_get_state(mk_ctx* ctx, int32_t* pos, int32_t* pending);
+
+/* Copy the context's configuration (as given to mk_create, with the mode
+ * set by mk_set_mode) into *out, so that a caller can size the buffers the
+ * other calls read and write.  Errors: INVALID_ARG. */
+int mk_get_config(mk_ctx* ctx, mk_model_cfg* out);
 
 /* Canonical little-endian serialisation of the task graph (header, event
  * table, task table in topological order).  If buf is NULL or *len is too

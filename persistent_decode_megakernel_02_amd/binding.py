@@ -41,6 +41,7 @@ class MkTensor(C.Structure):
 
 
 EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_load_kv", "mk_decode", "mk_set_mode", "mk_get_state",
+           "mk_get_config",
            "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
            "mk_read_bandwidth", "mk_copy_bandwidth",
            "mk_last_error", "mk_destroy"]
@@ -64,6 +65,7 @@ def lib():
         L.mk_decode.argtypes = [vp, C.c_int, vp, vp]
         L.mk_set_mode.argtypes = [vp, C.c_int]
         L.mk_get_state.argtypes = [vp, C.POINTER(i32), C.POINTER(i32)]
+        L.mk_get_config.argtypes = [vp, C.POINTER(MkModelCfg)]
         L.mk_get_graph.argtypes = [vp, vp, C.POINTER(sz)]
         L.mk_build_graph.argtypes = [C.POINTER(MkModelCfg), C.c_int, vp, C.POINTER(sz)]
         L.mk_reset.argtypes = [vp]
@@ -111,8 +113,10 @@ def mk_create(cfg: MkModelCfg):
 
 def mk_load_weights(ctx, named_tensors):
     """named_tensors: iterable of (name, bf16 torch tensor on any device)."""
+    import torch
     keep, arr = [], []
     for name, t in named_tensors:
+        _need(isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16, f"{name} must be a bf16 torch tensor")
         t = t.contiguous()
         keep.append(t)
         arr.append(MkTensor(name.encode(), C.c_void_p(t.data_ptr()), t.numel(), int(t.is_cuda)))
@@ -120,24 +124,62 @@ def mk_load_weights(ctx, named_tensors):
     _check(lib().mk_load_weights(ctx, a, len(arr)), ctx)
 
 
+def mk_get_config(ctx) -> MkModelCfg:
+    cfg = MkModelCfg()
+    _check(lib().mk_get_config(ctx, C.byref(cfg)), ctx)
+    return cfg
+
+
+# Argument checks.  The C calls take plain pointers and trust the sizes they imply; a host tensor, a
+# wrong dtype or a buffer too small for what the kernels write would make them access memory out of
+# bounds.  These checks compare each buffer with the sizes the context's configuration implies.
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise MkError(MK_ERR_INVALID_ARG, msg)
+
+
+def _check_device_buffer(t, dtype, numel: int, what: str):
+    import torch
+    _need(isinstance(t, torch.Tensor), f"{what} must be a torch tensor")
+    _need(t.is_cuda, f"{what} must be on the GPU")
+    _need(t.dtype == dtype, f"{what} must be {dtype}, got {t.dtype}")
+    _need(t.is_contiguous(), f"{what} must be contiguous")
+    _need(t.numel() >= numel, f"{what} holds {t.numel()} elements, the call writes {numel}")
+
+
 def mk_prefill(ctx, prompts):
+    """prompts: int [B, len] host array (B = the context's batch)."""
     p = np.ascontiguousarray(np.asarray(prompts, dtype=np.int32))
-    if p.ndim != 2:
-        raise ValueError("prompts must be [batch, len]")
+    cfg = mk_get_config(ctx)
+    _need(p.ndim == 2 and p.shape[0] == cfg.batch, f"prompts must be [batch={cfg.batch}, len], got {p.shape}")
     _check(lib().mk_prefill(ctx, p.ctypes.data_as(C.POINTER(C.c_int32)), p.shape[1]), ctx)
 
 
 def mk_load_kv(ctx, seq: int, k, v, pending: int):
     """k, v: bf16 torch tensors [L, n_pos, Hkv*D] on the GPU or the host."""
+    import torch
+    cfg = mk_get_config(ctx)
     k, v = k.contiguous(), v.contiguous()
+    for t, nm in ((k, "k"), (v, "v")):
+        _need(t.dtype == torch.bfloat16, f"{nm} must be bf16")
+        _need(t.dim() == 3 and t.shape[0] == cfg.n_layers and t.shape[2] == cfg.n_kv_heads * cfg.head_dim,
+              f"{nm} must be [n_layers={cfg.n_layers}, n_pos, {cfg.n_kv_heads * cfg.head_dim}], got {tuple(t.shape)}")
+    _need(k.shape == v.shape and k.is_cuda == v.is_cuda, "k and v must have the same shape and device")
     _check(lib().mk_load_kv(ctx, seq, k.shape[1], C.c_void_p(k.data_ptr()), C.c_void_p(v.data_ptr()), int(pending),
                             int(k.is_cuda)), ctx)
 
 
 def mk_decode(ctx, n_steps: int, out_tokens, out_logits=None):
     """out_tokens: int32 cuda tensor [n_steps, B]; out_logits: fp32 cuda tensor [n_steps, B, V] or None."""
-    _check(lib().mk_decode(ctx, n_steps, C.c_void_p(out_tokens.data_ptr()),
-                           C.c_void_p(out_logits.data_ptr()) if out_logits is not None else None), ctx)
+    import torch
+    cfg = mk_get_config(ctx)
+    if n_steps > 0:
+        _check_device_buffer(out_tokens, torch.int32, n_steps * cfg.batch, "out_tokens")
+        if out_logits is not None:
+            _check_device_buffer(out_logits, torch.float32, n_steps * cfg.batch * cfg.vocab, "out_logits")
+    tp = C.c_void_p(out_tokens.data_ptr()) if out_tokens is not None else None
+    _check(lib().mk_decode(ctx, n_steps, tp, C.c_void_p(out_logits.data_ptr()) if out_logits is not None else None),
+           ctx)
 
 
 def mk_set_mode(ctx, mode: int):

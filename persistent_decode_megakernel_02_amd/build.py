@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
 SOURCES = ["kernels.hip", "api.cpp", "graph.cpp"]
-HEADERS = ["mk_internal.h", "graph.h"]
+HEADERS = ["mk_internal.h", "graph.h", "gemv_stream.inc"]
 BATCHES = [1, 2, 4, 8, 16]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

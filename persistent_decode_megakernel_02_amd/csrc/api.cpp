@@ -24,6 +24,7 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* 
 hipError_t launch_copy_probe(void* buf, size_t bytes, int n_wg, hipStream_t st);
 size_t lds_bytes(const KParams& P);
 int max_coresident_workers(int B, size_t lds);
+
 constexpr int kLdsBytes = 163840;  // one worker per compute unit takes all of its LDS
 constexpr int kMiscBytes = 4096;   // per-worker scalars at the top of LDS (same size as in the kernels)
 constexpr int kMkSlice = 2048;     // K slice of the matrix-core GEMV (same as in the kernels)
@@ -37,6 +38,9 @@ using namespace mk;
 struct LdsPlan {
   int xs_doubles, red_doubles, red_off, misc_off;
   int mk_ks;  // batch >= 8: K slice of the matrix-core GEMV
+  // batch <= 4 (streaming GEMV engine): two activation regions, two row-sum and two residual
+  // buffers, and the K slices that fit a region with fp64 and with fp32 staging
+  int sg_rg0, sg_rg1, sg_red, sg_red_cap, sg_xold, sg_xold_cap, sg_kc64, sg_kc32;
 };
 
 struct mk_ctx {
@@ -68,6 +72,7 @@ struct mk_ctx {
   uint32_t* status = nullptr;
   EventRec* d_events = nullptr;
   TaskRec* d_tasks = nullptr;
+  SegRec* d_segrec = nullptr;
   uint32_t *d_task_cu = nullptr, *d_list_off = nullptr, *d_list_len = nullptr, *d_cu_tasks = nullptr;
   // state
   bool have_weights = false;
@@ -157,7 +162,18 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
     L.misc_off = kLdsBytes - kMiscBytes;
     L.red_off = L.misc_off - L.red_doubles * 8;
     L.xs_doubles = L.red_off / 8;
-    if (L.xs_doubles / B < 512) {
+    // streaming engine: [region 0][region 1][residual x 2][row sums x 2][misc]
+    const int resid = std::max(maxrows(cfg.hidden, g.n_wo), maxrows(cfg.hidden, g.n_down)) * B;
+    L.sg_red_cap = (worst * B + 1) / 2 * 2;
+    L.sg_red = (L.misc_off - 2 * L.sg_red_cap * 8) & ~15;
+    L.sg_xold_cap = (resid + 3) / 4 * 4;
+    L.sg_xold = (L.sg_red - 2 * L.sg_xold_cap * 4) & ~15;
+    const int rg = (L.sg_xold / 2) & ~15;
+    L.sg_rg0 = 0;
+    L.sg_rg1 = rg;
+    L.sg_kc64 = rg / (B * 8) / 512 * 512;
+    L.sg_kc32 = rg / (B * 4) / 512 * 512;
+    if (L.sg_kc64 < 512) {
       *why = "a GEMV tile has too many rows for LDS at this batch (use more workers or a smaller batch)";
       return MK_ERR_UNSUPPORTED;
     }
@@ -333,6 +349,44 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
       hipMemcpy(c->d_list_len, g.list_len.data(), g.list_len.size() * 4, hipMemcpyHostToDevice) ||
       hipMemcpy(c->d_cu_tasks, g.cu_tasks.data(), g.cu_tasks.size() * 4, hipMemcpyHostToDevice))
     return bail(fail(c, MK_ERR_HIP, "graph upload"));
+  // ---- per-task records of the streaming GEMV engine (weight addresses are fixed from here on)
+  {
+    std::vector<SegRec> sr(g.tasks.size());
+    for (size_t k = 0; k < g.tasks.size(); ++k) {
+      const TaskRec& t = g.tasks[k];
+      SegRec& r = sr[k];
+      std::memset(&r, 0, sizeof r);
+      r.op = t.op;
+      r.a1 = t.a1;
+      if (t.op == OP_ATTN) continue;
+      const LayerW& w = c->h_layers[t.op == OP_LM ? 0 : t.layer];
+      const uint16_t* W0;
+      const uint16_t* W1 = nullptr;
+      const uint16_t* gam = nullptr;
+      int K;
+      switch (t.op) {
+        case OP_QKV: W0 = w.wqkv; K = H; gam = w.attn_norm; break;
+        case OP_WO: W0 = w.wo; K = (int)QD; break;
+        case OP_GU: W0 = w.wg; W1 = w.wu; K = H; gam = w.ffn_norm; break;
+        case OP_DOWN: W0 = w.wd; K = F; break;
+        default: W0 = c->lm_head; K = H; gam = c->final_norm; break;
+      }
+      const uint32_t nu = t.a1 - t.a0;
+      r.w0 = W0 + (size_t)t.a0 * K;
+      r.w1 = W1 ? W1 + (size_t)t.a0 * K : r.w0 + (size_t)nu * K;
+      r.gamma = gam;
+      r.act = t.op == OP_WO ? c->o : t.op == OP_DOWN ? c->a : c->x;
+      r.K = (uint32_t)K;
+      r.nu = nu;
+      r.R = W1 ? 2 * nu : nu;
+      r.f64 = gam ? 1u : 0u;
+      r.kc = (uint32_t)(gam ? lp.sg_kc64 : lp.sg_kc32);
+      r.nsl = r.kc ? (uint32_t)((K + r.kc - 1) / r.kc) : 0u;
+    }
+    if ((rc = dalloc(c, (void**)&c->d_segrec, sr.size() * sizeof(SegRec)))) return bail(rc);
+    if (hipMemcpy(c->d_segrec, sr.data(), sr.size() * sizeof(SegRec), hipMemcpyHostToDevice) != hipSuccess)
+      return bail(fail(c, MK_ERR_HIP, "segment records upload"));
+  }
   if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess)
     return bail(fail(c, MK_ERR_HIP, "hipEventCreate"));
   c->seq_pos.assign(B, 0);
@@ -449,6 +503,14 @@ static KParams make_params(mk_ctx* c) {
   P.red_off = c->lds.red_off;
   P.misc_off = c->lds.misc_off;
   P.mk_ks = c->lds.mk_ks;
+  P.sg_rg0 = c->lds.sg_rg0;
+  P.sg_rg1 = c->lds.sg_rg1;
+  P.sg_red = c->lds.sg_red;
+  P.sg_red_cap = c->lds.sg_red_cap;
+  P.sg_xold = c->lds.sg_xold;
+  P.sg_xold_cap = c->lds.sg_xold_cap;
+  P.sg_kc64 = c->lds.sg_kc64;
+  P.sg_kc32 = c->lds.sg_kc32;
   P.layers = c->d_layers;
   P.embed = c->embed;
   P.final_norm = c->final_norm;
@@ -474,6 +536,7 @@ static KParams make_params(mk_ctx* c) {
   P.list_off = c->d_list_off;
   P.list_len = c->d_list_len;
   P.cu_tasks = c->d_cu_tasks;
+  P.segrec = c->d_segrec;
   P.status = c->status;
   P.watchdog = cfg.watchdog_polls ? cfg.watchdog_polls : kDefaultWatchdog;
   P.with_lm = 1;
@@ -503,45 +566,60 @@ static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
   return MK_OK;
 }
 
-int mk_prefill(mk_ctx* c, const int32_t* prompts, int len) {
-  if (!c || !prompts || len <= 0) return fail(c, MK_ERR_INVALID_ARG, "null prompts or len <= 0");
-  if (!c->have_weights) return fail(c, MK_ERR_STATE, "weights not loaded");
-  if (len > c->cfg.max_seq) return fail(c, MK_ERR_CAPACITY, "prompt longer than max_seq");
+// Prefill.  force: device int32 buffer of at least
+// B * (len - 1) elements for the forced tokens (step-major), staged here from the host prompts.
+// Allocates nothing.
+static int prefill_into(mk_ctx* c, const int32_t* prompts, int len, int32_t* force) {
   const int B = c->cfg.batch;
-  for (int64_t i = 0; i < (int64_t)B * len; ++i)
-    if (prompts[i] < 0 || prompts[i] >= c->cfg.vocab) return fail(c, MK_ERR_INVALID_ARG, "token id out of range");
   int rc = mk_reset(c);
   if (rc) return rc;
   const int n = len - 1;
   if (n > 0) {
-    std::vector<int32_t> f((size_t)n * B);
-    for (int s = 0; s < n; ++s)
-      for (int b = 0; b < B; ++b) f[(size_t)s * B + b] = prompts[(size_t)b * len + s];
-    if ((size_t)n * B > c->force_cap) {
-      if (c->force) {
-        (void)hipFree(c->force);
-        c->allocs.erase(std::find(c->allocs.begin(), c->allocs.end(), (void*)c->force));
-        c->force = nullptr;
-      }
-      if ((rc = dalloc(c, (void**)&c->force, f.size() * 4))) return rc;
-      c->force_cap = f.size();
-    }
-    HIPCHK(c, hipMemcpyAsync(c->force, f.data(), f.size() * 4, hipMemcpyHostToDevice, c->stream));
+    // forced token of step s, sequence b at force[s * B + b]: one strided copy per sequence
+    for (int b = 0; b < B; ++b)
+      HIPCHK(c, hipMemcpy2DAsync(force + b, (size_t)B * 4, prompts + (size_t)b * len, 4, 4, (size_t)n,
+                                 hipMemcpyHostToDevice, c->stream));
     KParams P = make_params(c);
     P.pos0 = 0;
     P.n_steps = n;
-    P.force_tok = c->force;
+    P.force_tok = force;
     P.with_lm = 0;
     if ((rc = run_per_op_steps(c, P, n, false))) return rc;
     c->epoch += (uint32_t)n;
   }
-  std::vector<int32_t> pend(B);
+  int32_t pend[16];
   for (int b = 0; b < B; ++b) pend[b] = prompts[(size_t)b * len + len - 1];
-  HIPCHK(c, hipMemcpyAsync(c->pending, pend.data(), (size_t)B * 4, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(c, hipMemcpyAsync(c->pending, pend, (size_t)B * 4, hipMemcpyHostToDevice, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
   c->pos = n;
   std::fill(c->seq_pos.begin(), c->seq_pos.end(), n);
   return MK_OK;
+}
+
+static int prefill_check(mk_ctx* c, const int32_t* prompts, int len) {
+  if (!c || !prompts || len <= 0) return fail(c, MK_ERR_INVALID_ARG, "null prompts or len <= 0");
+  if (!c->have_weights) return fail(c, MK_ERR_STATE, "weights not loaded");
+  if (len > c->cfg.max_seq) return fail(c, MK_ERR_CAPACITY, "prompt longer than max_seq");
+  for (int64_t i = 0; i < (int64_t)c->cfg.batch * len; ++i)
+    if (prompts[i] < 0 || prompts[i] >= c->cfg.vocab) return fail(c, MK_ERR_INVALID_ARG, "token id out of range");
+  return MK_OK;
+}
+
+int mk_prefill(mk_ctx* c, const int32_t* prompts, int len) {
+  int rc = prefill_check(c, prompts, len);
+  if (rc) return rc;
+  const size_t need = (size_t)(len - 1) * c->cfg.batch;
+  if (need > c->force_cap) {
+    if (c->force) {
+      (void)hipFree(c->force);
+      c->allocs.erase(std::find(c->allocs.begin(), c->allocs.end(), (void*)c->force));
+      c->force = nullptr;
+      c->force_cap = 0;
+    }
+    if ((rc = dalloc(c, (void**)&c->force, need * 4))) return rc;
+    c->force_cap = need;
+  }
+  return prefill_into(c, prompts, len, c->force);
 }
 
 int mk_load_kv(mk_ctx* c, int seq, int n_pos, const void* k, const void* v, int32_t pending, int on_device) {
@@ -571,6 +649,12 @@ int mk_set_mode(mk_ctx* c, int mode) {
   if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
   if (mode != MK_MODE_MEGAKERNEL && mode != MK_MODE_PER_OP) return fail(c, MK_ERR_INVALID_ARG, "unknown mode");
   c->cfg.mode = mode;
+  return MK_OK;
+}
+
+int mk_get_config(mk_ctx* c, mk_model_cfg* out) {
+  if (!c || !out) return fail(c, MK_ERR_INVALID_ARG, "null argument");
+  *out = c->cfg;
   return MK_OK;
 }
 

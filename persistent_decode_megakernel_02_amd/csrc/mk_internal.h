@@ -54,6 +54,22 @@ struct LayerW {
   const uint16_t* k_norm;     // [D] or null
 };
 
+// What the streaming GEMV engine (batch <= 4) reads about a task, built by the host once the
+// weight arena exists.  GEMV tasks stream rows w0 + r K for r < nu, then (gate/up) the up rows
+// w1 + (r - nu) K for nu <= r < R.  Their input is act [B][K] (x, o or a); the activations of K
+// slices of kc elements are staged as fp64 x * gamma when f64 (operators with a norm), else as
+// fp32.  Attention tasks carry only op and a1 (their split), which is what the engine needs to
+// skip the ones with no work.
+struct SegRec {
+  const uint16_t* w0;
+  const uint16_t* w1;
+  const uint16_t* gamma;
+  const float* act;
+  uint32_t op, a1;
+  uint32_t K, nu, R, kc, nsl, f64;
+};
+static_assert(sizeof(SegRec) == 64, "SegRec layout");
+
 struct LmPart {
   float val;
   int32_t idx;
@@ -83,6 +99,9 @@ struct KParams {
   int32_t xs_doubles, red_doubles;
   int32_t red_off, misc_off;  // byte offsets
   int32_t mk_ks;              // B >= 8: K slice staged per pass of the matrix-core GEMV
+  // B <= 4, streaming GEMV engine: two activation regions, two row-sum buffers, two residual
+  // buffers (byte offsets), their capacities, and the K slice of fp64- and fp32-staged operators
+  int32_t sg_rg0, sg_rg1, sg_red, sg_red_cap, sg_xold, sg_xold_cap, sg_kc64, sg_kc32;
   // weights
   const LayerW* layers;
   const uint16_t* embed;
@@ -114,6 +133,7 @@ struct KParams {
   const uint32_t* list_off;
   const uint32_t* list_len;
   const uint32_t* cu_tasks;
+  const SegRec* segrec;       // per task (batch <= 4)
   uint32_t* status;
   // run
   int32_t pos0, n_steps, with_lm;
