@@ -230,11 +230,11 @@ def main():
             "higher_is_better": False,
             "scaling": "weak",
             "vs_baseline": None,
-            "dtype": "f32",
+            "dtype": "f64",
             "data": "synthetic",
             "config": {"workload": w.name, "batch": B, "prompt_tokens": w.prompt_len, "kv_prefill": w.kv_prefill,
                        "decode_steps": K, "weights": "bf16 N(0,0.02) seeded", "kv_cache": "bf16",
-                       "activations": "f32", "mode": "persistent megakernel, one launch"},
+                       "activations": "f32 stored, f64 evaluation", "mode": "persistent megakernel, one launch"},
             "tokens_per_s": round(B * 1000.0 / ms_per_step, 2),
             "kernel_ms_library_events": round(ms_kernel, 3),
             "ablation_per_op_ms_per_step": round(ablation, 5) if ablation else None,
