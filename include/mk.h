@@ -116,6 +116,16 @@ int mk_load_weights(mk_ctx* ctx, const mk_tensor* tensors, int n);
  * (len > max_seq), STATE (no weights), HIP. */
 int mk_prefill(mk_ctx* ctx, const int32_t* prompts, int len);
 
+/* mk_prefill for callers that cannot allocate memory (code inside a HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, results and errors, but the forced prompt tokens are
+ * staged in a static device array that the library holds for the life of
+ * the process (one per device, resolved at mk_create) instead of a buffer
+ * the context allocates on first use.  It calls no hipMalloc or hipFree.
+ * Limit: batch * (len - 1) <= 65536 tokens; a longer prompt set returns
+ * MK_ERR_CAPACITY.  Every context on a device shares the array, which
+ * keeps the last call's tokens: calls that overlap on one device race. */
+int mk_prefill_noalloc(mk_ctx* ctx, const int32_t* prompts, int len);
 
 /* Install a pre-filled KV cache for sequence seq: k and v are bf16
  * [L][n_pos][Hkv*D] (keys already rotated), host memory or device memory

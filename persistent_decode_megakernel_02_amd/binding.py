@@ -40,7 +40,7 @@ class MkTensor(C.Structure):
     _fields_ = [("name", C.c_char_p), ("data", C.c_void_p), ("numel", C.c_int64), ("on_device", C.c_int32)]
 
 
-EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_load_kv", "mk_decode", "mk_set_mode", "mk_get_state",
+EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_prefill_noalloc", "mk_load_kv", "mk_decode", "mk_set_mode", "mk_get_state",
            "mk_get_config",
            "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
            "mk_read_bandwidth", "mk_copy_bandwidth",
@@ -61,6 +61,7 @@ def lib():
         L.mk_create.argtypes = [C.POINTER(MkModelCfg), C.POINTER(vp)]
         L.mk_load_weights.argtypes = [vp, C.POINTER(MkTensor), C.c_int]
         L.mk_prefill.argtypes = [vp, C.POINTER(i32), C.c_int]
+        L.mk_prefill_noalloc.argtypes = [vp, C.POINTER(i32), C.c_int]
         L.mk_load_kv.argtypes = [vp, C.c_int, C.c_int, vp, vp, i32, C.c_int]
         L.mk_decode.argtypes = [vp, C.c_int, vp, vp]
         L.mk_set_mode.argtypes = [vp, C.c_int]
@@ -153,6 +154,14 @@ def mk_prefill(ctx, prompts):
     cfg = mk_get_config(ctx)
     _need(p.ndim == 2 and p.shape[0] == cfg.batch, f"prompts must be [batch={cfg.batch}, len], got {p.shape}")
     _check(lib().mk_prefill(ctx, p.ctypes.data_as(C.POINTER(C.c_int32)), p.shape[1]), ctx)
+
+
+def mk_prefill_noalloc(ctx, prompts):
+    """As mk_prefill, with the prompt tokens staged in the library's static device array."""
+    p = np.ascontiguousarray(np.asarray(prompts, dtype=np.int32))
+    cfg = mk_get_config(ctx)
+    _need(p.ndim == 2 and p.shape[0] == cfg.batch, f"prompts must be [batch={cfg.batch}, len], got {p.shape}")
+    _check(lib().mk_prefill_noalloc(ctx, p.ctypes.data_as(C.POINTER(C.c_int32)), p.shape[1]), ctx)
 
 
 def mk_load_kv(ctx, seq: int, k, v, pending: int):

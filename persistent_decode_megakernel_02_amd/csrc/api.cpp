@@ -24,7 +24,8 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* 
 hipError_t launch_copy_probe(void* buf, size_t bytes, int n_wg, hipStream_t st);
 size_t lds_bytes(const KParams& P);
 int max_coresident_workers(int B, size_t lds);
-
+hipError_t noalloc_token_staging(int device, int32_t** ptr);
+constexpr int kNoAllocTokens = 1 << 16;  // capacity of the static token staging array (same as in kernels.hip)
 constexpr int kLdsBytes = 163840;  // one worker per compute unit takes all of its LDS
 constexpr int kMiscBytes = 4096;   // per-worker scalars at the top of LDS (same size as in the kernels)
 constexpr int kMkSlice = 2048;     // K slice of the matrix-core GEMV (same as in the kernels)
@@ -68,6 +69,7 @@ struct mk_ctx {
   int32_t* pending = nullptr;
   int32_t* force = nullptr;
   size_t force_cap = 0;
+  int32_t* noalloc_tokens = nullptr;  // this device's static staging array (mk_prefill_noalloc)
   uint32_t* flags = nullptr;
   uint32_t* status = nullptr;
   EventRec* d_events = nullptr;
@@ -223,6 +225,10 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if (hipGetDevice(&c->device) != hipSuccess) return bail(fail(c, MK_ERR_HIP, "hipGetDevice failed"));
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) return bail(fail(c, MK_ERR_HIP, "hipGetDeviceProperties"));
+  // the static token staging array of mk_prefill_noalloc: its address on this device, resolved
+  // once per device and kept for the life of the process
+  if (noalloc_token_staging(c->device, &c->noalloc_tokens) != hipSuccess)
+    return bail(fail(c, MK_ERR_HIP, "hipGetSymbolAddress of the static token staging array failed"));
   int nw = cfg.n_workers > 0 ? cfg.n_workers : prop.multiProcessorCount;
   why = build_graph(cfg, nw, &c->g);
   if (!why.empty()) return bail(fail(c, MK_ERR_UNSUPPORTED, why));
@@ -566,7 +572,7 @@ static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
   return MK_OK;
 }
 
-// Prefill.  force: device int32 buffer of at least
+// Prefill shared by mk_prefill and mk_prefill_noalloc.  force: device int32 buffer of at least
 // B * (len - 1) elements for the forced tokens (step-major), staged here from the host prompts.
 // Allocates nothing.
 static int prefill_into(mk_ctx* c, const int32_t* prompts, int len, int32_t* force) {
@@ -620,6 +626,17 @@ int mk_prefill(mk_ctx* c, const int32_t* prompts, int len) {
     c->force_cap = need;
   }
   return prefill_into(c, prompts, len, c->force);
+}
+
+int mk_prefill_noalloc(mk_ctx* c, const int32_t* prompts, int len) {
+  int rc = prefill_check(c, prompts, len);
+  if (rc) return rc;
+  const size_t need = (size_t)(len - 1) * c->cfg.batch;
+  if (need > (size_t)kNoAllocTokens)
+    return fail(c, MK_ERR_CAPACITY, "prompt needs " + std::to_string(need) + " staged tokens (batch * (len - 1)); "
+                                    "mk_prefill_noalloc holds at most " + std::to_string(kNoAllocTokens));
+  if (!c->noalloc_tokens) return fail(c, MK_ERR_STATE, "static token staging not resolved on this device");
+  return prefill_into(c, prompts, len, c->noalloc_tokens);
 }
 
 int mk_load_kv(mk_ctx* c, int seq, int n_pos, const void* k, const void* v, int32_t pending, int on_device) {

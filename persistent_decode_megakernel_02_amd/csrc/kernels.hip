@@ -21,6 +21,8 @@
 // or non-temporal loads.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "mk_internal.h"
 
 namespace mk {
@@ -1811,6 +1813,29 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* 
 
 size_t lds_bytes(const KParams& P) { return worker_lds_bytes(P); }
 
+// Token staging of mk_prefill_noalloc: a static device array (every context on a device shares
+// it; calls that overlap on one device race for it).  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, resolved once per device with that
+// device current, and only that address is ever handed to kernels or copies.
+constexpr int kNoAllocTokens = 1 << 16;
+static __device__ __align__(256) int32_t scratch[kNoAllocTokens];
+static int32_t* g_scratch_ptr[64];
+static bool g_scratch_ok[64];
+static std::mutex g_scratch_mu;
+
+hipError_t noalloc_token_staging(int device, int32_t** ptr) {
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ok[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = (int32_t*)p;
+    g_scratch_ok[device] = true;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 #define MK_DECL(nb)                                                         \
   hipError_t launch_b##nb(int kind, const KParams& P, hipStream_t st); \
