@@ -50,6 +50,10 @@ extern "C" {
 #define MK_MODE_MEGAKERNEL 0 /* one persistent cooperative launch per mk_decode */
 #define MK_MODE_PER_OP 1     /* ablation: one kernel launch per operator        */
 
+/* ---- schedules ------------------------------------------------------------ */
+#define MK_SCHEDULE_FROZEN 0 /* the schedule the offline search froze for this case */
+#define MK_SCHEDULE_GIVEN 1  /* the schedule fields of mk_model_cfg, as given        */
+
 /* ---- model / runtime configuration (plain data, copied by mk_create) ---- */
 typedef struct mk_model_cfg {
   int32_t n_layers;   /* decoder layers L                                   */
@@ -69,6 +73,20 @@ typedef struct mk_model_cfg {
   int32_t n_workers;  /* persistent workgroups; 0 = one per compute unit    */
   uint32_t watchdog_polls; /* max polls of one event wait; 0 = default     */
   void* stream;       /* hipStream_t the library launches on, or NULL       */
+  /* Schedule of the task graph (Ada-MK, gist.science, "L'Itinéraire
+   * Pré-planifié": searched offline, then fixed).  With schedule ==
+   * MK_SCHEDULE_FROZEN the fields below are ignored and the builder takes
+   * the entry the offline search froze for this shape, batch, worker count
+   * and max_seq (csrc/schedule_table.inc), else the plain rules; split > 0
+   * still overrides the split.  With MK_SCHEDULE_GIVEN they are used as
+   * given, 0 in a tile count meaning the plain rule.  All must be >= 0. */
+  int32_t schedule;   /* MK_SCHEDULE_*                                      */
+  int32_t qkv_tiles;  /* QKV tiles per KV-head group (at most workers / Hkv) */
+  int32_t wo_tiles, gu_tiles, down_tiles, lm_tiles; /* tiles per operator (<= workers) */
+  int32_t rotate;     /* tile i of a layer's k-th GEMV operator (QKV 0, WO 1,
+                         gate/up 2, down 3; LM head 4) runs on worker
+                         (i + k * rotate) mod workers                        */
+  int32_t attn_offset; /* attention task k runs on worker (k + attn_offset) mod workers */
 } mk_model_cfg;
 
 typedef struct mk_ctx mk_ctx;

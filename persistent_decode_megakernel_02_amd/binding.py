@@ -12,7 +12,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmk.so")
+# MK_LIBRARY selects a variant build (build.py VARIANTS) for measurements; the default is the
+# in-tree library.
+LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(HERE, "libmk.so")
 
 MK_OK = 0
 MK_ERR = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OOM", -4: "HIP", -5: "CAPACITY", -6: "TIMEOUT", -7: "STATE"}
@@ -20,6 +22,9 @@ MK_ERR = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OOM", -4: "HIP", -5: "CAPAC
  MK_ERR_STATE) = range(-1, -8, -1)
 MK_MODE_MEGAKERNEL = 0
 MK_MODE_PER_OP = 1
+MK_SCHEDULE_FROZEN = 0
+MK_SCHEDULE_GIVEN = 1
+SCHEDULE_FIELDS = ("qkv_tiles", "wo_tiles", "gu_tiles", "down_tiles", "lm_tiles", "rotate", "attn_offset")
 
 
 class MkError(RuntimeError):
@@ -33,7 +38,9 @@ class MkModelCfg(C.Structure):
                 ("head_dim", C.c_int32), ("ffn", C.c_int32), ("vocab", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_double), ("qk_norm", C.c_int32), ("batch", C.c_int32), ("max_seq", C.c_int32),
                 ("mode", C.c_int32), ("split", C.c_int32), ("n_workers", C.c_int32), ("watchdog_polls", C.c_uint32),
-                ("stream", C.c_void_p)]
+                ("stream", C.c_void_p), ("schedule", C.c_int32), ("qkv_tiles", C.c_int32), ("wo_tiles", C.c_int32),
+                ("gu_tiles", C.c_int32), ("down_tiles", C.c_int32), ("lm_tiles", C.c_int32), ("rotate", C.c_int32),
+                ("attn_offset", C.c_int32)]
 
 
 class MkTensor(C.Structure):
@@ -94,10 +101,18 @@ def _check(rc: int, ctx=None):
 
 
 def make_cfg(shape, batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, split: int = 0, n_workers: int = 0,
-             watchdog_polls: int = 0, stream=None) -> MkModelCfg:
-    return MkModelCfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
-                      shape.vocab, shape.rms_eps, shape.rope_theta, int(shape.qk_norm), batch, max_seq, mode, split,
-                      n_workers, watchdog_polls, stream)
+             watchdog_polls: int = 0, stream=None, schedule: dict | None = None) -> MkModelCfg:
+    """schedule: None for the frozen schedule, else a dict of SCHEDULE_FIELDS (missing ones 0)."""
+    cfg = MkModelCfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                     shape.vocab, shape.rms_eps, shape.rope_theta, int(shape.qk_norm), batch, max_seq, mode, split,
+                     n_workers, watchdog_polls, stream)
+    if schedule is not None:
+        unknown = set(schedule) - set(SCHEDULE_FIELDS)
+        _need(not unknown, f"unknown schedule fields {sorted(unknown)}")
+        cfg.schedule = MK_SCHEDULE_GIVEN
+        for k, v in schedule.items():
+            setattr(cfg, k, int(v))
+    return cfg
 
 
 def _current_stream_handle():
@@ -268,9 +283,10 @@ class Engine:
     """Owns one context: create -> load weights -> prefill/load_kv -> decode."""
 
     def __init__(self, shape, batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, split: int = 0,
-                 n_workers: int = 0, watchdog_polls: int = 0):
+                 n_workers: int = 0, watchdog_polls: int = 0, schedule: dict | None = None):
         self.shape, self.batch, self.max_seq = shape, batch, max_seq
-        self.cfg = make_cfg(shape, batch, max_seq, mode, split, n_workers, watchdog_polls, _current_stream_handle())
+        self.cfg = make_cfg(shape, batch, max_seq, mode, split, n_workers, watchdog_polls, _current_stream_handle(),
+                            schedule)
         self.ctx = mk_create(self.cfg)
 
     def load_weights(self, named_tensors):

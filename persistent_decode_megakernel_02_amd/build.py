@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
 SOURCES = ["kernels.hip", "api.cpp", "graph.cpp"]
-HEADERS = ["mk_internal.h", "graph.h", "gemv_stream.inc"]
+HEADERS = ["mk_internal.h", "graph.h", "gemv_stream.inc", "schedule_table.inc"]
 BATCHES = [1, 2, 4, 8, 16]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
@@ -37,11 +37,13 @@ def _run(cmd):
     return r.returncode, " ".join(cmd), err
 
 
-def build(verbose: bool = False, extra=(), jobs: int = 0) -> str:
+def build(verbose: bool = False, extra=(), jobs: int = 0, out: str = LIB) -> str:
+    """Compile and link the library to `out` (default: the in-tree libmk.so).  extra: additional
+    hipcc arguments, e.g. -D options that select a measured alternative (see VARIANTS)."""
     tmp = tempfile.mkdtemp(prefix="mkbuild_")
     try:
         units = _units(tmp)
-        units = [(cmd[:1] + list(extra) + cmd[1:], out) for cmd, out in units]
+        units = [(cmd[:1] + list(extra) + cmd[1:], obj) for cmd, obj in units]
         jobs = jobs or min(len(units), max(1, min(os.cpu_count() or 1, 16)))
         with ThreadPoolExecutor(jobs) as ex:
             results = list(ex.map(_run, [c for c, _ in units]))
@@ -52,16 +54,32 @@ def build(verbose: bool = False, extra=(), jobs: int = 0) -> str:
                 raise RuntimeError(f"hipcc failed ({rc}): {cmd}\n{err}")
             if verbose and err.strip():
                 print(err)
-        link = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o in units], "-o", LIB + ".tmp"]
+        link = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o in units], "-o", out + ".tmp"]
         rc, cmd, err = _run(link)
         if verbose:
             print(cmd, flush=True)
         if rc != 0:
             raise RuntimeError(f"link failed ({rc}): {cmd}\n{err}")
-        os.replace(LIB + ".tmp", LIB)
+        os.replace(out + ".tmp", out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out
+
+
+# Compile-time alternatives that the offline measurements compare with the built default:
+# the GEMV pipeline depth (groups of 4 KB in flight per wave) and the counter form of events.
+VARIANTS = {
+    "depth1": ["-DMK_GEMV_DEPTH=1"],
+    "depth3": ["-DMK_GEMV_DEPTH=3"],
+    "counter_events": ["-DMK_EVENT_COUNTER=1"],
+}
+VARIANT_DIR = os.path.join(HERE, "variants")
+
+
+def build_variant(name: str, verbose: bool = False) -> str:
+    """Build variants/libmk_<name>.so; load it by setting MK_LIBRARY to its path."""
+    os.makedirs(VARIANT_DIR, exist_ok=True)
+    return build(verbose, VARIANTS[name], out=os.path.join(VARIANT_DIR, f"libmk_{name}.so"))
 
 
 def sources_newer_than_lib() -> bool:
@@ -73,4 +91,8 @@ def sources_newer_than_lib() -> bool:
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    if sys.argv[1:2] == ["--variants"]:
+        for name in sys.argv[2:] or VARIANTS:
+            print(build_variant(name, verbose=True))
+    else:
+        build(verbose=True, extra=sys.argv[1:])

@@ -76,11 +76,13 @@ struct mk_ctx {
   TaskRec* d_tasks = nullptr;
   SegRec* d_segrec = nullptr;
   uint32_t *d_task_cu = nullptr, *d_list_off = nullptr, *d_list_len = nullptr, *d_cu_tasks = nullptr;
+  uint32_t* d_range_start = nullptr;
   // state
   bool have_weights = false;
   int pos = 0;
   std::vector<int> seq_pos;
   uint32_t epoch = 0;
+  uint32_t lm_skip = 0;  // steps of epoch run without the LM head (prefill)
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float last_ms = 0.f;
   // tracing
@@ -348,7 +350,9 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if ((rc = dalloc(c, (void**)&c->d_list_off, g.list_off.size() * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->d_list_len, g.list_len.size() * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->d_cu_tasks, g.cu_tasks.size() * 4))) return bail(rc);
-  if (hipMemcpy(c->d_events, g.events.data(), g.events.size() * sizeof(EventRec), hipMemcpyHostToDevice) ||
+  if ((rc = dalloc(c, (void**)&c->d_range_start, g.range_start.size() * 4))) return bail(rc);
+  if (hipMemcpy(c->d_range_start, g.range_start.data(), g.range_start.size() * 4, hipMemcpyHostToDevice) ||
+      hipMemcpy(c->d_events, g.events.data(), g.events.size() * sizeof(EventRec), hipMemcpyHostToDevice) ||
       hipMemcpy(c->d_tasks, g.tasks.data(), g.tasks.size() * sizeof(TaskRec), hipMemcpyHostToDevice) ||
       hipMemcpy(c->d_task_cu, g.task_cu.data(), g.task_cu.size() * 4, hipMemcpyHostToDevice) ||
       hipMemcpy(c->d_list_off, g.list_off.data(), g.list_off.size() * 4, hipMemcpyHostToDevice) ||
@@ -427,6 +431,7 @@ int mk_reset(mk_ctx* c) {
   c->pos = 0;
   std::fill(c->seq_pos.begin(), c->seq_pos.end(), 0);
   c->epoch = 0;
+  c->lm_skip = 0;
   return MK_OK;
 }
 
@@ -533,6 +538,7 @@ static KParams make_params(mk_ctx* c) {
   P.part_acc = c->part_acc;
   P.ntag = (uint32_t)c->g.events.size();
   P.epoch = c->epoch;
+  P.lm_skip = c->lm_skip;
   P.lm_part = c->lm_part;
   P.pending = c->pending;
   P.flags = c->flags;
@@ -542,6 +548,7 @@ static KParams make_params(mk_ctx* c) {
   P.list_off = c->d_list_off;
   P.list_len = c->d_list_len;
   P.cu_tasks = c->d_cu_tasks;
+  P.range_start = c->d_range_start;
   P.segrec = c->d_segrec;
   P.status = c->status;
   P.watchdog = cfg.watchdog_polls ? cfg.watchdog_polls : kDefaultWatchdog;
@@ -561,6 +568,7 @@ static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
     for (size_t r = 0; r < n_ranges; ++r) {
       P.op_first = (int)g.op_ranges[r].first;
       P.op_count = (int)g.op_ranges[r].count;
+      P.op_range = (int)r;
       const bool attn = g.tasks[g.op_ranges[r].first].op == OP_ATTN;
       HIPCHK(c, launch(attn ? 3 : 1, P, c->stream));
     }
@@ -592,6 +600,7 @@ static int prefill_into(mk_ctx* c, const int32_t* prompts, int len, int32_t* for
     P.with_lm = 0;
     if ((rc = run_per_op_steps(c, P, n, false))) return rc;
     c->epoch += (uint32_t)n;
+    c->lm_skip += (uint32_t)n;
   }
   int32_t pend[16];
   for (int b = 0; b < B; ++b) pend[b] = prompts[(size_t)b * len + len - 1];
@@ -697,6 +706,7 @@ int mk_decode(mk_ctx* c, int n_steps, int32_t* out_tokens, float* out_logits) {
   P.out_tokens = out_tokens;
   P.out_logits = out_logits;
   P.epoch = c->epoch;
+  P.lm_skip = c->lm_skip;
   if (c->trace && c->trace_step >= 0 && c->trace_step < n_steps && c->cfg.mode == MK_MODE_MEGAKERNEL) {
     HIPCHK(c, hipMemsetAsync(c->trace, 0, (size_t)c->g.n_workers * c->trace_stride * 4 * 8, c->stream));
     P.trace = c->trace;

@@ -15,7 +15,13 @@
 //    tiles per group of RG = (G + 2) D rows.  Gate/up units are row pairs.
 //  * Attention tasks: one per (split s, sequence b, KV head g), enumerated
 //    split-major; split s covers positions [s S, (s+1) S).
-//  * Task t of an operator goes to worker (index mod workers).
+//  * Placement: tile i of the k-th GEMV operator of a layer (QKV 0, WO 1, GU 2,
+//    DOWN 3; the LM head 4) goes to worker (i + k * rotate) mod workers, and
+//    attention task k to worker (k + attn_offset) mod workers.
+//  * Tile counts, the split and the placement form the schedule: either given
+//    in the configuration or, by default, the one the offline search froze
+//    for the shape (frozen_schedule), else the rules above with rotate =
+//    attn_offset = 0.
 //  * Topological order per layer: QKV, ATTN, WO, GU, DOWN; then LM.  Every
 //    worker walks its tasks in this order, so the unfinished task with the
 //    lowest index always has its inputs ready: no deadlock while all
@@ -30,6 +36,17 @@ namespace mk {
 namespace {
 uint32_t tile_lo(uint64_t i, uint64_t R, uint64_t T) { return (uint32_t)(i * R / T); }
 }  // namespace
+
+#include "schedule_table.inc"
+
+Schedule frozen_schedule(const mk_model_cfg& c, int n_workers) {
+  for (const FrozenSchedule& f : kFrozenSchedules)
+    if (f.L == c.n_layers && f.H == c.hidden && f.Hq == c.n_q_heads && f.Hkv == c.n_kv_heads && f.D == c.head_dim &&
+        f.F == c.ffn && f.V == c.vocab && f.B == c.batch && f.workers == n_workers && c.max_seq >= f.seq_lo &&
+        c.max_seq <= f.seq_hi)
+      return f.s;
+  return Schedule{};
+}
 
 std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   Graph g;
@@ -48,7 +65,27 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   // head per KV head).  Attention tasks are
   // latency-bound at short contexts, so more, shorter splits finish sooner.
   const int smax = (G == 1 ? 8 : 5) * 4096 / D;
-  int S = c.split;
+  Schedule sc;
+  if (c.schedule == MK_SCHEDULE_GIVEN) {
+    sc.qkv_tiles = c.qkv_tiles;
+    sc.wo_tiles = c.wo_tiles;
+    sc.gu_tiles = c.gu_tiles;
+    sc.down_tiles = c.down_tiles;
+    sc.lm_tiles = c.lm_tiles;
+    sc.rotate = c.rotate;
+    sc.attn_offset = c.attn_offset;
+  } else if (c.schedule == MK_SCHEDULE_FROZEN) {
+    sc = frozen_schedule(c, n_workers);
+  } else {
+    return "schedule must be MK_SCHEDULE_FROZEN or MK_SCHEDULE_GIVEN";
+  }
+  if (c.split > 0) sc.split = c.split;
+  if (sc.qkv_tiles < 0 || sc.wo_tiles < 0 || sc.gu_tiles < 0 || sc.down_tiles < 0 || sc.lm_tiles < 0 || sc.rotate < 0 ||
+      sc.attn_offset < 0)
+    return "schedule fields must be >= 0";
+  if (sc.wo_tiles > n_workers || sc.gu_tiles > n_workers || sc.down_tiles > n_workers || sc.lm_tiles > n_workers)
+    return "at most one tile per worker for each GEMV operator";
+  int S = sc.split;
   if (S <= 0) {
     const int per = std::max(1, c.batch * Hkv);  // attention tasks per split
     const int ns_target = std::max(1, n_workers / per);
@@ -70,14 +107,20 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   g.split = S;
   g.n_splits = (c.max_seq + S - 1) / S;
   const int RG = (G + 2) * D;
-  const int TG = std::min(std::max(1, n_workers / Hkv), RG);
+  const int TG = std::min(sc.qkv_tiles > 0 ? sc.qkv_tiles : std::max(1, n_workers / Hkv), RG);
   g.qkv_tiles_per_group = TG;
   g.n_qkv = TG * Hkv;
-  g.n_wo = std::min(n_workers, c.hidden);
-  g.n_gu = std::min(n_workers, c.ffn);
-  g.n_down = std::min(n_workers, c.hidden);
-  g.n_lm = std::min(n_workers, c.vocab);
-  if ((int64_t)g.n_qkv > n_workers) return "internal: too many QKV tiles";
+  auto tiles = [&](int want, int rows) { return std::min(want > 0 ? want : n_workers, rows); };
+  g.n_wo = tiles(sc.wo_tiles, c.hidden);
+  g.n_gu = tiles(sc.gu_tiles, c.ffn);
+  g.n_down = tiles(sc.down_tiles, c.hidden);
+  g.n_lm = tiles(sc.lm_tiles, c.vocab);
+  if ((int64_t)g.n_qkv > n_workers) return "QKV tiles (per group times n_kv_heads) exceed the workers";
+  g.rotate = sc.rotate % n_workers;
+  g.attn_offset = sc.attn_offset % n_workers;
+  // worker of tile i of the k-th GEMV operator of a layer, and of attention task k
+  auto place = [&](int k, uint32_t i) { return (uint32_t)((i + (uint64_t)k * g.rotate) % (uint32_t)n_workers); };
+  auto place_att = [&](uint32_t k) { return (uint32_t)((k + (uint64_t)g.attn_offset) % (uint32_t)n_workers); };
   // When every attention task of a layer has a worker of its own, all of a head's splits run
   // at once and each merges a slice of the outputs, signalling its own slot; otherwise the
   // split holding the current position merges everything and signals for its (sequence, head).
@@ -134,7 +177,7 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
       for (int i = 0; i < TG; ++i) {
         uint32_t tile = (uint32_t)(gg * TG + i);
         uint32_t r0 = (uint32_t)(gg * RG) + tile_lo(i, RG, TG), r1 = (uint32_t)(gg * RG) + tile_lo(i + 1, RG, TG);
-        push(OP_QKV, l, tile, r0, r1, in_ev, in_lag, ev_qkv(l, gg), (uint32_t)i, tile);
+        push(OP_QKV, l, tile, r0, r1, in_ev, in_lag, ev_qkv(l, gg), (uint32_t)i, place(0, tile));
       }
     range_end(f);
     f = range_begin();
@@ -143,26 +186,28 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
       for (int b = 0; b < c.batch; ++b)
         for (int gg = 0; gg < Hkv; ++gg, ++idx)
           push(OP_ATTN, l, idx, (uint32_t)(b * Hkv + gg), (uint32_t)s, ev_qkv(l, gg), 0, ev_att(l),
-               dist ? idx : (uint32_t)(b * Hkv + gg), idx);
+               dist ? idx : (uint32_t)(b * Hkv + gg), place_att(idx));
     range_end(f);
     f = range_begin();
     for (int i = 0; i < g.n_wo; ++i)
-      push(OP_WO, l, i, tile_lo(i, c.hidden, g.n_wo), tile_lo(i + 1, c.hidden, g.n_wo), ev_att(l), 0, ev_o(l), i, i);
+      push(OP_WO, l, i, tile_lo(i, c.hidden, g.n_wo), tile_lo(i + 1, c.hidden, g.n_wo), ev_att(l), 0, ev_o(l), i,
+           place(1, i));
     range_end(f);
     f = range_begin();
     for (int i = 0; i < g.n_gu; ++i)
-      push(OP_GU, l, i, tile_lo(i, c.ffn, g.n_gu), tile_lo(i + 1, c.ffn, g.n_gu), ev_o(l), 0, ev_a(l), i, i);
+      push(OP_GU, l, i, tile_lo(i, c.ffn, g.n_gu), tile_lo(i + 1, c.ffn, g.n_gu), ev_o(l), 0, ev_a(l), i,
+           place(2, i));
     range_end(f);
     f = range_begin();
     for (int i = 0; i < g.n_down; ++i)
       push(OP_DOWN, l, i, tile_lo(i, c.hidden, g.n_down), tile_lo(i + 1, c.hidden, g.n_down), ev_a(l), 0, ev_x(l), i,
-           i);
+           place(3, i));
     range_end(f);
   }
   uint32_t f = range_begin();
   for (int i = 0; i < g.n_lm; ++i)
     push(OP_LM, 0, i, tile_lo(i, c.vocab, g.n_lm), tile_lo(i + 1, c.vocab, g.n_lm), ev_x(c.n_layers - 1), 0, ev_lm, i,
-         i);
+         place(4, i));
   range_end(f);
 
   // per-worker lists in topological order
@@ -179,6 +224,16 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   for (uint32_t i = 0; i < g.tasks.size(); ++i) {
     uint32_t cu = g.task_cu[i];
     g.cu_tasks[g.list_off[cu] + fill[cu]++] = i;
+  }
+  const size_t nr = g.op_ranges.size();
+  g.range_start.assign((nr + 1) * n_workers, 0);
+  for (int w = 0; w < n_workers; ++w) {
+    uint32_t j = 0;
+    for (size_t r = 0; r < nr; ++r) {
+      while (j < g.list_len[w] && g.cu_tasks[g.list_off[w] + j] < g.op_ranges[r].first) ++j;
+      g.range_start[r * n_workers + w] = j;
+    }
+    g.range_start[nr * n_workers + w] = g.list_len[w];
   }
   *out = std::move(g);
   return "";

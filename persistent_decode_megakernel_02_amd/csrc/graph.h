@@ -19,7 +19,25 @@ struct Graph {
   std::vector<uint32_t> list_off, list_len, cu_tasks;  // per-worker ordered task lists
   struct Range { uint32_t first, count; };
   std::vector<Range> op_ranges;     // operator instances of one step, in topological order
+  // [op_ranges.size() + 1][n_workers]: position in worker w's list of its first task of range r
+  // (row op_ranges.size(): the list lengths), so a per-operator launch finds each worker's tasks
+  std::vector<uint32_t> range_start;
+  int rotate = 0, attn_offset = 0;  // placement (see build_graph)
 };
+
+// The schedule choices of one graph: what the offline search varies (tile counts per operator,
+// the attention split, where each operator's tasks sit on the workers).  0 in a field of
+// mk_model_cfg means the frozen default for the shape (frozen_schedule).
+struct Schedule {
+  int split = 0;       // positions per attention task (0: the default rule)
+  int qkv_tiles = 0;   // QKV tiles per KV-head group
+  int wo_tiles = 0, gu_tiles = 0, down_tiles = 0, lm_tiles = 0;
+  int rotate = 0;      // GEMV operator k of a layer (QKV 0, WO 1, GU 2, DOWN 3; LM 4): tile i on worker i + k rotate
+  int attn_offset = 0; // attention task k on worker k + attn_offset
+};
+
+// The search's winner for cfg's shape and batch at n_workers (all fields 0 where it has none).
+Schedule frozen_schedule(const mk_model_cfg& cfg, int n_workers);
 
 // Validate the shape and build the graph; returns "" or an error message.
 std::string build_graph(const mk_model_cfg& cfg, int n_workers, Graph* g);

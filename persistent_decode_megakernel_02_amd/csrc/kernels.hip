@@ -30,7 +30,10 @@ namespace mk {
 constexpr int NT = 512;  // threads per worker
 constexpr int NW = NT / 64;
 constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
-constexpr int DEPTH = 2;   // pipeline groups in flight per wave (8 KB per wave): a wave's loads complete in
+#ifndef MK_GEMV_DEPTH
+#define MK_GEMV_DEPTH 2
+#endif
+constexpr int DEPTH = MK_GEMV_DEPTH;   // pipeline groups in flight per wave (8 KB per wave): a wave's loads complete in
                           // order, so a deeper queue delays the activation and flag loads behind it
 constexpr int MISC_BYTES = 4096;
 constexpr int ATT_MAXL = 5;   // most K/V 16-byte loads per thread per attention task (split <= 5 * 512 / (D / 8)) ...
@@ -312,6 +315,18 @@ __device__ __forceinline__ double silu_d(double z) { return z / (1.0 + exp(-z));
 // (without dist, in slot b Hkv + g, and a split may wait only on splits listed before it).
 constexpr int ATT_MCH = 8;
 __device__ __forceinline__ bool att_dist(const KParams& P) { return P.NS * P.B * P.Hkv <= P.n_workers; }
+
+// Event form.  Default: one 32-bit slot per producer holding the number of the last step it
+// completed; an event fires for step t when every slot it waits on holds t (plain stores, no
+// read-modify-write).  MK_EVENT_COUNTER=1 builds the counter form instead, to measure one
+// against the other: one word per event, advanced by one device-scope atomic add per producer
+// and step, firing for step t at fanin * t.  Every producer then signals every step (attention
+// splits beyond the current length included, after their wait, so that no step's add can land
+// before the previous step's event has fired).
+#ifndef MK_EVENT_COUNTER
+#define MK_EVENT_COUNTER 0
+#endif
+constexpr bool kEventCounter = MK_EVENT_COUNTER != 0;
 __device__ __forceinline__ int att_active(const KParams& P, int s) { return (P.pos0 + s + 1 + P.S - 1) / P.S; }
 
 // att: ev is a layer's attention event; cached: an attention task's wait, which first checks
@@ -332,8 +347,14 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
     const EventRec e = ldg(P.events + ev);
     const uint32_t* f = P.flags + e.slot0;
     uint32_t fanin = e.fanin;
-    // a dist attention event: only the slots of the step's signalling splits
-    if (att && att_dist(P)) {
+    uint32_t want = target;
+    if constexpr (kEventCounter) {  // the event's one counter word, at fanin adds per step
+      f = P.flags + ev;
+      fanin = 1;
+      // the LM head's event saw no adds in the steps run without it (prefill)
+      const bool lm = ev == (uint32_t)(P.L * (P.Hkv + 4));
+      want = e.fanin * (target - (lm ? P.lm_skip : 0u));
+    } else if (att && att_dist(P)) {  // a dist attention event: only the slots of the step's signalling splits
       const int n_act = att_active(P, (int)(target - P.epoch) - 1);
       const uint32_t bh = (uint32_t)(P.B * P.Hkv);
       if (n_act > ATT_MCH) {
@@ -350,14 +371,14 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
     constexpr uint32_t PW = 4;
     for (;;) {
       bool mine = true;
-      uint32_t seen = target;
+      uint32_t seen = want;
       for (uint32_t i0 = 0; i0 < fanin; i0 += 64 * PW) {
         uint32_t v[PW];
 #pragma unroll
         for (uint32_t k = 0; k < PW; ++k) v[k] = ldc_u(f + min(i0 + lane + 64 * k, fanin - 1));
 #pragma unroll
         for (uint32_t k = 0; k < PW; ++k)
-          if ((int32_t)(v[k] - target) < 0) {
+          if ((int32_t)(v[k] - want) < 0) {
             mine = false;
             seen = v[k];
           }
@@ -377,7 +398,7 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
             stc_u(P.status + ST_TASK, task);
             stc_u(P.status + ST_EVENT, ev);
             stc_u(P.status + ST_SEEN, seen);
-            stc_u(P.status + ST_WANT, target);
+            stc_u(P.status + ST_WANT, want);
           }
           if (lane == 0) stc_u(P.status + ST_ABORT, 1u);
           break;
@@ -401,7 +422,12 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
 __device__ __forceinline__ void signal_event(const KParams& P, uint32_t ev, uint32_t slot, uint32_t val) {
   __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent stores have completed
   __syncthreads();                // ... and every other wave's
-  if (threadIdx.x == 0) stc_u(P.flags + ldg(P.events + ev).slot0 + slot, val);
+  if (threadIdx.x == 0) {
+    if constexpr (kEventCounter)
+      __hip_atomic_fetch_add((GAS uint32_t*)(P.flags + ev), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      stc_u(P.flags + ldg(P.events + ev).slot0 + slot, val);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1181,7 +1207,16 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   constexpr int MCH = ATT_MCH;  // single merger: accumulator splits in flight per thread
   const bool dist = att_dist(P);
   const bool slice = dist && n_act > MCH;
-  if (sp >= n_act) return true;  // split beyond the current length: nothing to do
+  if (sp >= n_act) {  // split beyond the current length: nothing to do
+    if constexpr (kEventCounter) {  // ... but its add, in step (dist: every attention task signals)
+      if (dist) {
+        Misc* mm = (Misc*)(lds + P.misc_off);
+        if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, mm, tr, false, false)) return false;
+        signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+      }
+    }
+    return true;
+  }
   const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   const int j0 = sp * S, j1 = min(j0 + S, N);
   const bool has_cur = (j1 == N);  // this split holds the current position (and appends it)
@@ -1384,6 +1419,12 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   }
   if (tr && tid == 0) tr[2] = wall_clock64();  // partial stored
   if (!has_cur && !slice) {  // the merger checks this split's partial by its tags
+    if constexpr (kEventCounter) {
+      if (dist) {
+        signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+        return true;
+      }
+    }
     __syncthreads();
     return true;
   }
@@ -1680,11 +1721,12 @@ __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
     if constexpr (NB < 8) m->qk_step = 0u;  // no rotated queries in LDS yet
   }
   __syncthreads();
-  // task k of an operator runs on worker k mod workers, so a worker steps through its own tasks
-  // (in list order) instead of scanning the operator's whole list
-  for (int k = blockIdx.x; k < P.op_count; k += P.n_workers) {
-    const int i = P.op_first + k;
-    if (ldg(P.task_cu + i) != blockIdx.x) continue;
+  // a worker's tasks of this operator instance are a contiguous stretch of its list (the lists
+  // are in topological order), located by the host: no scan of the operator's other tasks
+  const uint32_t w = blockIdx.x, nw = (uint32_t)P.n_workers, r = (uint32_t)P.op_range;
+  const uint32_t j1 = ldg(P.range_start + (r + 1u) * nw + w), off = ldg(P.list_off + w);
+  for (uint32_t j = ldg(P.range_start + r * nw + w); j < j1; ++j) {
+    const int i = (int)ldg(P.cu_tasks + off + j);
     const TaskRec t = ldg(P.tasks + i);
     if constexpr (NB <= 4 && kStreamEngine) {
       if (t.op != OP_ATTN) {  // a segment of one task

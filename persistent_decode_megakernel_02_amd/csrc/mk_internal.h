@@ -133,14 +133,16 @@ struct KParams {
   const uint32_t* list_off;
   const uint32_t* list_len;
   const uint32_t* cu_tasks;
+  const uint32_t* range_start;  // [n_ranges + 1][workers]: a worker's first list position per operator instance
   const SegRec* segrec;       // per task (batch <= 4)
   uint32_t* status;
   // run
   int32_t pos0, n_steps, with_lm;
   uint32_t epoch, watchdog;  // epoch: decode steps run by this context so far (any mode, prefill included)
+  uint32_t lm_skip;          // steps of epoch run without the LM head (counter-form events only)
   uint32_t ntag;             // tag period: number of events
   // per-operator launch
-  int32_t op_first, op_count, step;
+  int32_t op_first, op_count, op_range, step;
   // optional trace of one decode step: [worker][list index][4] wall-clock stamps
   uint64_t* trace;
   int32_t trace_step, trace_stride;

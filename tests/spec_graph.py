@@ -15,7 +15,11 @@ Rules (one decode step; the persistent kernel repeats it every step):
     Default rule: S = min(Smax, max(32, ceil(max_seq / (workers // (B Hkv))))); when Smax caps it and
     the resulting tasks come to at most 3 per worker, S = max(32, ceil(max_seq / ns)) with ns the
     largest split count that keeps that per-worker count (and at least ceil(max_seq / Smax)).
-  * Task number k of an operator runs on worker k mod workers.
+  * Placement: tile i of the k-th GEMV operator of a layer (QKV 0, WO 1, GU 2, DOWN 3; the LM
+    head 4) runs on worker (i + k * rotate) mod workers; attention task k on worker
+    (k + attn_offset) mod workers.
+  * A schedule may fix the tile counts: TG = min(qkv_tiles, RG) QKV tiles per group, and
+    T = min(x_tiles, R) for the other GEMV operators (0 keeps the rules above).
   * Events per layer: Hkv QKV-group events, ATT, O, A, X; then one LM event.
     Fan-ins: TG, F_att, T_wo, T_gu, T_down, T_lm.  Slots are numbered
     consecutively in event order.  The attention tasks are "distributed" when
@@ -52,7 +56,8 @@ class Task:
     worker: int
 
 
-def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
+def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0, wo_tiles=0, gu_tiles=0,
+               down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0):
     G = Hq // Hkv
     if split > 0:
         S = split
@@ -68,8 +73,13 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
                 S = max(32, -(-max_seq // max(ns_min, per_worker * workers // per)))
     NS = -(-max_seq // S)
     RG = (G + 2) * D
-    TG = min(max(1, workers // Hkv), RG)
-    n_wo, n_gu, n_down, n_lm = min(workers, H), min(workers, F), min(workers, H), min(workers, V)
+    TG = min(qkv_tiles or max(1, workers // Hkv), RG)
+    n_wo, n_gu = min(wo_tiles or workers, H), min(gu_tiles or workers, F)
+    n_down, n_lm = min(down_tiles or workers, H), min(lm_tiles or workers, V)
+    rot, aoff = rotate % workers, attn_offset % workers
+
+    def place(k, i):
+        return (i + k * rot) % workers
     per_layer = Hkv + 4
     dist = NS * B * Hkv <= workers
 
@@ -92,22 +102,22 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0):
             for i in range(TG):
                 t = g * TG + i
                 tasks.append(Task(OP_QKV, layer, t, g * RG + lo(i, RG, TG), g * RG + lo(i + 1, RG, TG),
-                                  in_ev, lag, ev(layer, g), i, t % workers))
+                                  in_ev, lag, ev(layer, g), i, place(0, t)))
         k = 0
         for s in range(NS):
             for b in range(B):
                 for g in range(Hkv):
                     tasks.append(Task(OP_ATTN, layer, k, b * Hkv + g, s, ev(layer, g), 0, ev(layer, Hkv),
-                                      k if dist else b * Hkv + g, k % workers))
+                                      k if dist else b * Hkv + g, (k + aoff) % workers))
                     k += 1
-        for op, R, T, wait, sig in ((OP_WO, H, n_wo, Hkv, Hkv + 1), (OP_GU, F, n_gu, Hkv + 1, Hkv + 2),
-                                    (OP_DOWN, H, n_down, Hkv + 2, Hkv + 3)):
+        for k, (op, R, T, wait, sig) in enumerate(((OP_WO, H, n_wo, Hkv, Hkv + 1), (OP_GU, F, n_gu, Hkv + 1, Hkv + 2),
+                                                   (OP_DOWN, H, n_down, Hkv + 2, Hkv + 3)), start=1):
             for i in range(T):
                 tasks.append(Task(op, layer, i, lo(i, R, T), lo(i + 1, R, T), ev(layer, wait), 0, ev(layer, sig), i,
-                                  i % workers))
+                                  place(k, i)))
     for i in range(n_lm):
         tasks.append(Task(OP_LM, 0, i, lo(i, V, n_lm), lo(i + 1, V, n_lm), ev(L - 1, Hkv + 3), 0, ev_lm, i,
-                          i % workers))
+                          place(4, i)))
     return {"split": S, "n_splits": NS, "fanin": fanin, "tasks": tasks}
 
 

@@ -28,11 +28,13 @@ def say(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def run_prompt_case(shape, batch, prompt_len, n_steps, mode=mk.MK_MODE_MEGAKERNEL, split=0, n_workers=0, seed=0):
+def run_prompt_case(shape, batch, prompt_len, n_steps, mode=mk.MK_MODE_MEGAKERNEL, split=0, n_workers=0, seed=0,
+                    schedule=None):
     weights = synth.make_weights(shape, seed=seed, device="cuda")
     seqs = synth.make_sequences(shape, batch, prompt_len, 0, seed=seed)
     max_seq = prompt_len - 1 + n_steps
-    eng = mk.Engine(shape, batch=batch, max_seq=max_seq, mode=mode, split=split, n_workers=n_workers)
+    eng = mk.Engine(shape, batch=batch, max_seq=max_seq, mode=mode, split=split, n_workers=n_workers,
+                    schedule=schedule)
     eng.load_weights(weights)
     eng.prefill(seqs["prompts"].numpy())
     toks, logits = eng.decode(n_steps)
@@ -73,6 +75,31 @@ def test_tiny_per_op_is_bit_identical_to_megakernel(n_workers, split):
     _, _, (t1, l1) = run_prompt_case(TINY, 1, 39, 32, mode=mk.MK_MODE_PER_OP, split=split, n_workers=n_workers)
     assert np.array_equal(t0, t1)
     assert np.array_equal(l0.view(np.uint32), l1.view(np.uint32))
+
+
+# A schedule moves tiles between workers and changes their sizes; every row's sum and every attention
+# split is computed the same way wherever it runs, so the results are bit-identical to the plain
+# schedule's, in both modes.
+SCHEDULES = [
+    (1, 0, 0, dict(rotate=1, attn_offset=3)),
+    (1, 8, 0, dict(qkv_tiles=3, wo_tiles=5, gu_tiles=7, down_tiles=6, lm_tiles=4, rotate=5, attn_offset=2)),
+    (2, 37, 8, dict(qkv_tiles=7, wo_tiles=37, gu_tiles=20, down_tiles=11, lm_tiles=37, rotate=36, attn_offset=30)),
+    (4, 0, 0, dict(qkv_tiles=16, wo_tiles=128, gu_tiles=200, down_tiles=255, lm_tiles=64, rotate=77,
+                   attn_offset=129)),
+]
+
+
+@pytest.mark.parametrize("batch,n_workers,split,sched", SCHEDULES)
+def test_tiny_schedules_are_bit_identical(batch, n_workers, split, sched):
+    say(f"tiny schedule batch={batch} workers={n_workers} split={split} {sched}")
+    w, s, (t0, l0) = run_prompt_case(TINY, batch, 23, 24, split=split, n_workers=n_workers)
+    _, _, (t1, l1) = run_prompt_case(TINY, batch, 23, 24, split=split, n_workers=n_workers, schedule=sched)
+    _, _, (t2, l2) = run_prompt_case(TINY, batch, 23, 24, mode=mk.MK_MODE_PER_OP, split=split, n_workers=n_workers,
+                                     schedule=sched)
+    assert np.array_equal(t0, t1) and np.array_equal(t0, t2)
+    assert np.array_equal(l0.view(np.uint32), l1.view(np.uint32))
+    assert np.array_equal(l0.view(np.uint32), l2.view(np.uint32))
+    check_against_oracle(TINY, w, s, t1, l1, 24, "tiny scheduled")
 
 
 def test_tiny_megakernel_deterministic_and_resumable():

@@ -17,8 +17,48 @@ CASES = [
 ]
 
 
-def cfg_of(shape, B, max_seq, split):
-    return mk.make_cfg(shape, batch=B, max_seq=max_seq, split=split)
+def cfg_of(shape, B, max_seq, split, schedule=None):
+    return mk.make_cfg(shape, batch=B, max_seq=max_seq, split=split, schedule=schedule)
+
+
+SPEC_ARGS = ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab")
+
+
+def spec_bytes(shape, B, max_seq, workers, split, **sched):
+    dims = [getattr(shape, a) for a in SPEC_ARGS]
+    return canonical_bytes(spec_graph(*dims, B, max_seq, workers, split, **sched), workers)
+
+
+# schedules the offline search may give: tile counts below and at the worker count, rotations,
+# attention offsets (some wrap past the worker count)
+SCHEDULE_CASES = [
+    (LLAMA8B, 1, 550, 256, 0, dict(rotate=1)),
+    (LLAMA8B, 1, 550, 256, 0, dict(rotate=37, attn_offset=100)),
+    (LLAMA8B, 1, 550, 256, 40, dict(qkv_tiles=16, wo_tiles=128, gu_tiles=200, down_tiles=255, lm_tiles=64)),
+    (LLAMA8B, 4, 1088, 256, 0, dict(wo_tiles=192, rotate=64, attn_offset=300)),
+    (LLAMA8B, 16, 1088, 256, 0, dict(gu_tiles=256, down_tiles=128, rotate=3, attn_offset=7)),
+    (TINY, 2, 40, 37, 0, dict(qkv_tiles=5, wo_tiles=30, rotate=36, attn_offset=36)),
+    (CHAMELEON7B, 1, 4224, 256, 0, dict(qkv_tiles=6, rotate=128, attn_offset=1)),
+]
+
+
+@pytest.mark.parametrize("shape,B,max_seq,workers,split,sched", SCHEDULE_CASES)
+def test_given_schedule_bytes_equal_spec(shape, B, max_seq, workers, split, sched):
+    got = mk.mk_build_graph(cfg_of(shape, B, max_seq, split, sched), workers)
+    assert got == spec_bytes(shape, B, max_seq, workers, split, **sched)
+
+
+def test_given_schedule_of_zeros_is_the_plain_rule():
+    for shape, B, max_seq, workers, split in CASES[:6]:
+        assert mk.mk_build_graph(cfg_of(shape, B, max_seq, split, {}), workers) == \
+            spec_bytes(shape, B, max_seq, workers, split)
+
+
+@pytest.mark.parametrize("bad", [dict(wo_tiles=257), dict(lm_tiles=-1), dict(rotate=-3), dict(qkv_tiles=33)])
+def test_given_schedule_rejects_bad_fields(bad):
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_build_graph(cfg_of(LLAMA8B, 1, 550, 0, bad), 256)
+    assert e.value.code == mk.MK_ERR_INVALID_ARG or e.value.code == mk.MK_ERR_UNSUPPORTED
 
 
 def parse(raw: bytes):
