@@ -93,6 +93,31 @@ void orc_matvec(const uint16_t* W, int rows, int cols, const double* x, double* 
 }
 
 /* ------------------------------------------------------------------ */
+/* LoRA-adapted linear layer (Mirage article, "Case 2: LoRA + Linear"): */
+/* y = W x + B (A x), taken in the concatenated form the article gives, */
+/* (W|B) times (x|A x).  The low-rank projection u = A x is summed in   */
+/* fp64 and materialised as fp32 (the second half of the concatenated   */
+/* operand); each output row is then one sequential fp64 sum over its   */
+/* concatenated row: the cols products of W with x, followed by the r   */
+/* products of B with u.                                                */
+/* ------------------------------------------------------------------ */
+void orc_lora_linear(const uint16_t* W, const uint16_t* A, const uint16_t* B, int rows, int cols, int r,
+                     const double* x, double* y, int n_threads) {
+  orc_matvec(W, rows, cols, x, y, n_threads);
+  if (!A || !B || r <= 0) return;
+  double* ud = (double*)malloc(sizeof(double) * r);
+  matvec_rows(A, 0, r, cols, x, ud);
+  for (int j = 0; j < r; ++j) ud[j] = (double)(float)ud[j];
+  for (int i = 0; i < rows; ++i) {
+    const uint16_t* b = B + (size_t)i * r;
+    double a = y[i];
+    for (int j = 0; j < r; ++j) a += (double)orc_bf16_to_f32(b[j]) * ud[j];
+    y[i] = a;
+  }
+  free(ud);
+}
+
+/* ------------------------------------------------------------------ */
 /* RMSNorm (Mirage article, "Case 1": the norm divides x by the root   */
 /* mean square; the weight gamma scales each element), in fp64:        */
 /*   y_i = x_i * (1 / sqrt(mean(x^2) + eps)) * gamma_i                 */
@@ -179,13 +204,31 @@ struct orc_seq {
 
 static int per_layer(const orc_cfg* c) { return 9 + (c->qk_norm ? 2 : 0); }
 
-int orc_n_weights(const orc_cfg* c) { return 1 + c->n_layers * per_layer(c) + 2; }
+static int n_base(const orc_cfg* c) { return 1 + c->n_layers * per_layer(c) + 2; }
+enum { LORA_PER_LAYER = 14 }; /* lora_a and lora_b of q, k, v, o, gate, up, down */
+
+int orc_n_weights(const orc_cfg* c) { return n_base(c) + (c->lora_rank > 0 ? c->n_layers * LORA_PER_LAYER : 0); }
+
+/* input and output width of adapter target t (q, k, v, o, gate, up, down) */
+static void lora_dims(const orc_cfg* c, int t, int64_t* in, int64_t* out) {
+  const int64_t H = c->hidden, QD = (int64_t)c->n_q_heads * c->head_dim, KD = (int64_t)c->n_kv_heads * c->head_dim;
+  const int64_t F = c->ffn;
+  const int64_t ins[7] = {H, H, H, QD, H, H, F}, outs[7] = {QD, KD, KD, H, F, F, H};
+  *in = ins[t];
+  *out = outs[t];
+}
 
 int64_t orc_weight_numel(const orc_cfg* c, int i) {
   int64_t H = c->hidden, QD = (int64_t)c->n_q_heads * c->head_dim, KD = (int64_t)c->n_kv_heads * c->head_dim;
   int64_t F = c->ffn, Vv = c->vocab, D = c->head_dim;
-  int n = orc_n_weights(c);
-  if (i < 0 || i >= n) return -1;
+  int n = n_base(c);
+  if (i < 0 || i >= orc_n_weights(c)) return -1;
+  if (i >= n) { /* LoRA adapters */
+    const int j = (i - n) % LORA_PER_LAYER;
+    int64_t in, out;
+    lora_dims(c, j / 2, &in, &out);
+    return (int64_t)c->lora_rank * (j % 2 ? out : in);
+  }
   if (i == 0) return Vv * H;           /* embed */
   if (i == n - 2) return H;            /* final_norm */
   if (i == n - 1) return Vv * H;       /* lm_head */
@@ -277,9 +320,13 @@ int orc_seq_step(orc_seq* s, int token, float* logits) {
   /* embedding lookup */
   for (int i = 0; i < H; ++i) x[i] = orc_bf16_to_f32(W[0][(size_t)token * H + i]);
 
-  const int pl = per_layer(c);
+  const int pl = per_layer(c), r = c->lora_rank;
   for (int l = 0; l < c->n_layers; ++l) {
     const uint16_t* const* Lw = W + 1 + l * pl;
+    /* adapter t of this layer: A = La[2 t], B = La[2 t + 1] (none without LoRA) */
+    const uint16_t* const* La = r > 0 ? W + n_base(c) + l * LORA_PER_LAYER : NULL;
+#define LA(t) (La ? La[2 * (t)] : NULL)
+#define LB(t) (La ? La[2 * (t) + 1] : NULL)
     const uint16_t *attn_norm = Lw[0], *wq = Lw[1], *wk = Lw[2], *wv = Lw[3], *wo = Lw[4];
     const uint16_t *q_norm = c->qk_norm ? Lw[5] : NULL, *k_norm = c->qk_norm ? Lw[6] : NULL;
     const int b = c->qk_norm ? 7 : 5;
@@ -287,11 +334,11 @@ int orc_seq_step(orc_seq* s, int token, float* logits) {
 
     /* attention sublayer: q, k, v stored in fp32 */
     orc_rmsnorm(x, attn_norm, H, c->rms_eps, h);
-    orc_matvec(wq, QD, H, h, y, nt);
+    orc_lora_linear(wq, LA(0), LB(0), QD, H, r, h, y, nt);
     for (int i = 0; i < QD; ++i) q[i] = (float)y[i];
-    orc_matvec(wk, KD, H, h, y, nt);
+    orc_lora_linear(wk, LA(1), LB(1), KD, H, r, h, y, nt);
     for (int i = 0; i < KD; ++i) k[i] = (float)y[i];
-    orc_matvec(wv, KD, H, h, y, nt);
+    orc_lora_linear(wv, LA(2), LB(2), KD, H, r, h, y, nt);
     for (int i = 0; i < KD; ++i) v[i] = (float)y[i];
     /* per-head QK-norm and RoPE in fp64 */
     for (int hh = 0; hh < Hq; ++hh) {
@@ -316,21 +363,23 @@ int orc_seq_step(orc_seq* s, int token, float* logits) {
       orc_attend(qh + hh * D, Kl + g * D, Vl + g * D, pos + 1, D, KD, o + hh * D);
     }
     for (int i = 0; i < QD; ++i) qh[i] = (double)o[i];
-    orc_matvec(wo, H, QD, qh, y, nt);
+    orc_lora_linear(wo, LA(3), LB(3), H, QD, r, qh, y, nt);
     for (int i = 0; i < H; ++i) x[i] = (float)((double)x[i] + y[i]);
 
     /* MLP sublayer */
     orc_rmsnorm(x, ffn_norm, H, c->rms_eps, h);
-    orc_matvec(wg, F, H, h, gt, nt);
-    orc_matvec(wu, F, H, h, up, nt);
+    orc_lora_linear(wg, LA(4), LB(4), F, H, r, h, gt, nt);
+    orc_lora_linear(wu, LA(5), LB(5), F, H, r, h, up, nt);
     for (int i = 0; i < F; ++i) a[i] = (float)(orc_silu(gt[i]) * up[i]);
     for (int i = 0; i < F; ++i) h[i] = (double)a[i];
-    orc_matvec(wd, H, F, h, y, nt);
+    orc_lora_linear(wd, LA(6), LB(6), H, F, r, h, y, nt);
     for (int i = 0; i < H; ++i) x[i] = (float)((double)x[i] + y[i]);
+#undef LA
+#undef LB
   }
 
   if (logits) {
-    const int n = orc_n_weights(c);
+    const int n = n_base(c);
     double* lg = (double*)malloc(sizeof(double) * c->vocab);
     orc_rmsnorm(x, W[n - 2], H, c->rms_eps, h);
     orc_matvec(W[n - 1], c->vocab, H, h, lg, nt);

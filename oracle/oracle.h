@@ -37,12 +37,15 @@ typedef struct {
   int qk_norm;   /* 1: per-head RMSNorm of q and k before RoPE */
   int max_seq;   /* KV capacity in positions */
   int n_threads; /* >1 splits independent output rows across threads; results are identical */
+  int lora_rank; /* r > 0: a LoRA adapter (A [r][in], B [out][r]) on every projection of every layer */
 } orc_cfg;
 
 typedef struct orc_model orc_model;
 typedef struct orc_seq orc_seq;
 
-/* Number of weight tensors in canonical order for this config. */
+/* Number of weight tensors in canonical order for this config.  With lora_rank > 0 the base
+ * tensors are followed, per layer, by lora_a and lora_b of q, k, v, o, gate, up, down in that
+ * order (14 tensors per layer). */
 int orc_n_weights(const orc_cfg* cfg);
 /* Element count of canonical tensor i. */
 int64_t orc_weight_numel(const orc_cfg* cfg, int i);
@@ -67,6 +70,11 @@ float orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16(float f);
 /* y[r] = sum_k W[r][k] * x[k] in fp64, W bf16 [rows][cols] */
 void orc_matvec(const uint16_t* W, int rows, int cols, const double* x, double* y, int n_threads);
+/* y = W x + B (A x), W bf16 [rows][cols], A bf16 [r][cols], B bf16 [rows][r]: u = A x in fp64
+ * stored as fp32, then each row one sequential fp64 sum over the concatenated row (W|B) against
+ * (x|u).  A == NULL or B == NULL or r == 0: y = W x exactly as orc_matvec. */
+void orc_lora_linear(const uint16_t* W, const uint16_t* A, const uint16_t* B, int rows, int cols, int r,
+                     const double* x, double* y, int n_threads);
 /* y = x * (1/sqrt(mean(x^2)+eps)) * gamma, in fp64 */
 void orc_rmsnorm(const float* x, const uint16_t* gamma, int n, float eps, double* y);
 /* rotate-half RoPE of one head vector of length d at position pos, in place, fp64 */

@@ -17,7 +17,8 @@ _lib = None
 class OrcCfg(C.Structure):
     _fields_ = [("n_layers", C.c_int), ("hidden", C.c_int), ("n_q_heads", C.c_int), ("n_kv_heads", C.c_int),
                 ("head_dim", C.c_int), ("ffn", C.c_int), ("vocab", C.c_int), ("rms_eps", C.c_float),
-                ("rope_theta", C.c_double), ("qk_norm", C.c_int), ("max_seq", C.c_int), ("n_threads", C.c_int)]
+                ("rope_theta", C.c_double), ("qk_norm", C.c_int), ("max_seq", C.c_int), ("n_threads", C.c_int),
+                ("lora_rank", C.c_int)]
 
 
 def lib():
@@ -42,6 +43,7 @@ def lib():
         L.orc_f32_to_bf16.argtypes = [C.c_float]
         L.orc_f32_to_bf16.restype = C.c_uint16
         L.orc_matvec.argtypes = [u16p, C.c_int, C.c_int, f64p, f64p, C.c_int]
+        L.orc_lora_linear.argtypes = [u16p, u16p, u16p, C.c_int, C.c_int, C.c_int, f64p, f64p, C.c_int]
         L.orc_rmsnorm.argtypes = [f32p, u16p, C.c_int, C.c_float, f64p]
         L.orc_rope.argtypes = [f64p, C.c_int, C.c_int, C.c_double]
         L.orc_attend.argtypes = [f64p, u16p, u16p, C.c_int, C.c_int, C.c_int, f32p]
@@ -83,6 +85,22 @@ def matvec(W16: np.ndarray, x: np.ndarray, n_threads: int = 1) -> np.ndarray:
     x, xp = _f64(x)
     y = np.zeros(rows, np.float64)
     lib().orc_matvec(wp, rows, cols, xp, y.ctypes.data_as(C.POINTER(C.c_double)), n_threads)
+    return y
+
+
+def lora_linear(W16: np.ndarray, A16: np.ndarray | None, B16: np.ndarray | None, x: np.ndarray,
+                n_threads: int = 1) -> np.ndarray:
+    """fp64 W @ x + B @ fp32(A @ x), one sequential sum per concatenated row."""
+    rows, cols = W16.shape
+    r = 0 if A16 is None else A16.shape[0]
+    W16, wp = _u16(W16)
+    ap = bp = None
+    if A16 is not None:
+        A16, ap = _u16(A16)
+        B16, bp = _u16(B16)
+    x, xp = _f64(x)
+    y = np.zeros(rows, np.float64)
+    lib().orc_lora_linear(wp, ap, bp, rows, cols, r, xp, y.ctypes.data_as(C.POINTER(C.c_double)), n_threads)
     return y
 
 
@@ -129,7 +147,7 @@ class Oracle:
     def __init__(self, shape, weights16: list[np.ndarray], max_seq: int, n_seq: int = 1, n_threads: int = 1):
         self.cfg = OrcCfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                           shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta, int(shape.qk_norm), max_seq,
-                          n_threads)
+                          n_threads, int(getattr(shape, "lora_rank", 0)))
         L = lib()
         n = L.orc_n_weights(C.byref(self.cfg))
         if n != len(weights16):

@@ -22,6 +22,7 @@ class ModelShape:
     rms_eps: float = 1e-5
     rope_theta: float = 10000.0
     qk_norm: bool = False
+    lora_rank: int = 0  # > 0: a LoRA adapter of this rank on every projection of every layer
 
 
 @dataclass(frozen=True)

@@ -6,6 +6,9 @@ sides of every parity check read the very same arrays.
 
 * Weights: N(0, 0.02) drawn in fp32 and rounded to bf16; every RMSNorm gamma
   is 1.  One generator seeded with `seed` draws the tensors in canonical order.
+  LoRA adapters (shapes with lora_rank > 0) follow the base tensors, per layer
+  lora_a then lora_b of q, k, v, o, gate, up, down, drawn the same way (both
+  non-zero, so that the adapters change every projection).
 * Prompts, pending tokens and pre-filled K/V: a second generator seeded with
   `seed + 1`, drawn per sequence in the order prompt, then per layer K then V,
   then the pending token.  Pre-filled K/V are N(0, 1) rounded to bf16 and
@@ -29,13 +32,25 @@ def canonical_names(m: ModelShape) -> list[str]:
             names += [p + "q_norm", p + "k_norm"]
         names += [p + "ffn_norm", p + "w_gate", p + "w_up", p + "w_down"]
     names += ["final_norm", "lm_head"]
+    if getattr(m, "lora_rank", 0) > 0:
+        for layer in range(m.n_layers):
+            for t in LORA_TARGETS:
+                names += [f"layers.{layer}.lora_a.{t}", f"layers.{layer}.lora_b.{t}"]
     return names
+
+
+LORA_TARGETS = ("q", "k", "v", "o", "gate", "up", "down")
 
 
 def canonical_shape(m: ModelShape, name: str) -> tuple[int, ...]:
     H, D, F, V = m.hidden, m.head_dim, m.ffn, m.vocab
     QD, KD = m.n_q_heads * D, m.n_kv_heads * D
-    base = name.split(".")[-1]
+    parts = name.split(".")
+    if len(parts) == 4 and parts[2] in ("lora_a", "lora_b"):
+        fan_in, fan_out = {"q": (H, QD), "k": (H, KD), "v": (H, KD), "o": (QD, H), "gate": (H, F), "up": (H, F),
+                           "down": (F, H)}[parts[3]]
+        return (m.lora_rank, fan_in) if parts[2] == "lora_a" else (fan_out, m.lora_rank)
+    base = parts[-1]
     return {
         "embed": (V, H), "lm_head": (V, H), "final_norm": (H,),
         "attn_norm": (H,), "ffn_norm": (H,), "q_norm": (D,), "k_norm": (D,),

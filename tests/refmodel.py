@@ -55,12 +55,21 @@ def forward_logits(shape, w: dict, tokens, kv_prefix=None, store32=False):
     P = 0 if kv_prefix is None else kv_prefix[0].shape[1]
     pos = np.arange(P, P + T)
     x = w["embed"][np.asarray(tokens)]
+    lora = getattr(shape, "lora_rank", 0) > 0
     for layer in range(shape.n_layers):
         p = f"layers.{layer}."
+
+        def lin(h, wname, t):
+            # a linear layer, plus its LoRA update B (A h) with A h materialised (fp32 under store32)
+            y = h @ w[p + wname].T
+            if lora:
+                y = y + st(h @ w[p + "lora_a." + t].T) @ w[p + "lora_b." + t].T
+            return y
+
         h = rms(x, w[p + "attn_norm"], eps)
-        q = st(h @ w[p + "wq"].T).reshape(T, Hq, D).transpose(1, 0, 2)
-        k = st(h @ w[p + "wk"].T).reshape(T, Hkv, D).transpose(1, 0, 2)
-        v = st(h @ w[p + "wv"].T).reshape(T, Hkv, D).transpose(1, 0, 2)
+        q = st(lin(h, "wq", "q")).reshape(T, Hq, D).transpose(1, 0, 2)
+        k = st(lin(h, "wk", "k")).reshape(T, Hkv, D).transpose(1, 0, 2)
+        v = st(lin(h, "wv", "v")).reshape(T, Hkv, D).transpose(1, 0, 2)
         if shape.qk_norm:
             q = rms(q, w[p + "q_norm"], eps)
             k = rms(k, w[p + "k_norm"], eps)
@@ -82,9 +91,9 @@ def forward_logits(shape, w: dict, tokens, kv_prefix=None, store32=False):
             s = s - s.max(axis=1, keepdims=True)
             e = np.exp(s)
             o[hh] = st((e @ v[g]) / e.sum(axis=1, keepdims=True))
-        x = st(x + o.transpose(1, 0, 2).reshape(T, Hq * D) @ w[p + "wo"].T)
+        x = st(x + lin(o.transpose(1, 0, 2).reshape(T, Hq * D), "wo", "o"))
         h2 = rms(x, w[p + "ffn_norm"], eps)
-        gt = h2 @ w[p + "w_gate"].T
-        up = h2 @ w[p + "w_up"].T
-        x = st(x + st(gt / (1.0 + np.exp(-gt)) * up) @ w[p + "w_down"].T)
+        gt = lin(h2, "w_gate", "gate")
+        up = lin(h2, "w_up", "up")
+        x = st(x + lin(st(gt / (1.0 + np.exp(-gt)) * up), "w_down", "down"))
     return st(rms(x, w["final_norm"], eps) @ w["lm_head"].T)

@@ -232,6 +232,10 @@ SHAPES = {
                                   vocab=512, qk_norm=True),
     "tiny_g4": ModelShape(n_layers=1, hidden=128, n_q_heads=8, n_kv_heads=2, head_dim=32, ffn=200, vocab=300,
                           rope_theta=500000.0),
+    "tiny_lora": ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=688, vocab=512,
+                            lora_rank=8),
+    "tiny_lora_qknorm": ModelShape(n_layers=1, hidden=128, n_q_heads=4, n_kv_heads=4, head_dim=32, ffn=200,
+                                   vocab=300, qk_norm=True, lora_rank=16),
 }
 
 
@@ -300,3 +304,62 @@ def test_cache_capacity_and_token_range_errors():
     orc.step(0, 2, want_logits=False)
     with pytest.raises(ValueError):
         orc.step(0, 3)
+
+
+# ---------------------------------------------------------------- LoRA + Linear
+# Mirage article, "Case 2: LoRA + Linear": W x + B A x = (W|B)(x|A x).
+def _lora_operands(rows, cols, r, seed):
+    rng = np.random.default_rng(seed)
+    W = bits(rng.standard_normal((rows, cols)) * 0.05)
+    A = bits(rng.standard_normal((r, cols)) * 0.05)
+    B = bits(rng.standard_normal((rows, r)) * 0.05)
+    x = rng.standard_normal(cols)
+    return W, A, B, x
+
+
+@pytest.mark.parametrize("rows,cols,r", [(7, 300, 1), (33, 129, 8), (64, 512, 16)])
+def test_lora_linear_is_the_concatenated_product(rows, cols, r):
+    # the article's identity, with the concatenations made explicit: the plain (pinned) matvec of
+    # [W | B] against [x | A x], A x materialised in fp32, gives the same bits
+    W, A, B, x = _lora_operands(rows, cols, r, seed=rows + cols)
+    u = po.matvec(A, x).astype(np.float32).astype(np.float64)
+    ref = po.matvec(np.concatenate([W, B], axis=1), np.concatenate([x, u]))
+    got = po.lora_linear(W, A, B, x)
+    assert np.array_equal(got, ref)
+
+
+def test_lora_linear_with_a_zero_adapter_is_the_plain_linear():
+    W, A, B, x = _lora_operands(40, 256, 8, seed=3)
+    plain = po.matvec(W, x)
+    assert np.array_equal(po.lora_linear(W, A, np.zeros_like(B), x), plain)
+    assert np.array_equal(po.lora_linear(W, np.zeros_like(A), B, x), plain)
+    assert np.array_equal(po.lora_linear(W, None, None, x), plain)
+
+
+def test_lora_linear_within_float64_bound_of_the_merged_weight():
+    # (W + B A) x in float64 with A x exact: differs from the oracle only by the fp32 rounding of A x
+    # (|u| 2^-24 relative, carried through B) and fp64 summation error
+    W, A, B, x = _lora_operands(50, 400, 16, seed=5)
+    Wf, Af, Bf = (bf16_bits_to_f64(a) for a in (W, A, B))
+    ref = (Wf + Bf @ Af) @ x
+    u = Af @ x
+    bound = np.abs(Bf) @ (np.abs(u) * 2.0 ** -24) + 1e-12 * (np.abs(Wf) @ np.abs(x) + np.abs(Bf) @ np.abs(u))
+    got = po.lora_linear(W, A, B, x)
+    assert np.all(np.abs(got - ref) <= bound)
+    assert np.abs(got - po.matvec(W, x)).max() > 1e-3   # the adapter is not a no-op here
+
+
+def test_lora_decoder_with_zero_b_equals_the_base_decoder():
+    # B = 0 on every adapter: the LoRA decoder's logits are bit-identical to the base model's
+    shape = SHAPES["tiny_lora"]
+    base = ModelShape(**{**shape.__dict__, "lora_rank": 0})
+    w16, _ = _weights(shape, seed=17)
+    names = synth.canonical_names(shape)
+    for i, n in enumerate(names):
+        if ".lora_b." in n:
+            w16[i] = np.zeros_like(w16[i])
+    n_base = len(synth.canonical_names(base))
+    tokens = np.random.default_rng(18).integers(0, shape.vocab, 6)
+    a, b = po.Oracle(shape, w16, max_seq=8), po.Oracle(base, w16[:n_base], max_seq=8)
+    for t in tokens:
+        assert np.array_equal(a.step(0, int(t)), b.step(0, int(t)))
