@@ -87,6 +87,12 @@ typedef struct mk_model_cfg {
                          gate/up 2, down 3; LM head 4) runs on worker
                          (i + k * rotate) mod workers                        */
   int32_t attn_offset; /* attention task k runs on worker (k + attn_offset) mod workers */
+  /* LoRA (Mirage article, "Case 2: LoRA + Linear"): rank r of an adapter
+   * on every projection of every layer (q, k, v, o, gate, up, down), each
+   * y = W x + B (A x) computed as one fused GEMV over the concatenation
+   * (W|B)(x|A x).  0: no adapters; else a multiple of 8 up to 64, batch
+   * <= 4 (UNSUPPORTED otherwise). */
+  int32_t lora_rank;
 } mk_model_cfg;
 
 typedef struct mk_ctx mk_ctx;
@@ -97,6 +103,9 @@ typedef struct mk_ctx mk_ctx;
  *   "wo" [H,Hq*D], ("q_norm" [D], "k_norm" [D] when qk_norm),
  *   "ffn_norm" [H], "w_gate" [F,H], "w_up" [F,H], "w_down" [H,F];
  *   "final_norm" [H], "lm_head" [V,H].
+ * With lora_rank r > 0, also per layer "lora_a.<t>" [r,in] and
+ *   "lora_b.<t>" [out,r] for t in q, k, v, o, gate, up, down (in and out
+ *   being the projection's input and output widths).
  * Matrices are [out, in] row-major.  data is a host pointer, or a device
  * pointer when on_device != 0. */
 typedef struct mk_tensor {

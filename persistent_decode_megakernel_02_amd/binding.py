@@ -40,7 +40,7 @@ class MkModelCfg(C.Structure):
                 ("mode", C.c_int32), ("split", C.c_int32), ("n_workers", C.c_int32), ("watchdog_polls", C.c_uint32),
                 ("stream", C.c_void_p), ("schedule", C.c_int32), ("qkv_tiles", C.c_int32), ("wo_tiles", C.c_int32),
                 ("gu_tiles", C.c_int32), ("down_tiles", C.c_int32), ("lm_tiles", C.c_int32), ("rotate", C.c_int32),
-                ("attn_offset", C.c_int32)]
+                ("attn_offset", C.c_int32), ("lora_rank", C.c_int32)]
 
 
 class MkTensor(C.Structure):
@@ -106,6 +106,7 @@ def make_cfg(shape, batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, sp
     cfg = MkModelCfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
                      shape.vocab, shape.rms_eps, shape.rope_theta, int(shape.qk_norm), batch, max_seq, mode, split,
                      n_workers, watchdog_polls, stream)
+    cfg.lora_rank = int(getattr(shape, "lora_rank", 0))
     if schedule is not None:
         unknown = set(schedule) - set(SCHEDULE_FIELDS)
         _need(not unknown, f"unknown schedule fields {sorted(unknown)}")

@@ -50,6 +50,7 @@ TINY = ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64
                   rope_theta=10000.0)
 LLAMA8B = ModelShape(n_layers=32, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=14336,
                      vocab=128256, rope_theta=500000.0)
+LLAMA8B_LORA16 = replace(LLAMA8B, lora_rank=16)
 CHAMELEON7B = ModelShape(n_layers=32, hidden=4096, n_q_heads=32, n_kv_heads=32, head_dim=128, ffn=11008,
                          vocab=65536, rope_theta=10000.0, qk_norm=True)
 
@@ -63,6 +64,9 @@ WORKLOADS = {
     "llama8b_b16_ctx1024": Workload("llama8b_b16_ctx1024", LLAMA8B, batch=16, prompt_len=0, kv_prefill=1024, n_steps=64),
     "chameleon7b_ctx4096": Workload("chameleon7b_ctx4096", CHAMELEON7B, batch=1, prompt_len=0, kv_prefill=4096,
                                     n_steps=128),
+    # the decode512 workload with a rank-16 LoRA adapter on every projection (Mirage article, "Case 2")
+    "llama8b_lora16_decode512": Workload("llama8b_lora16_decode512", LLAMA8B_LORA16, batch=1, prompt_len=39,
+                                         kv_prefill=0, n_steps=512),
 }
 
 
@@ -71,9 +75,14 @@ def small_variant(w: Workload, **kw) -> Workload:
 
 
 def weight_bytes(m: ModelShape) -> int:
-    """bf16 bytes of every weight read in one decode step (one embedding row)."""
+    """bf16 bytes of every weight read in one decode step (one embedding row), adapters included."""
     H, D = m.hidden, m.head_dim
     per_layer = ((m.n_q_heads + 2 * m.n_kv_heads) * D * H + H * m.n_q_heads * D + 3 * m.ffn * H) * 2
+    if m.lora_rank:  # A [r][in] and B [out][r] of q, k, v, o, gate, up, down
+        QD, KD, F = m.n_q_heads * D, m.n_kv_heads * D, m.ffn
+        ins = 3 * H + QD + 2 * H + F
+        outs = QD + 2 * KD + H + 2 * F + H
+        per_layer += m.lora_rank * (ins + outs) * 2
     norms = (2 * H + (2 * D if m.qk_norm else 0)) * 2
     return m.n_layers * (per_layer + norms) + (m.vocab * H + H + H) * 2
 

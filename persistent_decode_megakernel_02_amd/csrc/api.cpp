@@ -66,6 +66,7 @@ struct mk_ctx {
   TV *part_ml = nullptr, *part_acc = nullptr;
   size_t n_part_ml = 0, n_part_acc = 0;
   LmPart* lm_part = nullptr;
+  float* lora_u = nullptr;  // [4][B][3 r] adapter A x of the current GEMV operator (LoRA)
   int32_t* pending = nullptr;
   int32_t* force = nullptr;
   size_t force_cap = 0;
@@ -123,6 +124,7 @@ static std::string validate(const mk_model_cfg& cfg) {
   if (cfg.head_dim != 64 && cfg.head_dim != 128) return "head_dim must be 64 or 128";
   if (cfg.mode != MK_MODE_MEGAKERNEL && cfg.mode != MK_MODE_PER_OP) return "unknown mode";
   if (!(cfg.rms_eps > 0.f) || !(cfg.rope_theta > 0.0)) return "rms_eps and rope_theta must be positive";
+  if (cfg.lora_rank < 0 || cfg.lora_rank > 64 || cfg.lora_rank % 8) return "lora_rank must be 0 or a multiple of 8 up to 64";
   return "";
 }
 
@@ -141,8 +143,12 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
   const int64_t att_bytes = (int64_t)(G + 2) * D * 4 + (int64_t)G * D * 8 + 2 * D * 2 + (int64_t)G * ((S + 1) & ~1) * 8 +
                             (int64_t)S * D * 2 + std::max<int64_t>(4 * 512, merge_doubles) * 8;
   auto maxrows = [](int R, int T) { return (R + T - 1) / T; };
-  const int worst = std::max({maxrows(cfg.hidden, g.n_wo), maxrows(cfg.ffn, g.n_gu) * 2, maxrows(cfg.hidden, g.n_down),
-                              maxrows(cfg.vocab, g.n_lm), (G + 2) * D / g.qkv_tiles_per_group + 1});
+  // with LoRA a tile also sums up to ceil(A rows / tiles) adapter rows (row pairs at gate/up)
+  const int lr = cfg.lora_rank;
+  const int worst = std::max({maxrows(cfg.hidden, g.n_wo) + maxrows(lr, g.n_wo),
+                              (maxrows(cfg.ffn, g.n_gu) + maxrows(lr, g.n_gu)) * 2,
+                              maxrows(cfg.hidden, g.n_down) + maxrows(lr, g.n_down), maxrows(cfg.vocab, g.n_lm),
+                              (G + 2) * D / g.qkv_tiles_per_group + 1 + maxrows(3 * lr, g.n_qkv)});
   LdsPlan L;
   L.mk_ks = 0;
   if (B >= 8) {
@@ -232,6 +238,8 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if (noalloc_token_staging(c->device, &c->noalloc_tokens) != hipSuccess)
     return bail(fail(c, MK_ERR_HIP, "hipGetSymbolAddress of the static token staging array failed"));
   int nw = cfg.n_workers > 0 ? cfg.n_workers : prop.multiProcessorCount;
+  if (cfg.lora_rank > 0 && cfg.batch >= 8)
+    return bail(fail(c, MK_ERR_UNSUPPORTED, "LoRA adapters run on the batch <= 4 GEMV path only"));
   why = build_graph(cfg, nw, &c->g);
   if (!why.empty()) return bail(fail(c, MK_ERR_UNSUPPORTED, why));
   LdsPlan lp{};
@@ -257,18 +265,29 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
     off += (elems * 2 + 255) / 256 * 128;  // elems of bf16, rounded to 256 bytes
     return o;
   };
-  std::vector<size_t> lo(L * 9);
+  // With LoRA (rank r), each weight matrix is followed by its adapters' A rows (wqkv: A_q, A_k,
+  // A_v), so that a GEMV tile streams its A rows exactly like its weight rows; the B matrices
+  // [rows][r] have their own slots (b_qkv with rows in wqkv's grouped order).
+  const size_t r = (size_t)cfg.lora_rank;
+  std::vector<size_t> lo(L * 14);
   const size_t o_embed = take((size_t)V * H);
   for (int l = 0; l < L; ++l) {
-    lo[l * 9 + 0] = take(QKVR * H);
-    lo[l * 9 + 1] = take((size_t)H * QD);
-    lo[l * 9 + 2] = take((size_t)F * H);
-    lo[l * 9 + 3] = take((size_t)F * H);
-    lo[l * 9 + 4] = take((size_t)H * F);
-    lo[l * 9 + 5] = take(H);
-    lo[l * 9 + 6] = take(H);
-    lo[l * 9 + 7] = take(D);
-    lo[l * 9 + 8] = take(D);
+    lo[l * 14 + 0] = take(QKVR * H + 3 * r * H);
+    lo[l * 14 + 1] = take((size_t)H * QD + r * QD);
+    lo[l * 14 + 2] = take((size_t)F * H + r * H);
+    lo[l * 14 + 3] = take((size_t)F * H + r * H);
+    lo[l * 14 + 4] = take((size_t)H * F + r * F);
+    lo[l * 14 + 5] = take(H);
+    lo[l * 14 + 6] = take(H);
+    lo[l * 14 + 7] = take(D);
+    lo[l * 14 + 8] = take(D);
+    if (r) {
+      lo[l * 14 + 9] = take(QKVR * r);
+      lo[l * 14 + 10] = take((size_t)H * r);
+      lo[l * 14 + 11] = take((size_t)F * r);
+      lo[l * 14 + 12] = take((size_t)F * r);
+      lo[l * 14 + 13] = take((size_t)H * r);
+    }
   }
   const size_t o_fn = take(H), o_lm = take((size_t)V * H);
   c->wbytes = off * 2;
@@ -279,25 +298,44 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   c->h_layers.resize(L);
   for (int l = 0; l < L; ++l) {
     LayerW& w = c->h_layers[l];
-    w.wqkv = c->warena + lo[l * 9 + 0];
-    w.wo = c->warena + lo[l * 9 + 1];
-    w.wg = c->warena + lo[l * 9 + 2];
-    w.wu = c->warena + lo[l * 9 + 3];
-    w.wd = c->warena + lo[l * 9 + 4];
-    w.attn_norm = c->warena + lo[l * 9 + 5];
-    w.ffn_norm = c->warena + lo[l * 9 + 6];
-    w.q_norm = cfg.qk_norm ? c->warena + lo[l * 9 + 7] : nullptr;
-    w.k_norm = cfg.qk_norm ? c->warena + lo[l * 9 + 8] : nullptr;
+    const size_t* o = &lo[l * 14];
+    w.wqkv = c->warena + o[0];
+    w.wo = c->warena + o[1];
+    w.wg = c->warena + o[2];
+    w.wu = c->warena + o[3];
+    w.wd = c->warena + o[4];
+    w.attn_norm = c->warena + o[5];
+    w.ffn_norm = c->warena + o[6];
+    w.q_norm = cfg.qk_norm ? c->warena + o[7] : nullptr;
+    w.k_norm = cfg.qk_norm ? c->warena + o[8] : nullptr;
+    w.b_qkv = r ? c->warena + o[9] : nullptr;
+    w.b_o = r ? c->warena + o[10] : nullptr;
+    w.b_g = r ? c->warena + o[11] : nullptr;
+    w.b_u = r ? c->warena + o[12] : nullptr;
+    w.b_d = r ? c->warena + o[13] : nullptr;
     const std::string p = "layers." + std::to_string(l) + ".";
-    c->wslots[p + "wo"] = {lo[l * 9 + 1], (int64_t)H * QD};
-    c->wslots[p + "w_gate"] = {lo[l * 9 + 2], (int64_t)F * H};
-    c->wslots[p + "w_up"] = {lo[l * 9 + 3], (int64_t)F * H};
-    c->wslots[p + "w_down"] = {lo[l * 9 + 4], (int64_t)H * F};
-    c->wslots[p + "attn_norm"] = {lo[l * 9 + 5], H};
-    c->wslots[p + "ffn_norm"] = {lo[l * 9 + 6], H};
+    c->wslots[p + "wo"] = {o[1], (int64_t)H * QD};
+    c->wslots[p + "w_gate"] = {o[2], (int64_t)F * H};
+    c->wslots[p + "w_up"] = {o[3], (int64_t)F * H};
+    c->wslots[p + "w_down"] = {o[4], (int64_t)H * F};
+    c->wslots[p + "attn_norm"] = {o[5], H};
+    c->wslots[p + "ffn_norm"] = {o[6], H};
     if (cfg.qk_norm) {
-      c->wslots[p + "q_norm"] = {lo[l * 9 + 7], D};
-      c->wslots[p + "k_norm"] = {lo[l * 9 + 8], D};
+      c->wslots[p + "q_norm"] = {o[7], D};
+      c->wslots[p + "k_norm"] = {o[8], D};
+    }
+    if (r) {  // A rows after their weight matrix; B matrices in their own slots (b_qkv: regrouped at load)
+      c->wslots[p + "lora_a.q"] = {o[0] + QKVR * H, (int64_t)(r * H)};
+      c->wslots[p + "lora_a.k"] = {o[0] + QKVR * H + r * H, (int64_t)(r * H)};
+      c->wslots[p + "lora_a.v"] = {o[0] + QKVR * H + 2 * r * H, (int64_t)(r * H)};
+      c->wslots[p + "lora_a.o"] = {o[1] + (size_t)H * QD, (int64_t)(r * QD)};
+      c->wslots[p + "lora_a.gate"] = {o[2] + (size_t)F * H, (int64_t)(r * H)};
+      c->wslots[p + "lora_a.up"] = {o[3] + (size_t)F * H, (int64_t)(r * H)};
+      c->wslots[p + "lora_a.down"] = {o[4] + (size_t)H * F, (int64_t)(r * F)};
+      c->wslots[p + "lora_b.o"] = {o[10], (int64_t)(H * r)};
+      c->wslots[p + "lora_b.gate"] = {o[11], (int64_t)(F * r)};
+      c->wslots[p + "lora_b.up"] = {o[12], (int64_t)(F * r)};
+      c->wslots[p + "lora_b.down"] = {o[13], (int64_t)(H * r)};
     }
   }
   c->wslots["embed"] = {o_embed, (int64_t)V * H};
@@ -339,6 +377,7 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if ((rc = dalloc(c, (void**)&c->part_ml, c->n_part_ml * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->part_acc, c->n_part_acc * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->lm_part, (size_t)B * c->g.n_lm * sizeof(LmPart)))) return bail(rc);
+  if (r && (rc = dalloc(c, (void**)&c->lora_u, (size_t)4 * B * 3 * r * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->pending, (size_t)B * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->flags, (size_t)c->g.n_slots * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->status, 64))) return bail(rc);
@@ -442,7 +481,8 @@ int mk_load_weights(mk_ctx* c, const mk_tensor* t, int n) {
   const int G = Hq / Hkv;
   const size_t RG = (size_t)(G + 2) * D;
   std::map<std::string, int> seen;
-  const int expected = 1 + L * (9 + (cfg.qk_norm ? 2 : 0)) + 2;
+  const int lr = cfg.lora_rank;
+  const int expected = 1 + L * (9 + (cfg.qk_norm ? 2 : 0)) + 2 + (lr > 0 ? 14 * L : 0);
   for (int i = 0; i < n; ++i) {
     if (!t[i].name || !t[i].data) return fail(c, MK_ERR_INVALID_ARG, "tensor with null name or data");
     if (seen.count(t[i].name)) return fail(c, MK_ERR_INVALID_ARG, std::string("duplicate tensor ") + t[i].name);
@@ -462,16 +502,23 @@ int mk_load_weights(mk_ctx* c, const mk_tensor* t, int n) {
     // q/k/v: pack per KV-head group [G q heads | k | v]
     int l = -1;
     char which[16] = {0};
-    if (std::sscanf(name.c_str(), "layers.%d.%15s", &l, which) == 2 && l >= 0 && l < L &&
-        (!std::strcmp(which, "wq") || !std::strcmp(which, "wk") || !std::strcmp(which, "wv"))) {
-      const bool isq = which[1] == 'q';
+    // q/k/v weights and (LoRA) their B matrices: rows regrouped per KV-head group like wqkv
+    const bool scanned = std::sscanf(name.c_str(), "layers.%d.%15s", &l, which) == 2 && l >= 0 && l < L;
+    const bool is_w = scanned && (!std::strcmp(which, "wq") || !std::strcmp(which, "wk") || !std::strcmp(which, "wv"));
+    const bool is_b = scanned && lr > 0 &&
+                      (!std::strcmp(which, "lora_b.q") || !std::strcmp(which, "lora_b.k") || !std::strcmp(which, "lora_b.v"));
+    if (is_w || is_b) {
+      const char kind_c = is_w ? which[1] : which[7];  // q, k or v
+      const bool isq = kind_c == 'q';
       const int nh = isq ? Hq : Hkv;
-      if (t[i].numel != (int64_t)nh * D * H) return fail(c, MK_ERR_INVALID_ARG, "wrong numel for " + name);
-      uint16_t* dst0 = const_cast<uint16_t*>(c->h_layers[l].wqkv);
+      const size_t rowlen = is_w ? (size_t)H : (size_t)lr;
+      if (t[i].numel != (int64_t)nh * D * (int64_t)rowlen) return fail(c, MK_ERR_INVALID_ARG, "wrong numel for " + name);
+      uint16_t* dst0 = const_cast<uint16_t*>(is_w ? c->h_layers[l].wqkv : c->h_layers[l].b_qkv);
       for (int h = 0; h < nh; ++h) {
         const int grp = isq ? h / G : h;
-        const size_t row = grp * RG + (isq ? (size_t)(h % G) * D : (which[1] == 'k' ? (size_t)G * D : (size_t)(G + 1) * D));
-        HIPCHK(c, hipMemcpyAsync(dst0 + row * H, src + (size_t)h * D * H, (size_t)D * H * 2, kind, c->stream));
+        const size_t row = grp * RG + (isq ? (size_t)(h % G) * D : (kind_c == 'k' ? (size_t)G * D : (size_t)(G + 1) * D));
+        HIPCHK(c, hipMemcpyAsync(dst0 + row * rowlen, src + (size_t)h * D * rowlen, (size_t)D * rowlen * 2, kind,
+                                 c->stream));
       }
       continue;
     }
@@ -540,6 +587,8 @@ static KParams make_params(mk_ctx* c) {
   P.epoch = c->epoch;
   P.lm_skip = c->lm_skip;
   P.lm_part = c->lm_part;
+  P.lora_u = c->lora_u;
+  P.lora_r = cfg.lora_rank;
   P.pending = c->pending;
   P.flags = c->flags;
   P.events = c->d_events;
@@ -569,8 +618,11 @@ static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
       P.op_first = (int)g.op_ranges[r].first;
       P.op_count = (int)g.op_ranges[r].count;
       P.op_range = (int)r;
-      const bool attn = g.tasks[g.op_ranges[r].first].op == OP_ATTN;
-      HIPCHK(c, launch(attn ? 3 : 1, P, c->stream));
+      // cooperative where tasks of one launch wait on each other: attention mergers poll the other
+      // splits' partials, and with LoRA every GEMV tile waits for its operator's adapter rows
+      const uint32_t op = g.tasks[g.op_ranges[r].first].op;
+      const bool coop = op == OP_ATTN || (c->cfg.lora_rank > 0 && op != OP_LM);
+      HIPCHK(c, launch(coop ? 3 : 1, P, c->stream));
     }
   }
   if (with_lm) {

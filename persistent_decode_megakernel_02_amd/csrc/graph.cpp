@@ -126,7 +126,13 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   // split holding the current position merges everything and signals for its (sequence, head).
   const bool dist = (int64_t)g.n_splits * c.batch * Hkv <= n_workers;
 
-  // events: per layer [QKV group 0..Hkv-1, ATT, O, A, X], then LM
+  // LoRA: each GEMV operator of a layer spreads the A rows (units) of its adapters over its first
+  // tiles, q per tile; QKV 3r rows (A_q, A_k, A_v), WO r, GU r (A_gate, A_up row pairs), DOWN r.
+  const int lr = c.lora_rank;
+  if (lr < 0 || lr > 64 || lr % 8) return "lora_rank must be 0 or a multiple of 8 up to 64";
+
+  // events: per layer [QKV group 0..Hkv-1, ATT, O, A, X], then LM, then (LoRA) per layer the A-row
+  // events of QKV, WO, GU and DOWN
   const int per_layer = Hkv + 4;
   auto ev_qkv = [&](int l, int gg) { return (uint32_t)(l * per_layer + gg); };
   auto ev_att = [&](int l) { return (uint32_t)(l * per_layer + Hkv); };
@@ -134,7 +140,15 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   auto ev_a = [&](int l) { return (uint32_t)(l * per_layer + Hkv + 2); };
   auto ev_x = [&](int l) { return (uint32_t)(l * per_layer + Hkv + 3); };
   const uint32_t ev_lm = (uint32_t)(c.n_layers * per_layer);
-  g.events.resize(ev_lm + 1);
+  auto ev_lora = [&](int l, int k) { return ev_lm + 1u + (uint32_t)(4 * l + k); };
+  const int n_tiles[4] = {g.n_qkv, g.n_wo, g.n_gu, g.n_down};
+  const int n_arows[4] = {3 * lr, lr, lr, lr};
+  int per_tile[4] = {0, 0, 0, 0}, holders[4] = {0, 0, 0, 0};
+  for (int k = 0; k < 4 && lr > 0; ++k) {
+    per_tile[k] = (n_arows[k] + n_tiles[k] - 1) / n_tiles[k];
+    holders[k] = (n_arows[k] + per_tile[k] - 1) / per_tile[k];
+  }
+  g.events.resize(ev_lm + 1 + (lr > 0 ? 4 * c.n_layers : 0));
   for (int l = 0; l < c.n_layers; ++l) {
     for (int gg = 0; gg < Hkv; ++gg) g.events[ev_qkv(l, gg)].fanin = TG;
     g.events[ev_att(l)].fanin = dist ? g.n_splits * c.batch * Hkv : c.batch * Hkv;
@@ -143,6 +157,8 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
     g.events[ev_x(l)].fanin = g.n_down;
   }
   g.events[ev_lm].fanin = g.n_lm;
+  for (int l = 0; l < c.n_layers && lr > 0; ++l)
+    for (int k = 0; k < 4; ++k) g.events[ev_lora(l, k)].fanin = holders[k];
   uint32_t slot = 0;
   for (auto& e : g.events) {
     e.slot0 = slot;
@@ -154,6 +170,13 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
                   uint32_t sig_ev, uint32_t sig_slot, uint32_t cu) {
     TaskRec t;
     std::memset(&t, 0, sizeof t);
+    t.lora_ev = EV_NONE;
+    const int k = op == OP_QKV ? 0 : op == OP_WO ? 1 : op == OP_GU ? 2 : op == OP_DOWN ? 3 : -1;
+    if (lr > 0 && k >= 0) {
+      t.la0 = (uint32_t)std::min<int64_t>((int64_t)tile * per_tile[k], n_arows[k]);
+      t.la1 = (uint32_t)std::min<int64_t>((int64_t)(tile + 1) * per_tile[k], n_arows[k]);
+      t.lora_ev = ev_lora(layer, k);
+    }
     t.op = op;
     t.layer = (uint32_t)layer;
     t.tile = tile;
@@ -240,15 +263,15 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
 }
 
 // Canonical bytes: little-endian u32 words.
-//   header: 'MKG1', version 1, n_workers, split, n_splits, n_events, n_tasks, n_slots
+//   header: 'MKG1', version 2, n_workers, split, n_splits, n_events, n_tasks, n_slots
 //   events: id, fanin, slot0
 //   tasks (topological order): topo, op, layer, tile, a0, a1, wait_ev, wait_fanin, wait_lag,
-//                              sig_ev, sig_slot, worker
+//                              sig_ev, sig_slot, worker, la0, la1, lora_ev
 std::vector<uint8_t> serialize_graph(const mk_model_cfg& c, const Graph& g) {
   (void)c;
   std::vector<uint32_t> w;
   w.push_back(0x31474B4Du);
-  w.push_back(1);
+  w.push_back(2);
   w.push_back((uint32_t)g.n_workers);
   w.push_back((uint32_t)g.split);
   w.push_back((uint32_t)g.n_splits);
@@ -274,6 +297,9 @@ std::vector<uint8_t> serialize_graph(const mk_model_cfg& c, const Graph& g) {
     w.push_back(t.sig_ev);
     w.push_back(t.sig_slot);
     w.push_back(g.task_cu[i]);
+    w.push_back(t.la0);
+    w.push_back(t.la1);
+    w.push_back(t.lora_ev);
   }
   std::vector<uint8_t> bytes(w.size() * 4);
   for (size_t i = 0; i < w.size(); ++i) {

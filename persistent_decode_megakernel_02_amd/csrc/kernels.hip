@@ -477,7 +477,9 @@ __device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
 // weight are exact in fp64; each row is summed in fp64 (lane-serial, then a
 // fixed tree) and the result is rounded once to fp32 where it is stored.
 // ---------------------------------------------------------------------------
-template <int NB>
+// LO: compiled with the LoRA adapters (a separate instantiation, so that the plain GEMV keeps its
+// registers)
+template <int NB, bool LO>
 __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                           uint64_t* tr) {
   const int op = (int)t.op, l = (int)t.layer;
@@ -501,7 +503,17 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   const bool norm = gamma != nullptr;
   const bool embed_src = (op == OP_QKV && l == 0);
   const int u0 = (int)t.a0, nu = (int)t.a1 - (int)t.a0;
-  const int my_units = nu > w ? (nu - w + NW - 1) / NW : 0;
+  // LoRA (Mirage article, "Case 2: LoRA + Linear", (W|B)(x|A x)): the tile also streams the
+  // adapter A units [la0, la1) of its operator, stored right after the operator's R_op weight units,
+  // as units nu.. of its own list; their sums u = A x are exchanged through the tile's LoRA event.
+  const bool lora = LO && t.lora_ev != EV_NONE;
+  const int na = lora ? (int)(t.la1 - t.la0) : 0;
+  // (arithmetic, not a choice between fields of P: a select of field addresses would make the
+  // compiler keep a copy of the whole parameter block in scratch memory)
+  const int R_op = (op == OP_QKV) * P.QKVR + (op == OP_GU) * P.F + (op == OP_WO || op == OP_DOWN) * P.H;
+  const int a_off = R_op + (int)t.la0 - nu;  // unit U >= nu is A unit la0 + U - nu
+  const int nut = nu + na;
+  const int my_units = nut > w ? (nut - w + NW - 1) / NW : 0;
   const int my_rows = my_units * RU;
   const int kc = min(K, (P.xs_doubles / NB) / 512 * 512);
   const int ps = kc >> 2;  // one plane: elements (2p, 2p+1) of every 8-element chunk, kc/8 pairs
@@ -510,7 +522,9 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   auto rowptr = [&](int r) -> const uint16_t* {
     const int ui = RU == 2 ? (r >> 1) : r;
     const uint16_t* base = (RU == 2 && (r & 1)) ? W1 : W0;
-    return base + (size_t)(u0 + w + NW * ui) * K;
+    const int U = w + NW * ui;
+    if constexpr (LO) return base + (size_t)(U + (U < nu ? u0 : a_off)) * K;
+    else return base + (size_t)(u0 + U) * K;
   };
 
   // pipeline state for one slice.  With four or more sequences the activations
@@ -685,7 +699,13 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
                 const uint2 q = ldg((const uint2*)er);
                 v[u][b] = v4f{bf_lo(q.x), bf_hi(q.x), bf_lo(q.y), bf_hi(q.y)};
               } else {
-                const float* src = op == OP_WO ? P.o + (size_t)b * P.QD : op == OP_DOWN ? P.a + (size_t)b * P.F : P.x + (size_t)b * P.H;
+                const float* src;
+                if constexpr (LO)  // the same choice without a select of field addresses (see R_op)
+                  src = (const float*)((op == OP_WO ? (uintptr_t)(P.o + (size_t)b * P.QD) : 0) |
+                                       (op == OP_DOWN ? (uintptr_t)(P.a + (size_t)b * P.F) : 0) |
+                                       (op != OP_WO && op != OP_DOWN ? (uintptr_t)(P.x + (size_t)b * P.H) : 0));
+                else
+                  src = op == OP_WO ? P.o + (size_t)b * P.QD : op == OP_DOWN ? P.a + (size_t)b * P.F : P.x + (size_t)b * P.H;
                 v[u][b] = ldc4(src, (uint32_t)e);
               }
             } else {
@@ -769,23 +789,74 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     rs[b] = norm ? 1.0 / sqrt(tot / (double)K + (double)P.eps) : 1.0;
   }
 
+  // ---- LoRA: publish this tile's adapter sums u = A x (scaled by the norm like the weight rows)
+  // as fp32, the stored second half of the concatenated operand; then wait for all of the
+  // operator's and stage them in LDS (the activation staging area is free from here on)
+  const int lr = P.lora_r;
+  const int nA = op == OP_QKV ? 3 * lr : op == OP_GU ? 2 * lr : lr;  // the operator's u per sequence
+  double* uu = xs;                                                   // [NB][nA]
+  if (lora) {
+    const int lk = op == OP_QKV ? 0 : op == OP_WO ? 1 : op == OP_GU ? 2 : 3;
+    float* ub = P.lora_u + (size_t)lk * P.B * 3 * lr;  // [B][3 r] region of this operator
+    for (int i = tid; i < na * RU * NB; i += NT) {
+      const int row = i / NB, b = i - row * NB;  // adapter row of the tile (RU per unit)
+      const int j = row / RU, rr = row - j * RU; // unit; gate (0) or up (1) A row of a pair
+      stc(ub + (size_t)b * 3 * lr + (int)t.la0 + j + rr * lr, (float)(red[((nu + j) * RU + rr) * NB + b] * rs[b]));
+    }
+    if (na > 0) signal_event(P, t.lora_ev, t.tile, P.epoch + (uint32_t)s + 1u);
+    // every mode: the other tiles of this operator run in the same launch
+    if (!wait_event(P, t.lora_ev, P.epoch + (uint32_t)s + 1u, t.tile, m)) return false;
+    for (int i = tid; i < NB * nA; i += NT) {
+      const int b = i / nA, j = i - b * nA;
+      uu[i] = (double)ldc(ub + (size_t)b * 3 * lr + j);
+    }
+    __syncthreads();
+  }
+  // B row `row` of Bm [rows][r] against u[b][seg, seg + r), summed in fp64 in order (exact products)
+  auto lora_term = [&](const uint16_t* Bm, int row, int seg, int b) -> double {
+    const uint16_t* br = Bm + (size_t)row * lr;
+    const double* ur = uu + b * nA + seg;
+    double acc = 0.0;
+    for (int j = 0; j < lr; j += 8) {
+      const uint4 q = ldg((const uint4*)(br + j));
+      const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fma((double)bf_lo(wv[e]), ur[j + 2 * e], acc);
+        acc = fma((double)bf_hi(wv[e]), ur[j + 2 * e + 1], acc);
+      }
+    }
+    return acc;
+  };
+
   // ---- epilogue per operator
   if (op == OP_QKV) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, (float)(red[ul * NB + b] * rs[b]));
+      double v = red[ul * NB + b] * rs[b];
+      if (lora) {  // the row's adapter: q, k or v by its place in the KV-head group
+        const int row = u0 + ul, gi = row % P.RG;
+        v += lora_term(LW.b_qkv, row, gi < P.G * P.D ? 0 : gi < (P.G + 1) * P.D ? lr : 2 * lr, b);
+      }
+      stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, (float)v);
     }
   } else if (resid) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
       float* xp = P.x + (size_t)b * P.H + u0 + ul;
-      stc(xp, (float)((double)(i == tid ? xpre : ldc(xp)) + red[ul * NB + b]));
+      double y = red[ul * NB + b];
+      if (lora) y += lora_term(op == OP_WO ? LW.b_o : LW.b_d, u0 + ul, 0, b);
+      stc(xp, (float)((double)(i == tid ? xpre : ldc(xp)) + y));
     }
   } else if (op == OP_GU) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      const double gt = red[(ul * 2) * NB + b] * rs[b];
-      const double up = red[(ul * 2 + 1) * NB + b] * rs[b];
+      double gt = red[(ul * 2) * NB + b] * rs[b];
+      double up = red[(ul * 2 + 1) * NB + b] * rs[b];
+      if (lora) {
+        gt += lora_term(LW.b_g, u0 + ul, 0, b);
+        up += lora_term(LW.b_u, u0 + ul, lr, b);
+      }
       stc(P.a + (size_t)b * P.F + u0 + ul, (float)(silu_d(gt) * up));
     }
   } else {  // OP_LM
@@ -1636,7 +1707,7 @@ __device__ __forceinline__ bool attn_nl(const KParams& P, const TaskRec& t, int 
 // access).  Until it is, GEMV tasks run as per-task GEMVs (task_gemv).
 constexpr bool kStreamEngine = false;
 
-template <int NB>
+template <int NB, bool LO>
 __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                          uint64_t* tr = nullptr) {
   if (t.op == OP_ATTN) {
@@ -1655,11 +1726,11 @@ __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int
     }
   }
   if constexpr (NB >= 8) return task_gemv_mfma<NB>(P, t, s, mega, lds, tr);
-  else return task_gemv<NB>(P, t, s, mega, lds, tr);
+  else return task_gemv<NB, LO>(P, t, s, mega, lds, tr);
 }
 
 // The megakernel: one launch runs n_steps decode steps of the whole model.
-template <int NB>
+template <int NB, bool LO>
 __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   char* lds = g_lds;
   const uint32_t off = ldg(P.list_off + blockIdx.x), n = ldg(P.list_len + blockIdx.x);
@@ -1680,7 +1751,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
       if (t.op == OP_ATTN) {
         uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + i) * 4 : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
-        if (!run_task<NB>(P, t, s, true, lds, tr)) return;
+        if (!run_task<NB, LO>(P, t, s, true, lds, tr)) return;
         if (tr && threadIdx.x == 0) tr[3] = wall_clock64();
         seg_step(L, s, i);
       } else if (!run_segment<NB>(P, L, s, i, lds, true)) {
@@ -1693,7 +1764,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
         const TaskRec t = ldg(P.tasks + ldg(P.cu_tasks + off + i));
         uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + i) * 4 : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
-        if (!run_task<NB>(P, t, s, true, lds, tr)) return;
+        if (!run_task<NB, LO>(P, t, s, true, lds, tr)) return;
         if (tr && threadIdx.x == 0) tr[3] = wall_clock64();
       }
     }
@@ -1712,7 +1783,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
 }
 
 // Ablation: one launch per operator instance, same tasks on the same workers.
-template <int NB>
+template <int NB, bool LO>
 __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
   char* lds = g_lds;
   if (threadIdx.x == 0) {
@@ -1737,7 +1808,7 @@ __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
         continue;
       }
     }
-    run_task<NB>(P, t, P.step, false, lds);
+    run_task<NB, LO>(P, t, P.step, false, lds);
   }
 }
 
@@ -1762,41 +1833,64 @@ static inline size_t worker_lds_bytes(const KParams& P) { return (size_t)P.misc_
 #define MK_CAT(a, b) MK_CAT2(a, b)
 
 #ifdef MK_NB
-template <int NB>
+// LoRA kernels exist for batch <= 4 (the library refuses adapters at larger batches)
+constexpr bool kLoraBuilt = MK_NB <= 4;
+
+template <int NB, bool LO>
 static hipError_t launch_nb(int kind, const KParams& P, hipStream_t st) {
   const size_t sh = worker_lds_bytes(P);
   KParams Q = P;
   if (kind == 0) {
     void* args[] = {&Q};
-    return hipLaunchCooperativeKernel((const void*)mk_persistent<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
+    return hipLaunchCooperativeKernel((const void*)mk_persistent<NB, LO>, dim3(P.n_workers), dim3(NT), args, sh, st);
   } else if (kind == 1) {
-    hipLaunchKernelGGL(mk_per_op<NB>, dim3(P.n_workers), dim3(NT), sh, st, Q);
+    hipLaunchKernelGGL((mk_per_op<NB, LO>), dim3(P.n_workers), dim3(NT), sh, st, Q);
   } else if (kind == 3) {
-    // cooperative: an attention merger polls partials written by other workgroups of the same launch
+    // cooperative: tasks of the launch wait on each other (attention mergers, LoRA adapter rows)
     void* args[] = {&Q};
-    return hipLaunchCooperativeKernel((const void*)mk_per_op<NB>, dim3(P.n_workers), dim3(NT), args, sh, st);
+    return hipLaunchCooperativeKernel((const void*)mk_per_op<NB, LO>, dim3(P.n_workers), dim3(NT), args, sh, st);
   } else {
     hipLaunchKernelGGL(mk_finish_tokens<NB>, dim3(1), dim3(NT), sh, st, Q);
   }
   return hipGetLastError();
 }
 
+template <int NB, bool LO>
+static hipError_t set_attrs_lo() {
+  const int sh = 163840;
+  hipError_t e = hipFuncSetAttribute((const void*)mk_persistent<NB, LO>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)mk_per_op<NB, LO>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+}
+
 template <int NB>
 static hipError_t set_attrs() {
   const int sh = 163840;
-  hipError_t e = hipFuncSetAttribute((const void*)mk_persistent<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
+  hipError_t e = set_attrs_lo<NB, false>();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)mk_per_op<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
-  if (e != hipSuccess) return e;
+  if constexpr (kLoraBuilt) {
+    e = set_attrs_lo<NB, true>();
+    if (e != hipSuccess) return e;
+  }
   return hipFuncSetAttribute((const void*)mk_finish_tokens<NB>, hipFuncAttributeMaxDynamicSharedMemorySize, sh);
 }
 
-hipError_t MK_CAT(launch_b, MK_NB)(int kind, const KParams& P, hipStream_t st) { return launch_nb<MK_NB>(kind, P, st); }
+hipError_t MK_CAT(launch_b, MK_NB)(int kind, const KParams& P, hipStream_t st) {
+  if constexpr (kLoraBuilt)
+    if (P.lora_r > 0) return launch_nb<MK_NB, true>(kind, P, st);
+  return launch_nb<MK_NB, false>(kind, P, st);
+}
 hipError_t MK_CAT(set_attrs_b, MK_NB)() { return set_attrs<MK_NB>(); }
 int MK_CAT(coresident_b, MK_NB)(size_t lds) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)mk_persistent<MK_NB>, NT, lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)mk_persistent<MK_NB, false>, NT, lds) != hipSuccess)
     return -1;
+  if constexpr (kLoraBuilt) {
+    int lo = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&lo, (const void*)mk_persistent<MK_NB, true>, NT, lds) != hipSuccess)
+      return -1;
+    per_cu = std::min(per_cu, lo);
+  }
   return per_cu;
 }
 #else

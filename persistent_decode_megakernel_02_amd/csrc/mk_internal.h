@@ -33,7 +33,10 @@ struct TaskRec {
   uint32_t wait_lag;  // 1: the event belongs to the previous decode step
   uint32_t sig_ev;    // event notified (slot sig_slot)
   uint32_t sig_slot;
-  uint32_t pad[3];
+  // LoRA (GEMV operators of a model with adapters): the tile also computes the adapters' A rows
+  // [la0, la1) of its operator, publishes them on event lora_ev (slot = tile), and waits for all of
+  // them before its epilogue.  lora_ev is EV_NONE without adapters.
+  uint32_t la0, la1, lora_ev;
 };
 static_assert(sizeof(TaskRec) == 48, "TaskRec layout");
 
@@ -52,6 +55,13 @@ struct LayerW {
   const uint16_t* ffn_norm;   // [H]
   const uint16_t* q_norm;     // [D] or null
   const uint16_t* k_norm;     // [D] or null
+  // LoRA B matrices [rows][r] (null without adapters); the A matrices [n][K] follow the rows of
+  // their weight matrix in the arena (wqkv: A_q, A_k, A_v; wo: A_o; wg: A_gate; wu: A_up; wd: A_down)
+  const uint16_t* b_qkv;  // [(Hq + 2 Hkv) D][r], rows in wqkv's order
+  const uint16_t* b_o;    // [H][r]
+  const uint16_t* b_g;    // [F][r]
+  const uint16_t* b_u;    // [F][r]
+  const uint16_t* b_d;    // [H][r]
 };
 
 // What the streaming GEMV engine (batch <= 4) reads about a task, built by the host once the
@@ -91,6 +101,7 @@ constexpr uint32_t ERR_WATCHDOG = 1;
 struct KParams {
   // model shape
   int32_t L, H, Hq, Hkv, D, F, V, G, RG, QKVR, QD, B, max_seq, S, NS, qk_norm;
+  int32_t lora_r;  // LoRA rank (0: no adapters)
   float eps;          // RMSNorm epsilon (an fp32 value, widened to fp64 where used)
   double attn_scale;  // 1 / sqrt(D)
   // tiling
@@ -120,6 +131,7 @@ struct KParams {
   TV* part_ml;      // [B][Hkv][NS][G][2][2] split max and sum (fp64 as two tagged words)
   TV* part_acc;     // [B][Hkv][NS][G][D][2] split unnormalised P.V (fp64 as two tagged words)
   LmPart* lm_part;    // [B][n_lm]
+  float* lora_u;      // [4 operators][B][3 r]: the adapters' A x of the current GEMV operator
   // tokens
   int32_t* pending;           // [B]
   int32_t* out_tokens;        // [n_steps][B] or null

@@ -174,7 +174,7 @@ def parse_graph(raw: bytes):
     base = 8 + 3 * nev
     op, layer, worker = [], [], []
     for i in range(nt):
-        r = w[base + 12 * i: base + 12 * (i + 1)]
+        r = w[base + 15 * i: base + 15 * (i + 1)]
         op.append(r[1])
         layer.append(r[2])
         worker.append(r[11])

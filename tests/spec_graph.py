@@ -32,6 +32,12 @@ Rules (one decode step; the persistent kernel repeats it every step):
     and notifies; splits beyond the current length notify at once), else slot b*Hkv+g
     (only the split holding the current position merges and notifies);
     GEMV tile i -> its event, slot i.
+  * LoRA (rank r > 0, a multiple of 8 up to 64): the GEMV operators QKV, WO, GU, DOWN have
+    nA = 3r, r, r, r adapter A rows (units); with T tiles, q = ceil(nA / T) per tile: tile i holds
+    [min(i q, nA), min((i+1) q, nA)).  One event per (layer, operator), appended after the LM event
+    in layer-major order QKV, WO, GU, DOWN, with fan-in ceil(nA / q) (the holders).  Other tasks:
+    la0 = la1 = 0, lora_ev = none.
+  * Canonical bytes, version 2: each task row ends with la0, la1, lora_ev.
 """
 from __future__ import annotations
 
@@ -54,10 +60,13 @@ class Task:
     sig_ev: int
     sig_slot: int
     worker: int
+    la0: int = 0
+    la1: int = 0
+    lora_ev: int = EV_NONE
 
 
 def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0, wo_tiles=0, gu_tiles=0,
-               down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0):
+               down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0, lora_rank=0):
     G = Hq // Hkv
     if split > 0:
         S = split
@@ -91,6 +100,22 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
     for _ in range(L):
         fanin += [TG] * Hkv + [NS * B * Hkv if dist else B * Hkv, n_wo, n_gu, n_down]
     fanin.append(n_lm)
+    # LoRA A-row events, after the LM event
+    n_arows = {OP_QKV: 3 * lora_rank, OP_WO: lora_rank, OP_GU: lora_rank, OP_DOWN: lora_rank}
+    tiles = {OP_QKV: TG * Hkv, OP_WO: n_wo, OP_GU: n_gu, OP_DOWN: n_down}
+    q = {op: -(-n_arows[op] // tiles[op]) for op in n_arows} if lora_rank else {}
+    kidx = {OP_QKV: 0, OP_WO: 1, OP_GU: 2, OP_DOWN: 3}
+    if lora_rank:
+        for _ in range(L):
+            for op in (OP_QKV, OP_WO, OP_GU, OP_DOWN):
+                fanin.append(-(-n_arows[op] // q[op]))
+
+    def lora_fields(op, layer, tile):
+        if not lora_rank or op not in kidx:
+            return {}
+        n = n_arows[op]
+        return dict(la0=min(tile * q[op], n), la1=min((tile + 1) * q[op], n),
+                    lora_ev=ev_lm + 1 + 4 * layer + kidx[op])
 
     def lo(i, R, T):
         return i * R // T
@@ -102,7 +127,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
             for i in range(TG):
                 t = g * TG + i
                 tasks.append(Task(OP_QKV, layer, t, g * RG + lo(i, RG, TG), g * RG + lo(i + 1, RG, TG),
-                                  in_ev, lag, ev(layer, g), i, place(0, t)))
+                                  in_ev, lag, ev(layer, g), i, place(0, t), **lora_fields(OP_QKV, layer, t)))
         k = 0
         for s in range(NS):
             for b in range(B):
@@ -114,7 +139,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
                                                    (OP_DOWN, H, n_down, Hkv + 2, Hkv + 3)), start=1):
             for i in range(T):
                 tasks.append(Task(op, layer, i, lo(i, R, T), lo(i + 1, R, T), ev(layer, wait), 0, ev(layer, sig), i,
-                                  place(k, i)))
+                                  place(k, i), **lora_fields(op, layer, i)))
     for i in range(n_lm):
         tasks.append(Task(OP_LM, 0, i, lo(i, V, n_lm), lo(i + 1, V, n_lm), ev(L - 1, Hkv + 3), 0, ev_lm, i,
                           place(4, i)))
@@ -127,10 +152,11 @@ def canonical_bytes(g, workers) -> bytes:
     for f in fanin:
         slot0.append(acc)
         acc += f
-    words = [0x31474B4D, 1, workers, g["split"], g["n_splits"], len(fanin), len(tasks), acc]
+    words = [0x31474B4D, 2, workers, g["split"], g["n_splits"], len(fanin), len(tasks), acc]
     for i, f in enumerate(fanin):
         words += [i, f, slot0[i]]
     for i, t in enumerate(tasks):
         wf = 0 if t.wait_ev == EV_NONE else fanin[t.wait_ev]
-        words += [i, t.op, t.layer, t.tile, t.a0, t.a1, t.wait_ev, wf, t.wait_lag, t.sig_ev, t.sig_slot, t.worker]
+        words += [i, t.op, t.layer, t.tile, t.a0, t.a1, t.wait_ev, wf, t.wait_lag, t.sig_ev, t.sig_slot, t.worker,
+                  t.la0, t.la1, t.lora_ev]
     return struct.pack(f"<{len(words)}I", *words)

@@ -166,6 +166,37 @@ def test_llama8b_prefilled_kv_matches_oracle(llama, name):
     oracle_check(llama, w, seqs, t, lg, name)
 
 
+def test_llama8b_lora16_decode512_matches_oracle_and_modes():
+    # the decode512 workload with a rank-16 adapter on every projection (fused LoRA + Linear)
+    w = WORKLOADS["llama8b_lora16_decode512"]
+    K = w.n_steps
+    say(f"{w.name}: one persistent launch of {K} steps")
+    model = Model(w.model)
+    try:
+        seqs = sequences(w)
+        eng = engine_for(model, w, K)
+        try:
+            restore(eng, w, seqs)
+            toks, logits = eng.decode(K)
+            torch.cuda.synchronize()
+            t, lg = toks.cpu().numpy(), logits.cpu().numpy()
+            del toks, logits
+            say(f"{w.name}: per-operator launches, {K} steps")
+            eng.set_mode(mk.MK_MODE_PER_OP)
+            restore(eng, w, seqs)
+            tp, lp = eng.decode(K)
+            torch.cuda.synchronize()
+            assert np.array_equal(tp.cpu().numpy(), t)
+            assert np.array_equal(lp.cpu().numpy().view(np.int32), lg.view(np.int32)), "per-op differs"
+            del tp, lp
+        finally:
+            eng.close()
+        check_properties(t, lg, w.name)
+        oracle_check(model, w, seqs, t, lg, w.name)
+    finally:
+        model.free()
+
+
 def test_chameleon7b_ctx4096_matches_oracle(llama):
     llama.free()  # the 8B weights are no longer needed by any later case in this module
     w = WORKLOADS["chameleon7b_ctx4096"]

@@ -2,6 +2,7 @@
 and a randomized-interleaving simulation of the event protocol (CPU only)."""
 import random
 import struct
+from dataclasses import replace
 
 import pytest
 
@@ -26,7 +27,46 @@ SPEC_ARGS = ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn",
 
 def spec_bytes(shape, B, max_seq, workers, split, **sched):
     dims = [getattr(shape, a) for a in SPEC_ARGS]
-    return canonical_bytes(spec_graph(*dims, B, max_seq, workers, split, **sched), workers)
+    return canonical_bytes(spec_graph(*dims, B, max_seq, workers, split, lora_rank=shape.lora_rank, **sched), workers)
+
+
+# LoRA: adapter A rows spread over the first tiles of every GEMV operator, one event per (layer, operator)
+LORA_CASES = [
+    (replace(TINY, lora_rank=8), 1, 71, 256, 0, None),
+    (replace(TINY, lora_rank=64), 2, 40, 8, 16, None),       # 192 QKV A rows over 8 tiles: 24 each
+    (replace(TINY, lora_rank=16), 4, 50, 37, 0, dict(qkv_tiles=3, wo_tiles=5, rotate=2)),
+    (replace(LLAMA8B, lora_rank=16), 1, 550, 256, 0, None),
+    (replace(LLAMA8B, lora_rank=64), 4, 1088, 256, 0, dict(gu_tiles=200, down_tiles=100)),
+]
+
+
+@pytest.mark.parametrize("shape,B,max_seq,workers,split,sched", LORA_CASES)
+def test_lora_graph_bytes_equal_spec(shape, B, max_seq, workers, split, sched):
+    got = mk.mk_build_graph(cfg_of(shape, B, max_seq, split, sched), workers)
+    assert got == spec_bytes(shape, B, max_seq, workers, split, **(sched or {}))
+    g = parse(got)
+    n_plain = len(parse(mk.mk_build_graph(cfg_of(replace(shape, lora_rank=0), B, max_seq, split, sched),
+                                          workers))["events"])
+    assert len(g["events"]) == n_plain + 4 * shape.n_layers
+    # every adapter row of every operator is held by exactly one tile, and the holders fill the event's slots
+    for layer in range(shape.n_layers):
+        for op, n_rows in ((OP_QKV, 3 * shape.lora_rank), (OP_WO, shape.lora_rank), (OP_GU, shape.lora_rank),
+                           (OP_DOWN, shape.lora_rank)):
+            ts = [t for t in g["tasks"] if t[1] == op and t[2] == layer]
+            held = sorted(r for t in ts for r in range(t[12], t[13]))
+            assert held == list(range(n_rows))
+            evs = {t[14] for t in ts}
+            assert len(evs) == 1
+            (ev,) = evs
+            holders = sorted(t[3] for t in ts if t[13] > t[12])
+            assert holders == list(range(len(holders))) and g["events"][ev][1] == len(holders)
+    assert all(t[14] == 0xFFFFFFFF for t in g["tasks"] if t[1] in (OP_ATTN, OP_LM))
+
+
+def test_lora_rank_is_validated():
+    for r in (4, 12, 72, -8):
+        with pytest.raises(mk.MkError):
+            mk.mk_build_graph(cfg_of(replace(TINY, lora_rank=r), 1, 40, 0), 256)
 
 
 # schedules the offline search may give: tile counts below and at the worker count, rotations,
@@ -66,7 +106,7 @@ def parse(raw: bytes):
     magic, ver, workers, split, ns, nev, nt, nslots = w[:8]
     ev = [w[8 + 3 * i: 11 + 3 * i] for i in range(nev)]
     base = 8 + 3 * nev
-    tasks = [w[base + 12 * i: base + 12 * (i + 1)] for i in range(nt)]
+    tasks = [w[base + 15 * i: base + 15 * (i + 1)] for i in range(nt)]
     return dict(magic=magic, ver=ver, workers=workers, split=split, ns=ns, events=ev, tasks=tasks, nslots=nslots)
 
 
@@ -82,7 +122,7 @@ def test_builder_bytes_equal_spec(shape, B, max_seq, workers, split):
 @pytest.mark.parametrize("shape,B,max_seq,workers,split", CASES)
 def test_graph_invariants(shape, B, max_seq, workers, split):
     g = parse(mk.mk_build_graph(cfg_of(shape, B, max_seq, split), workers))
-    assert g["magic"] == 0x31474B4D and g["ver"] == 1
+    assert g["magic"] == 0x31474B4D and g["ver"] == 2
     tasks, events = g["tasks"], g["events"]
     # topological indices are consecutive; slots partition the flag array
     assert [t[0] for t in tasks] == list(range(len(tasks)))
