@@ -101,6 +101,7 @@ def main():
     ap.add_argument("--workload", default="llama8b_decode512")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill timing")
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--probe-gib", type=float, default=8.0, help="read-probe buffer (0: skip)")
     args = ap.parse_args()
@@ -109,6 +110,7 @@ def main():
               "sharding is a design, not a measured path", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from persistent_decode_megakernel_02_amd import binding as mk
@@ -131,7 +133,8 @@ def main():
     # destroyed (mk_destroy synchronises its stream and frees its memory) in the finally clause, not by
     # a finaliser during interpreter shutdown.
     try:
-        eng = mk.Engine(shape, batch=B, max_seq=max_seq, split=args.split)
+        # prompts are prefilled through the megakernel (one launch per sequence; untimed)
+        eng = mk.Engine(shape, batch=B, max_seq=max_seq, split=args.split, prefill=mk.MK_PREFILL_MEGAKERNEL)
         eng.load_weights(weights)
         if not args.no_cpu:
             log("copying weights to host for the CPU baseline")
@@ -189,6 +192,31 @@ def main():
             log(f"per-operator: {ablation:.4f} ms/token; bit-identical to the megakernel: {identical}")
             eng.set_mode(mk.MK_MODE_MEGAKERNEL)
         prompt_tokens = (seqs["prompts"][0].cpu().tolist() if w.prompt_len > 0 else first_tokens)
+
+        prefill = None
+        if w.prompt_len > 0 and not args.no_prefill:
+            # prefill of the workload's prompt, per operator and through the megakernel (wall time of the
+            # synchronous call, median of 3), and of a longer prompt that fits the context
+            def time_prefill(mode, prompts):
+                eng.set_prefill(mode)
+                ts = []
+                for _ in range(3):
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    eng.prefill(prompts)
+                    ts.append((time.perf_counter() - t0) * 1000.0)
+                return sorted(ts)[1]
+            host_prompts = seqs["prompts"].cpu().numpy()
+            long_len = min(max_seq, 513)
+            long_prompts = np.random.default_rng(1).integers(0, shape.vocab, (B, long_len)).astype(np.int32)
+            prefill = {}
+            for name, pr in (("prompt", host_prompts), ("long", long_prompts)):
+                ms_op = time_prefill(mk.MK_PREFILL_PER_OP, pr)
+                ms_mk = time_prefill(mk.MK_PREFILL_MEGAKERNEL, pr)
+                prefill[name] = {"positions": int(pr.shape[1] - 1), "per_op_ms": round(ms_op, 2),
+                                 "megakernel_ms": round(ms_mk, 2)}
+                log(f"prefill of {pr.shape[1] - 1} positions: per operator {ms_op:.2f} ms, megakernel {ms_mk:.2f} ms")
+            eng.set_prefill(mk.MK_PREFILL_MEGAKERNEL)
         eng.close()
         eng = None
         del toks, logits, mega_toks, mega_logits, seqs
@@ -238,6 +266,7 @@ def main():
             "tokens_per_s": round(B * 1000.0 / ms_per_step, 2),
             "kernel_ms_library_events": round(ms_kernel, 3),
             "ablation_per_op_ms_per_step": round(ablation, 5) if ablation else None,
+            "prefill_ms": prefill,
             "ablation_bit_identical": identical,
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,

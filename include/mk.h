@@ -50,6 +50,11 @@ extern "C" {
 #define MK_MODE_MEGAKERNEL 0 /* one persistent cooperative launch per mk_decode */
 #define MK_MODE_PER_OP 1     /* ablation: one kernel launch per operator        */
 
+/* ---- prefill modes ---------------------------------------------------------- */
+#define MK_PREFILL_PER_OP 0     /* one launch per operator per prompt token            */
+#define MK_PREFILL_MEGAKERNEL 1 /* one persistent launch per sequence, chunk of tokens
+                                   per step as the columns of every projection         */
+
 /* ---- schedules ------------------------------------------------------------ */
 #define MK_SCHEDULE_FROZEN 0 /* the schedule the offline search froze for this case */
 #define MK_SCHEDULE_GIVEN 1  /* the schedule fields of mk_model_cfg, as given        */
@@ -93,6 +98,17 @@ typedef struct mk_model_cfg {
    * (W|B)(x|A x).  0: no adapters; else a multiple of 8 up to 64, batch
    * <= 4 (UNSUPPORTED otherwise). */
   int32_t lora_rank;
+  /* How mk_prefill runs the prompt (MK_PREFILL_*).  MK_PREFILL_MEGAKERNEL
+   * (Ada-MK, gist.science, "La « Flotte Hybride »" keeps prefill on a
+   * conventional engine; this runs it through the same task graph
+   * instead): per sequence one persistent launch; step s takes prompt
+   * tokens [s C, (s + 1) C) as C columns of every GEMV -- C = 16 on the
+   * matrix cores where hidden, ffn and n_q_heads * head_dim are multiples
+   * of 512 and there are no adapters, else 4 -- then an append task per
+   * KV-head group writes their rotated keys and values, and each token
+   * attends over the cache up to its own position.  mk_prefill_noalloc
+   * always runs per operator. */
+  int32_t prefill;
 } mk_model_cfg;
 
 typedef struct mk_ctx mk_ctx;
@@ -136,11 +152,15 @@ int mk_create(const mk_model_cfg* cfg, mk_ctx** out);
 int mk_load_weights(mk_ctx* ctx, const mk_tensor* tensors, int n);
 
 /* Prefill every sequence with its prompt: prompts is host int32 [B][len],
- * ids in [0, V).  Positions 0..len-2 are written to the KV cache (decode
- * steps run per operator, without the LM head) and prompts[b][len-1]
+ * ids in [0, V).  Positions 0..len-2 are written to the KV cache (per
+ * operator: decode steps without the LM head, one launch per operator; or
+ * through the megakernel, see mk_model_cfg.prefill) and prompts[b][len-1]
  * becomes the token decode step 0 consumes at position len-1.  Resets any
- * previous state.  Synchronous.  Errors: INVALID_ARG, CAPACITY
- * (len > max_seq), STATE (no weights), HIP. */
+ * previous state.  The prompts of all sequences have the same length: the
+ * sequences share one position (a sequence of its own length is installed
+ * with mk_load_kv instead).  Synchronous.  Errors: INVALID_ARG, CAPACITY
+ * (len > max_seq), STATE (no weights), UNSUPPORTED (megakernel prefill
+ * graph), TIMEOUT, HIP. */
 int mk_prefill(mk_ctx* ctx, const int32_t* prompts, int len);
 
 /* mk_prefill for callers that cannot allocate memory (code inside a HIP
@@ -175,6 +195,10 @@ int mk_decode(mk_ctx* ctx, int n_steps, int32_t* out_tokens, float* out_logits);
 /* Switch between MK_MODE_MEGAKERNEL and MK_MODE_PER_OP; state is kept. */
 int mk_set_mode(mk_ctx* ctx, int mode);
 
+/* Choose how the next mk_prefill runs (MK_PREFILL_PER_OP or
+ * MK_PREFILL_MEGAKERNEL, as mk_model_cfg.prefill).  Errors: INVALID_ARG. */
+int mk_set_prefill(mk_ctx* ctx, int prefill);
+
 /* Current position (shared by all sequences) and, if pending != NULL,
  * host int32 [B] pending tokens. */
 int mk_get_state(mk_ctx* ctx, int32_t* pos, int32_t* pending);
@@ -194,7 +218,10 @@ int mk_get_graph(mk_ctx* ctx, void* buf, size_t* len);
  * touching any GPU (same rules as mk_create). */
 int mk_build_graph(const mk_model_cfg* cfg, int n_workers, void* buf, size_t* len);
 
-/* Zero positions, pending tokens, event flags and tickets (weights kept). */
+/* Reset the whole context (every sequence): positions and pending tokens to
+ * zero, event slots and attention partials cleared, watchdog status cleared;
+ * weights, the schedule and the KV cache memory are kept (its contents become
+ * unreachable: decode reads only positions written since). */
 int mk_reset(mk_ctx* ctx);
 
 /* Measured streaming-read rate of this device: a plain kernel reads a

@@ -22,6 +22,8 @@ MK_ERR = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "OOM", -4: "HIP", -5: "CAPAC
  MK_ERR_STATE) = range(-1, -8, -1)
 MK_MODE_MEGAKERNEL = 0
 MK_MODE_PER_OP = 1
+MK_PREFILL_PER_OP = 0
+MK_PREFILL_MEGAKERNEL = 1
 MK_SCHEDULE_FROZEN = 0
 MK_SCHEDULE_GIVEN = 1
 SCHEDULE_FIELDS = ("qkv_tiles", "wo_tiles", "gu_tiles", "down_tiles", "lm_tiles", "rotate", "attn_offset")
@@ -40,14 +42,15 @@ class MkModelCfg(C.Structure):
                 ("mode", C.c_int32), ("split", C.c_int32), ("n_workers", C.c_int32), ("watchdog_polls", C.c_uint32),
                 ("stream", C.c_void_p), ("schedule", C.c_int32), ("qkv_tiles", C.c_int32), ("wo_tiles", C.c_int32),
                 ("gu_tiles", C.c_int32), ("down_tiles", C.c_int32), ("lm_tiles", C.c_int32), ("rotate", C.c_int32),
-                ("attn_offset", C.c_int32), ("lora_rank", C.c_int32)]
+                ("attn_offset", C.c_int32), ("lora_rank", C.c_int32), ("prefill", C.c_int32)]
 
 
 class MkTensor(C.Structure):
     _fields_ = [("name", C.c_char_p), ("data", C.c_void_p), ("numel", C.c_int64), ("on_device", C.c_int32)]
 
 
-EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_prefill_noalloc", "mk_load_kv", "mk_decode", "mk_set_mode", "mk_get_state",
+EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_prefill_noalloc", "mk_load_kv", "mk_decode", "mk_set_mode",
+           "mk_set_prefill", "mk_get_state",
            "mk_get_config",
            "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
            "mk_read_bandwidth", "mk_copy_bandwidth",
@@ -72,6 +75,7 @@ def lib():
         L.mk_load_kv.argtypes = [vp, C.c_int, C.c_int, vp, vp, i32, C.c_int]
         L.mk_decode.argtypes = [vp, C.c_int, vp, vp]
         L.mk_set_mode.argtypes = [vp, C.c_int]
+        L.mk_set_prefill.argtypes = [vp, C.c_int]
         L.mk_get_state.argtypes = [vp, C.POINTER(i32), C.POINTER(i32)]
         L.mk_get_config.argtypes = [vp, C.POINTER(MkModelCfg)]
         L.mk_get_graph.argtypes = [vp, vp, C.POINTER(sz)]
@@ -101,12 +105,14 @@ def _check(rc: int, ctx=None):
 
 
 def make_cfg(shape, batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, split: int = 0, n_workers: int = 0,
-             watchdog_polls: int = 0, stream=None, schedule: dict | None = None) -> MkModelCfg:
+             watchdog_polls: int = 0, stream=None, schedule: dict | None = None,
+             prefill: int = MK_PREFILL_PER_OP) -> MkModelCfg:
     """schedule: None for the frozen schedule, else a dict of SCHEDULE_FIELDS (missing ones 0)."""
     cfg = MkModelCfg(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
                      shape.vocab, shape.rms_eps, shape.rope_theta, int(shape.qk_norm), batch, max_seq, mode, split,
                      n_workers, watchdog_polls, stream)
     cfg.lora_rank = int(getattr(shape, "lora_rank", 0))
+    cfg.prefill = int(prefill)
     if schedule is not None:
         unknown = set(schedule) - set(SCHEDULE_FIELDS)
         _need(not unknown, f"unknown schedule fields {sorted(unknown)}")
@@ -211,6 +217,10 @@ def mk_set_mode(ctx, mode: int):
     _check(lib().mk_set_mode(ctx, mode), ctx)
 
 
+def mk_set_prefill(ctx, prefill: int):
+    _check(lib().mk_set_prefill(ctx, prefill), ctx)
+
+
 def mk_get_state(ctx, batch: int):
     pos = C.c_int32()
     pend = (C.c_int32 * batch)()
@@ -284,10 +294,11 @@ class Engine:
     """Owns one context: create -> load weights -> prefill/load_kv -> decode."""
 
     def __init__(self, shape, batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, split: int = 0,
-                 n_workers: int = 0, watchdog_polls: int = 0, schedule: dict | None = None):
+                 n_workers: int = 0, watchdog_polls: int = 0, schedule: dict | None = None,
+                 prefill: int = MK_PREFILL_PER_OP):
         self.shape, self.batch, self.max_seq = shape, batch, max_seq
         self.cfg = make_cfg(shape, batch, max_seq, mode, split, n_workers, watchdog_polls, _current_stream_handle(),
-                            schedule)
+                            schedule, prefill)
         self.ctx = mk_create(self.cfg)
 
     def load_weights(self, named_tensors):
@@ -309,6 +320,9 @@ class Engine:
 
     def set_mode(self, mode: int):
         mk_set_mode(self.ctx, mode)
+
+    def set_prefill(self, prefill: int):
+        mk_set_prefill(self.ctx, prefill)
 
     def state(self):
         return mk_get_state(self.ctx, self.batch)

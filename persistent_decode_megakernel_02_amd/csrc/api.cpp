@@ -44,10 +44,31 @@ struct LdsPlan {
   int sg_rg0, sg_rg1, sg_red, sg_red_cap, sg_xold, sg_xold_cap, sg_kc64, sg_kc32;
 };
 
+// The megakernel prefill (MK_PREFILL_MEGAKERNEL): its own graph of `chunk` virtual sequences, its
+// tables, event slots and activations; the weights and the KV cache are the context's.  Built on
+// first use.
+struct PrefillCtx {
+  bool built = false;
+  Graph g;
+  LdsPlan lds{};
+  EventRec* d_events = nullptr;
+  TaskRec* d_tasks = nullptr;
+  uint32_t *d_list_off = nullptr, *d_list_len = nullptr, *d_cu_tasks = nullptr, *d_range_start = nullptr;
+  uint32_t* flags = nullptr;
+  float *x = nullptr, *qkv = nullptr, *o = nullptr, *a = nullptr;
+  TV *part_ml = nullptr, *part_acc = nullptr, *lora_u = nullptr;
+  size_t n_part_ml = 0, n_part_acc = 0, n_lora_u = 0;
+  LmPart* lm_part = nullptr;
+  int32_t* force = nullptr;  // [steps][chunk] prompt tokens of one sequence, padded
+  size_t force_cap = 0;
+  uint32_t epoch = 0;        // steps run on this graph since the last reset
+};
+
 struct mk_ctx {
   mk_model_cfg cfg{};
   LdsPlan lds{};
   Graph g;
+  PrefillCtx pf;
   hipStream_t stream = nullptr;
   int device = 0;
   std::string err;
@@ -66,7 +87,8 @@ struct mk_ctx {
   TV *part_ml = nullptr, *part_acc = nullptr;
   size_t n_part_ml = 0, n_part_acc = 0;
   LmPart* lm_part = nullptr;
-  float* lora_u = nullptr;  // [4][B][3 r] adapter A x of the current GEMV operator (LoRA)
+  TV* lora_u = nullptr;  // [4][B][3 r] adapter A x of the current GEMV operator (LoRA), step-tagged
+  size_t n_lora_u = 0;
   int32_t* pending = nullptr;
   int32_t* force = nullptr;
   size_t force_cap = 0;
@@ -125,6 +147,7 @@ static std::string validate(const mk_model_cfg& cfg) {
   if (cfg.mode != MK_MODE_MEGAKERNEL && cfg.mode != MK_MODE_PER_OP) return "unknown mode";
   if (!(cfg.rms_eps > 0.f) || !(cfg.rope_theta > 0.0)) return "rms_eps and rope_theta must be positive";
   if (cfg.lora_rank < 0 || cfg.lora_rank > 64 || cfg.lora_rank % 8) return "lora_rank must be 0 or a multiple of 8 up to 64";
+  if (cfg.prefill != MK_PREFILL_PER_OP && cfg.prefill != MK_PREFILL_MEGAKERNEL) return "unknown prefill mode";
   return "";
 }
 
@@ -377,7 +400,8 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if ((rc = dalloc(c, (void**)&c->part_ml, c->n_part_ml * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->part_acc, c->n_part_acc * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->lm_part, (size_t)B * c->g.n_lm * sizeof(LmPart)))) return bail(rc);
-  if (r && (rc = dalloc(c, (void**)&c->lora_u, (size_t)4 * B * 3 * r * 4))) return bail(rc);
+  c->n_lora_u = (size_t)4 * B * 3 * r;
+  if (r && (rc = dalloc(c, (void**)&c->lora_u, c->n_lora_u * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->pending, (size_t)B * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->flags, (size_t)c->g.n_slots * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->status, 64))) return bail(rc);
@@ -464,6 +488,7 @@ int mk_reset(mk_ctx* c) {
   HIPCHK(c, hipMemsetAsync(c->flags, 0, (size_t)c->g.n_slots * 4, c->stream));
   HIPCHK(c, hipMemsetAsync(c->part_ml, 0, c->n_part_ml * sizeof(TV), c->stream));
   HIPCHK(c, hipMemsetAsync(c->part_acc, 0, c->n_part_acc * sizeof(TV), c->stream));
+  if (c->lora_u) HIPCHK(c, hipMemsetAsync(c->lora_u, 0, c->n_lora_u * sizeof(TV), c->stream));
   HIPCHK(c, hipMemsetAsync(c->status, 0, 64, c->stream));
   HIPCHK(c, hipMemsetAsync(c->pending, 0, (size_t)c->cfg.batch * 4, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
@@ -586,6 +611,8 @@ static KParams make_params(mk_ctx* c) {
   P.ntag = (uint32_t)c->g.events.size();
   P.epoch = c->epoch;
   P.lm_skip = c->lm_skip;
+  P.kvB = cfg.batch;
+  P.kv_seq = -1;
   P.lm_part = c->lm_part;
   P.lora_u = c->lora_u;
   P.lora_r = cfg.lora_rank;
@@ -663,6 +690,154 @@ static int prefill_into(mk_ctx* c, const int32_t* prompts, int len, int32_t* for
   return MK_OK;
 }
 
+// ---- megakernel prefill ------------------------------------------------------------------------
+// Columns per prefill step: 16 where the shape runs on the matrix-core GEMV (hidden, ffn and
+// n_q_heads * head_dim multiples of 512, no LoRA), else 4 (the fp64 GEMV).
+static int prefill_chunk(const mk_model_cfg& cfg) {
+  const bool mfma = cfg.hidden % 512 == 0 && cfg.ffn % 512 == 0 && (cfg.n_q_heads * cfg.head_dim) % 512 == 0 &&
+                    cfg.lora_rank == 0;
+  return mfma ? 16 : 4;
+}
+
+static int prefill_build(mk_ctx* c) {
+  PrefillCtx& f = c->pf;
+  if (f.built) return MK_OK;
+  const mk_model_cfg& cfg = c->cfg;
+  const int C = prefill_chunk(cfg), nw = c->g.n_workers;
+  std::string why = build_prefill_graph(cfg, nw, C, c->g.split, &f.g);
+  if (!why.empty()) return fail(c, MK_ERR_UNSUPPORTED, "prefill graph: " + why);
+  mk_model_cfg cc = cfg;
+  cc.batch = C;
+  int rc = plan_lds(cc, f.g, &f.lds, &why);
+  if (rc) return fail(c, rc, "prefill: " + why);
+  if (prepare_kernels(C) != hipSuccess) return fail(c, MK_ERR_HIP, "hipFuncSetAttribute failed");
+  {
+    KParams tmp{};
+    tmp.misc_off = f.lds.misc_off;
+    const int per_cu = max_coresident_workers(C, lds_bytes(tmp));
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) return fail(c, MK_ERR_HIP, "hipGetDeviceProperties");
+    if (per_cu < 1 || (int64_t)per_cu * prop.multiProcessorCount < nw)
+      return fail(c, MK_ERR_UNSUPPORTED, "prefill workers cannot all be resident at once");
+  }
+  const Graph& g = f.g;
+  const int H = cfg.hidden, D = cfg.head_dim, Hkv = cfg.n_kv_heads, G = cfg.n_q_heads / Hkv, NS = g.n_splits;
+  const size_t QD = (size_t)cfg.n_q_heads * D, QKVR = QD + 2 * (size_t)Hkv * D;
+  if ((rc = dalloc(c, (void**)&f.d_events, g.events.size() * sizeof(EventRec))) ||
+      (rc = dalloc(c, (void**)&f.d_tasks, g.tasks.size() * sizeof(TaskRec))) ||
+      (rc = dalloc(c, (void**)&f.d_list_off, g.list_off.size() * 4)) ||
+      (rc = dalloc(c, (void**)&f.d_list_len, g.list_len.size() * 4)) ||
+      (rc = dalloc(c, (void**)&f.d_cu_tasks, g.cu_tasks.size() * 4)) ||
+      (rc = dalloc(c, (void**)&f.d_range_start, g.range_start.size() * 4)) ||
+      (rc = dalloc(c, (void**)&f.flags, (size_t)g.n_slots * 4)) ||
+      (rc = dalloc(c, (void**)&f.x, (size_t)C * H * 4)) || (rc = dalloc(c, (void**)&f.qkv, (size_t)C * QKVR * 4)) ||
+      (rc = dalloc(c, (void**)&f.o, (size_t)C * QD * 4)) || (rc = dalloc(c, (void**)&f.a, (size_t)C * cfg.ffn * 4)) ||
+      (rc = dalloc(c, (void**)&f.part_ml, (f.n_part_ml = (size_t)C * Hkv * NS * G * 2 * 2) * sizeof(TV))) ||
+      (rc = dalloc(c, (void**)&f.part_acc, (f.n_part_acc = (size_t)C * Hkv * NS * G * D * 2) * sizeof(TV))) ||
+      (rc = dalloc(c, (void**)&f.lm_part, (size_t)C * g.n_lm * sizeof(LmPart))))
+    return rc;
+  f.n_lora_u = (size_t)4 * C * 3 * cfg.lora_rank;
+  if (cfg.lora_rank && (rc = dalloc(c, (void**)&f.lora_u, f.n_lora_u * sizeof(TV)))) return rc;
+  if (hipMemcpy(f.d_events, g.events.data(), g.events.size() * sizeof(EventRec), hipMemcpyHostToDevice) ||
+      hipMemcpy(f.d_tasks, g.tasks.data(), g.tasks.size() * sizeof(TaskRec), hipMemcpyHostToDevice) ||
+      hipMemcpy(f.d_list_off, g.list_off.data(), g.list_off.size() * 4, hipMemcpyHostToDevice) ||
+      hipMemcpy(f.d_list_len, g.list_len.data(), g.list_len.size() * 4, hipMemcpyHostToDevice) ||
+      hipMemcpy(f.d_cu_tasks, g.cu_tasks.data(), g.cu_tasks.size() * 4, hipMemcpyHostToDevice) ||
+      hipMemcpy(f.d_range_start, g.range_start.data(), g.range_start.size() * 4, hipMemcpyHostToDevice))
+    return fail(c, MK_ERR_HIP, "prefill graph upload");
+  f.built = true;
+  return MK_OK;
+}
+
+// Prefill through the persistent kernel: for each sequence, one launch whose step s takes prompt
+// tokens [s C, (s + 1) C) as the C columns of every projection.
+static int prefill_megakernel(mk_ctx* c, const int32_t* prompts, int len) {
+  int rc = mk_reset(c);
+  if (rc) return rc;
+  if ((rc = prefill_build(c))) return rc;
+  PrefillCtx& f = c->pf;
+  const Graph& g = f.g;
+  const int B = c->cfg.batch, C = g.chunk, n = len - 1;
+  if (n > 0) {
+    const int steps = (n + C - 1) / C;
+    if ((size_t)steps * C > f.force_cap) {
+      if ((rc = dalloc(c, (void**)&f.force, (size_t)steps * C * 4))) return rc;
+      f.force_cap = (size_t)steps * C;
+    }
+    // a fresh start of the prefill graph's steps: event slots and step-tagged words cleared
+    HIPCHK(c, hipMemsetAsync(f.flags, 0, (size_t)g.n_slots * 4, c->stream));
+    HIPCHK(c, hipMemsetAsync(f.part_ml, 0, f.n_part_ml * sizeof(TV), c->stream));
+    HIPCHK(c, hipMemsetAsync(f.part_acc, 0, f.n_part_acc * sizeof(TV), c->stream));
+    if (f.lora_u) HIPCHK(c, hipMemsetAsync(f.lora_u, 0, f.n_lora_u * sizeof(TV), c->stream));
+    f.epoch = 0;
+    KParams P = make_params(c);
+    P.B = C;
+    P.S = g.split;
+    P.NS = g.n_splits;
+    P.n_qkv = g.n_qkv;
+    P.n_wo = g.n_wo;
+    P.n_gu = g.n_gu;
+    P.n_down = g.n_down;
+    P.n_lm = g.n_lm;
+    P.xs_doubles = f.lds.xs_doubles;
+    P.red_doubles = f.lds.red_doubles;
+    P.red_off = f.lds.red_off;
+    P.misc_off = f.lds.misc_off;
+    P.mk_ks = f.lds.mk_ks;
+    P.x = f.x;
+    P.qkv = f.qkv;
+    P.o = f.o;
+    P.a = f.a;
+    P.part_ml = f.part_ml;
+    P.part_acc = f.part_acc;
+    P.lm_part = f.lm_part;
+    P.lora_u = f.lora_u;
+    P.flags = f.flags;
+    P.events = f.d_events;
+    P.tasks = f.d_tasks;
+    P.task_cu = nullptr;
+    P.list_off = f.d_list_off;
+    P.list_len = f.d_list_len;
+    P.cu_tasks = f.d_cu_tasks;
+    P.range_start = f.d_range_start;
+    P.segrec = nullptr;
+    P.ntag = (uint32_t)g.events.size();
+    P.with_lm = 0;
+    P.chunk = C;
+    P.kvB = B;
+    P.pos_end = n;
+    P.pos0 = 0;
+    P.n_steps = steps;
+    P.force_tok = f.force;
+    P.lm_skip = 0;
+    std::vector<int32_t> tok((size_t)steps * C, 0);  // padding tokens: id 0, masked in the kernel
+    for (int q = 0; q < B; ++q) {
+      for (int i = 0; i < n; ++i) tok[i] = prompts[(size_t)q * len + i];
+      HIPCHK(c, hipMemcpyAsync(f.force, tok.data(), tok.size() * 4, hipMemcpyHostToDevice, c->stream));
+      P.kv_seq = q;
+      P.epoch = f.epoch;
+      HIPCHK(c, launch(0, P, c->stream));
+      HIPCHK(c, hipStreamSynchronize(c->stream));
+      f.epoch += (uint32_t)steps;
+    }
+    uint32_t st[8];
+    HIPCHK(c, hipMemcpy(st, c->status, sizeof st, hipMemcpyDeviceToHost));
+    if (st[ST_ABORT] || st[ST_CODE]) {
+      char buf[256];
+      std::snprintf(buf, sizeof buf, "prefill watchdog: worker %u task %u waited on event %u (slot value %u, wanted %u)",
+                    st[ST_CU], st[ST_TASK], st[ST_EVENT], st[ST_SEEN], st[ST_WANT]);
+      return fail(c, MK_ERR_TIMEOUT, buf);
+    }
+  }
+  int32_t pend[16];
+  for (int b = 0; b < B; ++b) pend[b] = prompts[(size_t)b * len + len - 1];
+  HIPCHK(c, hipMemcpyAsync(c->pending, pend, (size_t)B * 4, hipMemcpyHostToDevice, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  c->pos = n;
+  std::fill(c->seq_pos.begin(), c->seq_pos.end(), n);
+  return MK_OK;
+}
+
 static int prefill_check(mk_ctx* c, const int32_t* prompts, int len) {
   if (!c || !prompts || len <= 0) return fail(c, MK_ERR_INVALID_ARG, "null prompts or len <= 0");
   if (!c->have_weights) return fail(c, MK_ERR_STATE, "weights not loaded");
@@ -675,6 +850,7 @@ static int prefill_check(mk_ctx* c, const int32_t* prompts, int len) {
 int mk_prefill(mk_ctx* c, const int32_t* prompts, int len) {
   int rc = prefill_check(c, prompts, len);
   if (rc) return rc;
+  if (c->cfg.prefill == MK_PREFILL_MEGAKERNEL) return prefill_megakernel(c, prompts, len);
   const size_t need = (size_t)(len - 1) * c->cfg.batch;
   if (need > c->force_cap) {
     if (c->force) {
@@ -727,6 +903,13 @@ int mk_set_mode(mk_ctx* c, int mode) {
   if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
   if (mode != MK_MODE_MEGAKERNEL && mode != MK_MODE_PER_OP) return fail(c, MK_ERR_INVALID_ARG, "unknown mode");
   c->cfg.mode = mode;
+  return MK_OK;
+}
+
+int mk_set_prefill(mk_ctx* c, int prefill) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
+  if (prefill != MK_PREFILL_PER_OP && prefill != MK_PREFILL_MEGAKERNEL) return fail(c, MK_ERR_INVALID_ARG, "unknown prefill mode");
+  c->cfg.prefill = prefill;
   return MK_OK;
 }
 

@@ -48,8 +48,10 @@ Schedule frozen_schedule(const mk_model_cfg& c, int n_workers) {
   return Schedule{};
 }
 
-std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
+// chunk > 0: the prefill graph (see build_prefill_graph); chunk == 0: the decode graph
+static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int chunk, int chunk_split, Graph* out) {
   Graph g;
+  g.chunk = chunk;
   if (n_workers <= 0) return "n_workers must be positive";
   if (c.n_layers <= 0 || c.hidden <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 ||
       c.vocab <= 0 || c.batch <= 0 || c.max_seq <= 0)
@@ -80,6 +82,12 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
     return "schedule must be MK_SCHEDULE_FROZEN or MK_SCHEDULE_GIVEN";
   }
   if (c.split > 0) sc.split = c.split;
+  // the prefill graph: the plain tiling, the decode graph's split, chunk virtual sequences
+  if (chunk > 0) {
+    sc = Schedule{};
+    sc.split = chunk_split;
+  }
+  const int B = chunk > 0 ? chunk : c.batch;
   if (sc.qkv_tiles < 0 || sc.wo_tiles < 0 || sc.gu_tiles < 0 || sc.down_tiles < 0 || sc.lm_tiles < 0 || sc.rotate < 0 ||
       sc.attn_offset < 0)
     return "schedule fields must be >= 0";
@@ -87,7 +95,7 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
     return "at most one tile per worker for each GEMV operator";
   int S = sc.split;
   if (S <= 0) {
-    const int per = std::max(1, c.batch * Hkv);  // attention tasks per split
+    const int per = std::max(1, B * Hkv);  // attention tasks per split
     const int ns_target = std::max(1, n_workers / per);
     S = std::min(smax, std::max(kDefaultSplit, (c.max_seq + ns_target - 1) / ns_target));
     // Capped by smax, the splits spill over into several tasks per worker.  Up to three per
@@ -124,7 +132,8 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   // When every attention task of a layer has a worker of its own, all of a head's splits run
   // at once and each merges a slice of the outputs, signalling its own slot; otherwise the
   // split holding the current position merges everything and signals for its (sequence, head).
-  const bool dist = (int64_t)g.n_splits * c.batch * Hkv <= n_workers;
+  // (never in the prefill graph, whose virtual sequences hold different positions in one step)
+  const bool dist = chunk == 0 && (int64_t)g.n_splits * B * Hkv <= n_workers;
 
   // LoRA: each GEMV operator of a layer spreads the A rows (units) of its adapters over its first
   // tiles, q per tile; QKV 3r rows (A_q, A_k, A_v), WO r, GU r (A_gate, A_up row pairs), DOWN r.
@@ -148,10 +157,15 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
     per_tile[k] = (n_arows[k] + n_tiles[k] - 1) / n_tiles[k];
     holders[k] = (n_arows[k] + per_tile[k] - 1) / per_tile[k];
   }
-  g.events.resize(ev_lm + 1 + (lr > 0 ? 4 * c.n_layers : 0));
+  // prefill graph: an append event per (layer, KV-head group) after all others; the appending task
+  // writes the group's rotated keys and values of the chunk to the cache before attention reads them
+  const uint32_t ev_app0 = ev_lm + 1u + (uint32_t)(lr > 0 ? 4 * c.n_layers : 0);
+  auto ev_app = [&](int l, int gg) { return ev_app0 + (uint32_t)(l * Hkv + gg); };
+  g.events.resize(ev_app0 + (chunk > 0 ? Hkv * c.n_layers : 0));
   for (int l = 0; l < c.n_layers; ++l) {
     for (int gg = 0; gg < Hkv; ++gg) g.events[ev_qkv(l, gg)].fanin = TG;
-    g.events[ev_att(l)].fanin = dist ? g.n_splits * c.batch * Hkv : c.batch * Hkv;
+    g.events[ev_att(l)].fanin = dist ? g.n_splits * B * Hkv : B * Hkv;
+    for (int gg = 0; gg < Hkv && chunk > 0; ++gg) g.events[ev_app(l, gg)].fanin = 1;
     g.events[ev_o(l)].fanin = g.n_wo;
     g.events[ev_a(l)].fanin = g.n_gu;
     g.events[ev_x(l)].fanin = g.n_down;
@@ -193,7 +207,8 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   auto range_end = [&](uint32_t first) { g.op_ranges.push_back({first, (uint32_t)g.tasks.size() - first}); };
 
   for (int l = 0; l < c.n_layers; ++l) {
-    const uint32_t in_ev = l == 0 ? ev_lm : ev_x(l - 1);
+    // layer 0 waits for the previous step's LM head (decode) or last layer (prefill: no LM head)
+    const uint32_t in_ev = l == 0 ? (chunk > 0 ? ev_x(c.n_layers - 1) : ev_lm) : ev_x(l - 1);
     const uint32_t in_lag = l == 0 ? 1u : 0u;
     uint32_t f = range_begin();
     for (int gg = 0; gg < Hkv; ++gg)
@@ -203,13 +218,19 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
         push(OP_QKV, l, tile, r0, r1, in_ev, in_lag, ev_qkv(l, gg), (uint32_t)i, place(0, tile));
       }
     range_end(f);
+    if (chunk > 0) {  // prefill: one append task per KV-head group, on the worker of the group's first QKV tile
+      f = range_begin();
+      for (int gg = 0; gg < Hkv; ++gg)
+        push(OP_APPEND, l, (uint32_t)gg, (uint32_t)gg, 0, ev_qkv(l, gg), 0, ev_app(l, gg), 0, place(0, gg * TG));
+      range_end(f);
+    }
     f = range_begin();
     uint32_t idx = 0;
     for (int s = 0; s < g.n_splits; ++s)
-      for (int b = 0; b < c.batch; ++b)
+      for (int b = 0; b < B; ++b)
         for (int gg = 0; gg < Hkv; ++gg, ++idx)
-          push(OP_ATTN, l, idx, (uint32_t)(b * Hkv + gg), (uint32_t)s, ev_qkv(l, gg), 0, ev_att(l),
-               dist ? idx : (uint32_t)(b * Hkv + gg), place_att(idx));
+          push(OP_ATTN, l, idx, (uint32_t)(b * Hkv + gg), (uint32_t)s, chunk > 0 ? ev_app(l, gg) : ev_qkv(l, gg), 0,
+               ev_att(l), dist ? idx : (uint32_t)(b * Hkv + gg), place_att(idx));
     range_end(f);
     f = range_begin();
     for (int i = 0; i < g.n_wo; ++i)
@@ -227,11 +248,13 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
            place(3, i));
     range_end(f);
   }
-  uint32_t f = range_begin();
-  for (int i = 0; i < g.n_lm; ++i)
-    push(OP_LM, 0, i, tile_lo(i, c.vocab, g.n_lm), tile_lo(i + 1, c.vocab, g.n_lm), ev_x(c.n_layers - 1), 0, ev_lm, i,
-         place(4, i));
-  range_end(f);
+  if (chunk == 0) {  // the prefill graph has no LM head
+    uint32_t f = range_begin();
+    for (int i = 0; i < g.n_lm; ++i)
+      push(OP_LM, 0, i, tile_lo(i, c.vocab, g.n_lm), tile_lo(i + 1, c.vocab, g.n_lm), ev_x(c.n_layers - 1), 0, ev_lm,
+           i, place(4, i));
+    range_end(f);
+  }
 
   // per-worker lists in topological order
   g.list_off.assign(n_workers, 0);
@@ -260,6 +283,15 @@ std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
   }
   *out = std::move(g);
   return "";
+}
+
+std::string build_graph(const mk_model_cfg& c, int n_workers, Graph* out) {
+  return build_graph_impl(c, n_workers, 0, 0, out);
+}
+
+std::string build_prefill_graph(const mk_model_cfg& c, int n_workers, int chunk, int split, Graph* out) {
+  if (chunk <= 0 || split <= 0) return "chunk and split must be positive";
+  return build_graph_impl(c, n_workers, chunk, split, out);
 }
 
 // Canonical bytes: little-endian u32 words.

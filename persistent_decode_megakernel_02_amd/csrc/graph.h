@@ -10,6 +10,7 @@ namespace mk {
 
 struct Graph {
   int n_workers = 0;
+  int chunk = 0;  // prefill graph: tokens per step (virtual sequences); 0: the decode graph
   int split = 0, n_splits = 0;
   int qkv_tiles_per_group = 0, n_qkv = 0, n_wo = 0, n_gu = 0, n_down = 0, n_lm = 0;
   int n_slots = 0;
@@ -41,6 +42,14 @@ Schedule frozen_schedule(const mk_model_cfg& cfg, int n_workers);
 
 // Validate the shape and build the graph; returns "" or an error message.
 std::string build_graph(const mk_model_cfg& cfg, int n_workers, Graph* g);
+
+// The prefill graph: one step takes `chunk` consecutive prompt tokens of one sequence as the
+// columns ("virtual sequences") of every GEMV, so the projections run as a skinny GEMM (on the
+// matrix cores at 16 columns).  Per layer an append task per KV-head group writes the chunk's
+// rotated keys and values to the cache after QKV, and the attention tasks (virtual sequence b at
+// its own position) wait for it; no LM head; layer 0 of step s waits for the last layer of step
+// s - 1.  The split is the decode graph's, so attention adds the same partials.
+std::string build_prefill_graph(const mk_model_cfg& cfg, int n_workers, int chunk, int split, Graph* g);
 std::vector<uint8_t> serialize_graph(const mk_model_cfg& cfg, const Graph& g);
 
 constexpr int kDefaultSplit = 32;  // smallest default split (positions per attention task)

@@ -62,6 +62,7 @@ struct Misc {
   uint32_t cev, ctgt;   // the last (event, target) this worker's wait saw complete
   uint32_t qk_step, qk_id;  // step tag and (layer, sequence, KV head) of the rotated queries in LDS
   int32_t att_fail;         // sticky: an attention merge of this worker exceeded its poll budget
+  int32_t lora_fail;        // a LoRA adapter sum of the current task was not published in its poll budget
   // streaming GEMV engine (batch <= 4)
   struct {
     uint32_t staged, done, abort;
@@ -314,7 +315,9 @@ __device__ __forceinline__ double silu_d(double z) { return z / (1.0 + exp(-z));
 // signals; otherwise the split holding the current position merges them all and alone signals
 // (without dist, in slot b Hkv + g, and a split may wait only on splits listed before it).
 constexpr int ATT_MCH = 8;
-__device__ __forceinline__ bool att_dist(const KParams& P) { return P.NS * P.B * P.Hkv <= P.n_workers; }
+__device__ __forceinline__ bool att_dist(const KParams& P) {
+  return P.chunk == 0 && P.NS * P.B * P.Hkv <= P.n_workers;
+}
 
 // Event form.  Default: one 32-bit slot per producer holding the number of the last step it
 // completed; an event fires for step t when every slot it waits on holds t (plain stores, no
@@ -471,6 +474,16 @@ __device__ __forceinline__ void reduce_tokens(const KParams& P, Misc* m) {
   __syncthreads();
 }
 
+// 32 bits of a value tagged with the step that wrote it, one 64-bit device-coherent access
+__device__ __forceinline__ void st_tv(TV* p, uint32_t bits, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | bits;
+  __hip_atomic_store((GAS uint64_t*)p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tv(const TV* p) {
+  return __hip_atomic_load((const GAS uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tv_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
 // ---------------------------------------------------------------------------
 // GEMV task: rows [a0, a1) of one weight matrix against B activation vectors.
 // Numerics: the staged activation x_k * gamma_k and every product with a bf16
@@ -504,15 +517,23 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   const bool embed_src = (op == OP_QKV && l == 0);
   const int u0 = (int)t.a0, nu = (int)t.a1 - (int)t.a0;
   // LoRA (Mirage article, "Case 2: LoRA + Linear", (W|B)(x|A x)): the tile also streams the
-  // adapter A units [la0, la1) of its operator, stored right after the operator's R_op weight units,
-  // as units nu.. of its own list; their sums u = A x are exchanged through the tile's LoRA event.
+  // adapter A units [la0, la1) of its operator, stored right after the operator's R_op weight
+  // units, as the first units of its own list (U < na), so that their sums u = A x are ready
+  // early; each is published as soon as its row completes, as a step-tagged fp32 word, and every
+  // tile of the operator reads all of them after its own rows.
   const bool lora = LO && t.lora_ev != EV_NONE;
   const int na = lora ? (int)(t.la1 - t.la0) : 0;
   // (arithmetic, not a choice between fields of P: a select of field addresses would make the
   // compiler keep a copy of the whole parameter block in scratch memory)
   const int R_op = (op == OP_QKV) * P.QKVR + (op == OP_GU) * P.F + (op == OP_WO || op == OP_DOWN) * P.H;
-  const int a_off = R_op + (int)t.la0 - nu;  // unit U >= nu is A unit la0 + U - nu
+  const int a_off = R_op + (int)t.la0;  // unit U < na: A unit la0 + U; else weight unit u0 + U - na
+  const int w_off = u0 - na;
   const int nut = nu + na;
+  const int wbase = na * RU * NB;  // the weight rows' sums follow the adapter rows' in red
+  const int lr = P.lora_r;
+  const int lk = op == OP_QKV ? 0 : op == OP_WO ? 1 : op == OP_GU ? 2 : 3;
+  TV* const ub = lora ? P.lora_u + (size_t)lk * P.B * 3 * lr : nullptr;  // [B][3 r] of this operator
+  const uint32_t utag = (P.epoch + (uint32_t)s) * P.ntag + t.lora_ev + 1u;
   const int my_units = nut > w ? (nut - w + NW - 1) / NW : 0;
   const int my_rows = my_units * RU;
   const int kc = min(K, (P.xs_doubles / NB) / 512 * 512);
@@ -523,7 +544,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     const int ui = RU == 2 ? (r >> 1) : r;
     const uint16_t* base = (RU == 2 && (r & 1)) ? W1 : W0;
     const int U = w + NW * ui;
-    if constexpr (LO) return base + (size_t)(U + (U < nu ? u0 : a_off)) * K;
+    if constexpr (LO) return base + (size_t)(U + (U < na ? a_off : w_off)) * K;
     else return base + (size_t)(u0 + U) * K;
   };
 
@@ -621,7 +642,20 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const double v = wave_sum_d(acc[rr][b]);
-          if (lane == 0 && (RPG == 1 || r < my_rows)) red[rl * NB + b] = sl_cur == 0 ? v : red[rl * NB + b] + v;
+          if (lane == 0 && (RPG == 1 || r < my_rows)) {
+            const double tot = sl_cur == 0 ? v : red[rl * NB + b] + v;
+            red[rl * NB + b] = tot;
+            if constexpr (LO) {  // a completed adapter row: publish u = (A x) scaled like the weight rows
+              const int U = w + NW * ui;
+              if (U < na && sl_cur == nsl - 1) {
+                double ss = 0.0;
+                for (int ww = 0; ww < NW; ++ww) ss += m->wred[ww][b];
+                const double rsb = norm ? 1.0 / sqrt(ss / (double)K + (double)P.eps) : 1.0;
+                const int idx = (int)t.la0 + U + (RU == 2 ? (r & 1) * lr : 0);
+                st_tv(ub + (size_t)b * 3 * lr + idx, __float_as_uint((float)(tot * rsb)), utag);
+              }
+            }
+          }
           acc[rr][b] = 0.0;
         }
       }
@@ -633,6 +667,29 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   slice_setup(0);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) issue(buf[d]);
+
+  // LoRA: the tile's B rows (r bf16 per output row) do not depend on it either; up to two 16-byte
+  // pieces per thread are requested now and parked in LDS after the rows are streamed
+  const int bper = LO ? lr / 8 : 1;              // 16-byte pieces per B row
+  const int nbq = lora ? nu * RU * bper : 0;     // pieces of the tile's B rows
+  const bool bpre = lora && nbq <= 2 * NT;
+  uint4 bq[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  // B row `row` of the tile (RU per unit; at gate/up the gate and up rows of unit row / 2)
+  auto brow = [&](int row) -> const uint16_t* {
+    const int ul = RU == 2 ? row >> 1 : row;
+    const uintptr_t bm = (op == OP_QKV ? (uintptr_t)LW.b_qkv : 0) | (op == OP_WO ? (uintptr_t)LW.b_o : 0) |
+                         (op == OP_DOWN ? (uintptr_t)LW.b_d : 0) |
+                         (op == OP_GU ? (uintptr_t)((row & 1) ? LW.b_u : LW.b_g) : 0);
+    return (const uint16_t*)bm + (size_t)(u0 + ul) * lr;
+  };
+  if constexpr (LO) {
+    if (bpre)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int q = tid + k * NT;
+        if (q < nbq) bq[k] = ldg((const uint4*)(brow(q / bper) + (q % bper) * 8));
+      }
+  }
 
   // a wait on the previous step is met by the launch boundary at the first step of a call
   if (mega && !(s == 0 && t.wait_lag) &&
@@ -789,36 +846,59 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     rs[b] = norm ? 1.0 / sqrt(tot / (double)K + (double)P.eps) : 1.0;
   }
 
-  // ---- LoRA: publish this tile's adapter sums u = A x (scaled by the norm like the weight rows)
-  // as fp32, the stored second half of the concatenated operand; then wait for all of the
-  // operator's and stage them in LDS (the activation staging area is free from here on)
-  const int lr = P.lora_r;
+  // ---- LoRA: read the operator's adapter sums u = A x (fp32, the stored second half of the
+  // concatenated operand), each a word tagged with this step, into LDS (the activation staging area
+  // is free from here on); a word not yet published is polled, every mode (the publishing tiles
+  // run in the same launch)
   const int nA = op == OP_QKV ? 3 * lr : op == OP_GU ? 2 * lr : lr;  // the operator's u per sequence
   double* uu = xs;                                                   // [NB][nA]
+  uint4* bl = (uint4*)(xs + ((NB * nA + 1) & ~1));                   // [nbq] the tile's B rows
   if (lora) {
-    const int lk = op == OP_QKV ? 0 : op == OP_WO ? 1 : op == OP_GU ? 2 : 3;
-    float* ub = P.lora_u + (size_t)lk * P.B * 3 * lr;  // [B][3 r] region of this operator
-    for (int i = tid; i < na * RU * NB; i += NT) {
-      const int row = i / NB, b = i - row * NB;  // adapter row of the tile (RU per unit)
-      const int j = row / RU, rr = row - j * RU; // unit; gate (0) or up (1) A row of a pair
-      stc(ub + (size_t)b * 3 * lr + (int)t.la0 + j + rr * lr, (float)(red[((nu + j) * RU + rr) * NB + b] * rs[b]));
-    }
-    if (na > 0) signal_event(P, t.lora_ev, t.tile, P.epoch + (uint32_t)s + 1u);
-    // every mode: the other tiles of this operator run in the same launch
-    if (!wait_event(P, t.lora_ev, P.epoch + (uint32_t)s + 1u, t.tile, m)) return false;
+    if (bpre)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (tid + k * NT < nbq) bl[tid + k * NT] = bq[k];
+    // (the verdict goes through LDS: the workgroup-reduction builtins reserve static LDS, and the
+    // workers take all of it dynamically)
+    if (tid == 0) m->lora_fail = 0;
+    __syncthreads();
+    bool ok = true;
     for (int i = tid; i < NB * nA; i += NT) {
       const int b = i / nA, j = i - b * nA;
-      uu[i] = (double)ldc(ub + (size_t)b * 3 * lr + j);
+      const TV* up = ub + (size_t)b * 3 * lr + j;
+      uint64_t v = ld_tv(up);
+      for (uint32_t polls = 0; !tv_ok(v, utag);) {
+        if (++polls >= P.watchdog || ldc_u(P.status + ST_ABORT)) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = ld_tv(up);
+      }
+      uu[i] = (double)__uint_as_float((uint32_t)v);
+    }
+    if (!ok) {
+      uint32_t zero = 0u;
+      if (__hip_atomic_compare_exchange_strong((GAS uint32_t*)(P.status + ST_CODE), &zero, ERR_WATCHDOG,
+                                               __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        stc_u(P.status + ST_CU, blockIdx.x);
+        stc_u(P.status + ST_TASK, t.tile);
+        stc_u(P.status + ST_EVENT, t.lora_ev);
+      }
+      stc_u(P.status + ST_ABORT, 1u);
+      m->lora_fail = 1;
     }
     __syncthreads();
+    if (m->lora_fail) return false;
   }
   // B row `row` of Bm [rows][r] against u[b][seg, seg + r), summed in fp64 in order (exact products)
-  auto lora_term = [&](const uint16_t* Bm, int row, int seg, int b) -> double {
-    const uint16_t* br = Bm + (size_t)row * lr;
+  // tile row `row` (as brow) against u[b][seg, seg + r), in fp64 in order (exact products)
+  auto lora_term = [&](int row, int seg, int b) -> double {
+    const uint16_t* br = brow(row);
     const double* ur = uu + b * nA + seg;
     double acc = 0.0;
     for (int j = 0; j < lr; j += 8) {
-      const uint4 q = ldg((const uint4*)(br + j));
+      const uint4 q = bpre ? bl[row * bper + j / 8] : ldg((const uint4*)(br + j));
       const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -833,10 +913,10 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   if (op == OP_QKV) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      double v = red[ul * NB + b] * rs[b];
+      double v = red[wbase + ul * NB + b] * rs[b];
       if (lora) {  // the row's adapter: q, k or v by its place in the KV-head group
-        const int row = u0 + ul, gi = row % P.RG;
-        v += lora_term(LW.b_qkv, row, gi < P.G * P.D ? 0 : gi < (P.G + 1) * P.D ? lr : 2 * lr, b);
+        const int gi = (u0 + ul) % P.RG;
+        v += lora_term(ul, gi < P.G * P.D ? 0 : gi < (P.G + 1) * P.D ? lr : 2 * lr, b);
       }
       stc(P.qkv + (size_t)b * P.QKVR + u0 + ul, (float)v);
     }
@@ -844,18 +924,18 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
       float* xp = P.x + (size_t)b * P.H + u0 + ul;
-      double y = red[ul * NB + b];
-      if (lora) y += lora_term(op == OP_WO ? LW.b_o : LW.b_d, u0 + ul, 0, b);
+      double y = red[wbase + ul * NB + b];
+      if (lora) y += lora_term(ul, 0, b);
       stc(xp, (float)((double)(i == tid ? xpre : ldc(xp)) + y));
     }
   } else if (op == OP_GU) {
     for (int i = tid; i < nu * NB; i += NT) {
       const int ul = i / NB, b = i - ul * NB;
-      double gt = red[(ul * 2) * NB + b] * rs[b];
-      double up = red[(ul * 2 + 1) * NB + b] * rs[b];
+      double gt = red[wbase + (ul * 2) * NB + b] * rs[b];
+      double up = red[wbase + (ul * 2 + 1) * NB + b] * rs[b];
       if (lora) {
-        gt += lora_term(LW.b_g, u0 + ul, 0, b);
-        up += lora_term(LW.b_u, u0 + ul, lr, b);
+        gt += lora_term(2 * ul, 0, b);
+        up += lora_term(2 * ul + 1, lr, b);
       }
       stc(P.a + (size_t)b * P.F + u0 + ul, (float)(silu_d(gt) * up));
     }
@@ -1244,20 +1324,12 @@ __device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& 
 // a worker per attention task, by every active split for a slice of the
 // outputs (the forms are described with att_dist).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void st_tv(TV* p, uint32_t bits, uint32_t tag) {
-  const uint64_t w = ((uint64_t)tag << 32) | bits;
-  __hip_atomic_store((GAS uint64_t*)p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_tv(const TV* p) {
-  return __hip_atomic_load((const GAS uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // the same coherent 8-byte load through a buffer resource: one 32-bit lane offset
 // and a scalar offset, so a burst of such loads holds no 64-bit addresses
 __device__ __forceinline__ uint64_t ld_tv_b(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 16 /* sc1 */);
   return ((uint64_t)v.y << 32) | v.x;
 }
-__device__ __forceinline__ bool tv_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 // an fp64 value as two tagged words: p[0] low half, p[1] high half
 __device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
   st_tv(p, (uint32_t)__double2loint(v), tag);
@@ -1273,8 +1345,15 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   constexpr int D = LPP * 8, PPB = NT / LPP;
   const int Hkv = P.Hkv, S = P.S;
   const int bg = (int)t.a0, b = bg / Hkv, g = bg - b * Hkv, sp = (int)t.a1, l = (int)t.layer;
-  const int pos = P.pos0 + s, N = pos + 1;
-  const int n_act = att_active(P, s);
+  // prefill graph: virtual sequence b is token pos0 + s chunk + b of sequence kv_seq, whose keys and
+  // values an append task has already written to the cache; padding tokens only signal
+  const bool chunked = P.chunk > 0;
+  const int pos = chunked ? P.pos0 + s * P.chunk + b : P.pos0 + s, N = pos + 1;
+  if (chunked && pos >= P.pos_end) {
+    if (sp == 0) signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+    return true;
+  }
+  const int n_act = (pos + S) / S;  // splits holding positions 0..pos
   constexpr int MCH = ATT_MCH;  // single merger: accumulator splits in flight per thread
   const bool dist = att_dist(P);
   const bool slice = dist && n_act > MCH;
@@ -1290,20 +1369,22 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   }
   const int tid = ltid(), lane = tid & 63, w = tid >> 6;
   const int j0 = sp * S, j1 = min(j0 + S, N);
-  const bool has_cur = (j1 == N);  // this split holds the current position (and appends it)
-  const int jc = has_cur ? pos : j1;  // cached positions [j0, jc)
+  const bool has_cur = (j1 == N);  // this split holds the current position (and merges)
+  const bool cur = has_cur && !chunked;  // ... and computes and appends its key and value (decode)
+  const int jc = cur ? pos : j1;  // cached positions [j0, jc)
   const int lp = tid % LPP, po = tid / LPP;
-  const size_t head = ((size_t)(l * P.B + b) * Hkv + g) * P.max_seq;
+  const size_t head = ((size_t)(l * P.kvB + (chunked ? P.kv_seq : b)) * Hkv + g) * P.max_seq;
   uint16_t* Kh = P.kc + head * D;
   uint16_t* Vh = P.vc + head * D;
   const uint32_t tag = (P.epoch + (uint32_t)s) * P.ntag + t.sig_ev + 1u;
 
-  // cached K/V do not depend on this step: load them before waiting
+  // cached K/V do not depend on this step: load them before waiting (decode; in the prefill
+  // graph they were written in this launch by other compute units, and are read after the wait)
   uint4 kr[NL], vr[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int j = j0 + po + i * PPB;
-    if (po + i * PPB < S && j < jc) {
+    if (!chunked && po + i * PPB < S && j < jc) {
       kr[i] = ld16(Kh + (size_t)j * D + lp * 8);
       vr[i] = ld16(Vh + (size_t)j * D + lp * 8);
     } else {
@@ -1320,7 +1401,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
 
   // so do this thread's RoPE factors (and QK-norm gains): item tid is (head tid / (D/2), pair tid % (D/2))
   constexpr int half = D / 2;
-  const int nh = G + (has_cur ? 1 : 0);  // heads to rotate (q heads, then k)
+  const int nh = G + (cur ? 1 : 0);  // heads to rotate (q heads, then k)
   const bool rot = !reuse && tid < nh * half;
   const int rh = tid / half, rk = tid - rh * half;
   double rc = 0.0, rsn = 0.0, g0 = 1.0, g1 = 1.0;
@@ -1337,6 +1418,22 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
 
   // (with dist a worker holds at most one attention task of a layer: nothing to reuse)
   if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr, false, !dist)) return false;
+  if (chunked) {  // device-coherent loads of this launch's appends (two 8-byte halves)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int j = j0 + po + i * PPB;
+      if (po + i * PPB < S && j < jc) {
+        const uint64_t* kp = (const uint64_t*)(Kh + (size_t)j * D + lp * 8);
+        const uint64_t* vp = (const uint64_t*)(Vh + (size_t)j * D + lp * 8);
+        const uint64_t k0 = __hip_atomic_load((const GAS uint64_t*)kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t k1 = __hip_atomic_load((const GAS uint64_t*)(kp + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t v0 = __hip_atomic_load((const GAS uint64_t*)vp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t v1 = __hip_atomic_load((const GAS uint64_t*)(vp + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        kr[i] = make_uint4((uint32_t)k0, (uint32_t)(k0 >> 32), (uint32_t)k1, (uint32_t)(k1 >> 32));
+        vr[i] = make_uint4((uint32_t)v0, (uint32_t)(v0 >> 32), (uint32_t)v1, (uint32_t)(v1 >> 32));
+      }
+    }
+  }
 
   float* raw = (float*)lds;                    // [(G+2) D]: q heads, k, v as stored (fp32)
   double* qrot = (double*)(raw + (G + 2) * D); // [G D]
@@ -1381,7 +1478,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
       kcur[k + half] = f2bf((float)y1);
     }
   }
-  if (has_cur)
+  if (cur)
     for (int i = tid; i < D; i += NT) vcur[i] = vsm[(pos - j0) * D + i] = f2bf(raw[(G + 1) * D + i]);
   if (QR && tid == 0) {
     m->qk_step = qk_step;
@@ -1393,7 +1490,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   // one at a time so that only one head's query slice and sums occupy registers.
   // The current position's key (rotated above) joins the cached ones first.
   const int n = j1 - j0;
-  if (has_cur)
+  if (cur)
 #pragma unroll
     for (int i = 0; i < NL; ++i)
       if (j0 + po + i * PPB == pos) kr[i] = *(const uint4*)(kcur + lp * 8);
@@ -1669,7 +1766,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
   // the signal below; issued here, the stores complete alongside those of o
   // instead of stalling the scores (a store's registers are reusable only
   // once it has completed).
-  if (has_cur && tid < LPP) {
+  if (cur && tid < LPP) {
     stg((uint4*)(Kh + (size_t)pos * D + tid * 8), *(const uint4*)(kcur + tid * 8));
     stg((uint4*)(Vh + (size_t)pos * D + tid * 8), *(const uint4*)(vcur + tid * 8));
   }
@@ -1707,9 +1804,65 @@ __device__ __forceinline__ bool attn_nl(const KParams& P, const TaskRec& t, int 
 // access).  Until it is, GEMV tasks run as per-task GEMVs (task_gemv).
 constexpr bool kStreamEngine = false;
 
+// Prefill graph: the rotated keys and the values of one KV-head group, for every token of the chunk,
+// go to the cache with device-coherent stores (the attention tasks that read them run on other
+// compute units of the same launch).  The arithmetic is a decoding attention task's for its current
+// position: QK-norm with the same fp64 lane sums and wave tree, RoPE in fp64, the key rounded to
+// fp32 and then bf16, the value to bf16.  One wave per token.
+__device__ __forceinline__ bool task_append(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
+                                            uint64_t* tr) {
+  const int g = (int)t.a0, l = (int)t.layer, D = P.D, half = D / 2, C = P.chunk;
+  const int tid = ltid(), lane = tid & 63, w = tid >> 6;
+  Misc* m = (Misc*)(lds + P.misc_off);
+  if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr)) return false;
+  uint16_t* kst = (uint16_t*)lds;  // [C][D] rotated keys, bf16
+  uint16_t* vst = kst + C * D;     // [C][D] values, bf16
+  const LayerW LW = ldg(P.layers + l);
+  for (int b = w; b < C; b += NW) {
+    const int pos = P.pos0 + s * C + b;
+    if (pos >= P.pos_end) continue;
+    const float* kraw = P.qkv + (size_t)b * P.QKVR + (size_t)g * P.RG + (size_t)P.G * D;
+    const float* vraw = kraw + D;
+    double hr = 1.0;
+    if (P.qk_norm) {
+      double ss = 0.0;
+      for (int d = lane; d < D; d += 64) {
+        const double x = (double)ldc(kraw + d);
+        ss += x * x;
+      }
+      ss = wave_sum_d(ss);
+      hr = 1.0 / sqrt(ss / (double)D + (double)P.eps);
+    }
+    for (int k = lane; k < half; k += 64) {
+      double x0 = (double)ldc(kraw + k), x1 = (double)ldc(kraw + k + half);
+      if (P.qk_norm) {
+        x0 = (x0 * hr) * (double)bf1(ldg(LW.k_norm + k));
+        x1 = (x1 * hr) * (double)bf1(ldg(LW.k_norm + k + half));
+      }
+      const double rc = ldg(P.rope_cos + (size_t)pos * half + k), rsn = ldg(P.rope_sin + (size_t)pos * half + k);
+      const double y0 = x0 * rc - x1 * rsn, y1 = x0 * rsn + x1 * rc;
+      kst[b * D + k] = f2bf((float)y0);
+      kst[b * D + k + half] = f2bf((float)y1);
+    }
+    for (int d = lane; d < D; d += 64) vst[b * D + d] = f2bf(ldc(vraw + d));
+  }
+  __syncthreads();
+  const size_t head = ((size_t)(l * P.kvB + P.kv_seq) * P.Hkv + g) * P.max_seq;
+  for (int i = tid; i < C * D / 2; i += NT) {
+    const int b = (2 * i) / D, e = 2 * i - b * D;
+    const int pos = P.pos0 + s * C + b;
+    if (pos >= P.pos_end) continue;
+    stc_u((uint32_t*)(P.kc + (head + pos) * D + e), *(const uint32_t*)(kst + b * D + e));
+    stc_u((uint32_t*)(P.vc + (head + pos) * D + e), *(const uint32_t*)(vst + b * D + e));
+  }
+  signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+  return true;
+}
+
 template <int NB, bool LO>
 __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                          uint64_t* tr = nullptr) {
+  if (t.op == OP_APPEND) return task_append(P, t, s, mega, lds, tr);
   if (t.op == OP_ATTN) {
     constexpr bool QR = NB < 8;  // at B >= 8 the matrix-core GEMV leaves no registers for it
     if (P.D == 64) {
@@ -1769,8 +1922,8 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
       }
     }
   }
-  if (blockIdx.x == 0) {
-    // last step's token: wait for every LM tile of the final step
+  if (blockIdx.x == 0 && P.chunk == 0) {
+    // last step's token: wait for every LM tile of the final step (the prefill graph has none)
     Misc* m = (Misc*)(lds + P.misc_off);
     const uint32_t ev_lm = (uint32_t)(P.L * (P.Hkv + 4));
     if (!wait_event(P, ev_lm, P.epoch + (uint32_t)P.n_steps, 0xffffffffu, m)) return;

@@ -19,6 +19,7 @@ enum Op : uint32_t {
   OP_GU = 4,    // norm + gate/up row pairs + SwiGLU
   OP_DOWN = 5,  // down-projection rows + residual
   OP_LM = 6,    // final norm + LM-head rows + per-tile argmax
+  OP_APPEND = 7,  // prefill: QK-norm + RoPE of a KV-head group's keys for every token of the chunk, K/V append
 };
 
 constexpr uint32_t EV_NONE = 0xffffffffu;
@@ -131,7 +132,7 @@ struct KParams {
   TV* part_ml;      // [B][Hkv][NS][G][2][2] split max and sum (fp64 as two tagged words)
   TV* part_acc;     // [B][Hkv][NS][G][D][2] split unnormalised P.V (fp64 as two tagged words)
   LmPart* lm_part;    // [B][n_lm]
-  float* lora_u;      // [4 operators][B][3 r]: the adapters' A x of the current GEMV operator
+  TV* lora_u;         // [4 operators][B][3 r]: the adapters' A x of the current GEMV operator (fp32, step-tagged)
   // tokens
   int32_t* pending;           // [B]
   int32_t* out_tokens;        // [n_steps][B] or null
@@ -155,6 +156,10 @@ struct KParams {
   uint32_t ntag;             // tag period: number of events
   // per-operator launch
   int32_t op_first, op_count, op_range, step;
+  // prefill graph (chunk > 0): virtual sequence b of step s is token pos0 + s chunk + b of real
+  // sequence kv_seq (of kvB in the cache layout); tokens at or past pos_end are padding.
+  // Decode: chunk = 0, kvB = B, and virtual sequence b is cache sequence b.
+  int32_t chunk, kv_seq, kvB, pos_end;
   // optional trace of one decode step: [worker][list index][4] wall-clock stamps
   uint64_t* trace;
   int32_t trace_step, trace_stride;

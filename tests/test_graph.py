@@ -176,7 +176,7 @@ def test_graph_invariants(shape, B, max_seq, workers, split):
             assert t[4] // RG == (t[5] - 1) // RG
 
 
-def simulate(g, shape, B, steps, start_pos, seed, drop=None):
+def simulate(g, shape, B, steps, start_pos, seed, drop=None, early=None, violations=None):
     """Run every worker's list under random interleaving with the event rules, one flag per slot
     holding the number of steps its producer signalled; returns True if all steps complete, False
     on deadlock.  Attention splits beyond the current length do nothing.  A merging split stores
@@ -184,7 +184,12 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None):
     signals; a split that does not merge stores and moves on without signalling.  The split
     holding the current position merges; with the attention tasks distributed (one slot per task)
     and more than 8 active splits, every active split merges a slice, and a wait on the attention
-    event reads only the slots of the step's merging splits."""
+    event reads only the slots of the step's merging splits.
+
+    Data check: a task's results count as written when it completes; a consumer that passes its
+    wait records, in `violations`, every waited slot whose last signaller has not completed that
+    step.  `early`: a task that signals before it completes (an early release), as two separate
+    moves of its worker, so that consumers may run in between."""
     rnd = random.Random(seed)
     tasks, events = g["tasks"], g["events"]
     workers, S, Hkv = g["workers"], g["split"], shape.n_kv_heads
@@ -196,6 +201,9 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None):
     stored = [False] * workers     # a merging split has stored and waits for its head's others
     pos = [0] * workers            # (step * len(list) + index)
     total = [steps * len(lst) for lst in lists]
+    completed = {}                 # topo index -> steps completed
+    signaller = {}                 # (event, slot) -> topo index of the last task that signalled it
+    released = [False] * workers   # the early-release task has signalled but not completed
 
     def n_active(step):
         return -(-(start_pos + step + 1) // S)
@@ -232,6 +240,19 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None):
         w = rnd.choice(ready)
         step, i = divmod(pos[w], len(lists[w]))
         t = lists[w][i]
+        if released[w]:  # the early-release task completes now
+            released[w] = False
+            completed[t[0]] = step + 1
+            pos[w] += 1
+            continue
+        if violations is not None and t[6] != 0xFFFFFFFF and not stored[w] and not (
+                t[1] == OP_ATTN and t[5] >= n_active(step)):
+            target = step + 1 - t[8]
+            if target > 0:
+                for sl in slots(t[6], step - t[8]):
+                    src = signaller.get((t[6], sl))
+                    if src is not None and completed.get(src, 0) < target:
+                        violations.append((t[0], src, step))
         signal = True
         if t[1] == OP_ATTN:
             if t[5] >= n_active(step):
@@ -245,10 +266,15 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None):
                 signal = False
             else:
                 stored[w] = False
-        pos[w] += 1
+        if early is not None and t[0] == early:  # signal now, complete on the worker's next move
+            released[w] = True
+        else:
+            completed[t[0]] = step + 1
+            pos[w] += 1
         if signal and not (drop is not None and t[0] == drop):
             assert flags.get((t[9], t[10]), 0) <= step, "slot signalled twice in a step"
             flags[(t[9], t[10])] = step + 1
+            signaller[(t[9], t[10])] = t[0]
 
 
 @pytest.mark.parametrize("workers,split,seed", [(8, 16, 0), (13, 8, 1), (37, 32, 2), (40, 8, 4), (20, 8, 5)])
@@ -265,6 +291,30 @@ def test_event_protocol_with_slice_merges(steps, start_pos, seed):
     g = parse(mk.mk_build_graph(cfg_of(shape, 2, 40, 2), 96))
     assert g["ns"] * 2 * shape.n_kv_heads <= 96
     assert simulate(g, shape, 2, steps=steps, start_pos=start_pos, seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_no_consumer_reads_unfinished_results_in_simulation(seed):
+    shape = ModelShape(2, 128, 4, 2, 64, 96, 100)
+    for workers, split in ((8, 16), (37, 8)):
+        g = parse(mk.mk_build_graph(cfg_of(shape, 1, 40, split), workers))
+        bad = []
+        assert simulate(g, shape, 1, steps=3, start_pos=5, seed=seed, violations=bad)
+        assert bad == []
+
+
+def test_early_release_is_caught_in_simulation():
+    # a GEMV tile that signals before its results are written: some interleaving lets a consumer
+    # pass its wait in between, and the data check sees it
+    shape = ModelShape(2, 128, 4, 2, 64, 96, 100)
+    g = parse(mk.mk_build_graph(cfg_of(shape, 1, 40, 16), 8))
+    victim = next(t[0] for t in g["tasks"] if t[1] == OP_WO and t[2] == 0)
+    caught = 0
+    for seed in range(20):
+        bad = []
+        assert simulate(g, shape, 1, steps=2, start_pos=5, seed=seed, early=victim, violations=bad)
+        caught += any(src == victim for _, src, _ in bad)
+    assert caught > 0
 
 
 def test_dropped_signal_deadlocks_in_simulation():
