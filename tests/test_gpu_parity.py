@@ -170,3 +170,34 @@ def test_k_sliced_batches_match_oracle(batch, prompt, steps):
     say(f"wide batch={batch}: K-sliced activation staging")
     w, s, (toks, logits) = run_prompt_case(WIDE, batch, prompt, steps)
     check_against_oracle(WIDE, w, s, toks, logits, steps, f"wide-b{batch}", n_threads=16)
+
+
+@pytest.mark.parametrize("batch,shape", [(1, TINY), (4, TINY), (16, WIDE)])
+def test_argmax_ties_go_to_the_lowest_index(batch, shape):
+    # Two LM-head rows made identical and dominant: their logits are equal and the largest, so the
+    # greedy token must be the lower row at every step, for every sequence.  The two rows sit in
+    # different LM tiles (the tie crosses the per-tile partial maxima).
+    say(f"argmax tie-break batch={batch}")
+    weights = synth.make_weights(shape, seed=3, device="cuda")
+    V = shape.vocab
+    lo_row, hi_row = 5, V - 7
+    named = dict(weights)
+    lm = named["lm_head"].clone()
+    lm[hi_row] = lm[lo_row] = (lm[lo_row].float() * 50.0).to(torch.bfloat16)
+    weights = [(n, lm if n == "lm_head" else t) for n, t in weights]
+    seqs = synth.make_sequences(shape, batch, 9, 0, seed=3)
+    eng = mk.Engine(shape, batch=batch, max_seq=8 + 6)
+    try:
+        eng.load_weights(weights)
+        eng.prefill(seqs["prompts"].numpy())
+        toks, logits = eng.decode(6)
+        torch.cuda.synchronize()
+        toks, logits = toks.cpu().numpy(), logits.cpu().numpy()
+    finally:
+        eng.close()
+    if batch < 8:  # one fp64 sum per row: identical rows give identical bits
+        assert np.array_equal(logits[..., lo_row].view(np.uint32), logits[..., hi_row].view(np.uint32))
+    top = logits.max(axis=-1)
+    tied = (logits[..., lo_row] == top) & (logits[..., hi_row] == top)
+    assert tied.any(), "the planted rows never held the maximum"
+    assert np.all(toks[tied] == lo_row)
