@@ -254,6 +254,15 @@ int mk_set_trace(mk_ctx* ctx, int step);
 int mk_get_trace(mk_ctx* ctx, uint64_t* out, size_t* len, int32_t* n_workers, int32_t* max_list,
                  int32_t* clock_khz);
 
+/* Canary (diagnostics): fill the context's scratch -- the activations x,
+ * q/k/v, o and a, the LM-head partial maxima, the step-tagged attention
+ * partials and LoRA sums -- with all-ones bytes (NaN, and tags no step
+ * uses).  A correct decode writes every such value before reading it, so
+ * its tokens and logits are unchanged; a read before a write shows up as
+ * NaN or a wait that never ends.  Event slots, the KV cache, positions and
+ * pending tokens are left alone.  Synchronous.  Errors: INVALID_ARG, HIP. */
+int mk_debug_poison(mk_ctx* ctx);
+
 /* Text of the last error on ctx (or of the last failed mk_create when ctx
  * is NULL).  Owned by the library; valid until the next call on ctx. */
 const char* mk_last_error(mk_ctx* ctx);

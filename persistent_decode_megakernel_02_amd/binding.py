@@ -53,7 +53,7 @@ EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_prefill_noalloc", "
            "mk_set_prefill", "mk_get_state",
            "mk_get_config",
            "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
-           "mk_read_bandwidth", "mk_copy_bandwidth",
+           "mk_read_bandwidth", "mk_copy_bandwidth", "mk_debug_poison",
            "mk_last_error", "mk_destroy"]
 
 _lib = None
@@ -76,6 +76,7 @@ def lib():
         L.mk_decode.argtypes = [vp, C.c_int, vp, vp]
         L.mk_set_mode.argtypes = [vp, C.c_int]
         L.mk_set_prefill.argtypes = [vp, C.c_int]
+        L.mk_debug_poison.argtypes = [vp]
         L.mk_get_state.argtypes = [vp, C.POINTER(i32), C.POINTER(i32)]
         L.mk_get_config.argtypes = [vp, C.POINTER(MkModelCfg)]
         L.mk_get_graph.argtypes = [vp, vp, C.POINTER(sz)]
@@ -215,6 +216,10 @@ def mk_decode(ctx, n_steps: int, out_tokens, out_logits=None):
 
 def mk_set_mode(ctx, mode: int):
     _check(lib().mk_set_mode(ctx, mode), ctx)
+
+
+def mk_debug_poison(ctx):
+    _check(lib().mk_debug_poison(ctx), ctx)
 
 
 def mk_set_prefill(ctx, prefill: int):

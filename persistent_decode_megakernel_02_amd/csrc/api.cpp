@@ -906,6 +906,23 @@ int mk_set_mode(mk_ctx* c, int mode) {
   return MK_OK;
 }
 
+int mk_debug_poison(mk_ctx* c) {
+  if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
+  const mk_model_cfg& cfg = c->cfg;
+  const size_t B = (size_t)cfg.batch, QD = (size_t)cfg.n_q_heads * cfg.head_dim;
+  const size_t QKVR = QD + 2 * (size_t)cfg.n_kv_heads * cfg.head_dim;
+  HIPCHK(c, hipMemsetAsync(c->x, 0xff, B * cfg.hidden * 4, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->qkv, 0xff, B * QKVR * 4, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->o, 0xff, B * QD * 4, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->a, 0xff, B * cfg.ffn * 4, c->stream));
+  HIPCHK(c, hipMemsetAsync(c->lm_part, 0xff, B * c->g.n_lm * sizeof(LmPart), c->stream));
+  HIPCHK(c, hipMemsetAsync(c->part_ml, 0xff, c->n_part_ml * sizeof(TV), c->stream));
+  HIPCHK(c, hipMemsetAsync(c->part_acc, 0xff, c->n_part_acc * sizeof(TV), c->stream));
+  if (c->lora_u) HIPCHK(c, hipMemsetAsync(c->lora_u, 0xff, c->n_lora_u * sizeof(TV), c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  return MK_OK;
+}
+
 int mk_set_prefill(mk_ctx* c, int prefill) {
   if (!c) return fail(nullptr, MK_ERR_INVALID_ARG, "null ctx");
   if (prefill != MK_PREFILL_PER_OP && prefill != MK_PREFILL_MEGAKERNEL) return fail(c, MK_ERR_INVALID_ARG, "unknown prefill mode");

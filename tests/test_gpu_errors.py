@@ -91,3 +91,31 @@ def test_exhausted_poll_budget_ends_the_launch_with_a_timeout():
     # the GPU keeps decoding correctly
     t_after, _ = _decode_fresh(weights, prompt, max_seq, n)
     assert np.array_equal(t_after, t_ref)
+
+
+@pytest.mark.parametrize("batch,lora", [(1, 0), (4, 16), (16, 0)])
+def test_nan_canaries_in_scratch_are_never_read(batch, lora):
+    # Scratch filled with NaN (and tags no step uses) after the prefill: the decode writes every
+    # activation and partial before reading it, so tokens and logits equal a clean context's.
+    from dataclasses import replace
+    from persistent_decode_megakernel_02_amd.configs import ModelShape
+    shape = replace(TINY, lora_rank=lora) if batch < 8 else ModelShape(2, 512, 8, 2, 64, 1024, 1000)
+    print(f"[case] NaN canaries batch={batch} lora={lora}", flush=True)
+    weights = synth.make_weights(shape, seed=4, device="cuda")
+    seqs = synth.make_sequences(shape, batch, 11, 0, seed=4)
+    outs = []
+    for poison in (False, True):
+        eng = mk.Engine(shape, batch=batch, max_seq=10 + 8)
+        try:
+            eng.load_weights(weights)
+            eng.prefill(seqs["prompts"].numpy())
+            if poison:
+                mk.mk_debug_poison(eng.ctx)
+            toks, logits = eng.decode(8)
+            torch.cuda.synchronize()
+            outs.append((toks.cpu().numpy(), logits.cpu().numpy()))
+        finally:
+            eng.close()
+    assert np.all(np.isfinite(outs[1][1]))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
