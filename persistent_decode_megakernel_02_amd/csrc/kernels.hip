@@ -986,7 +986,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
 // wave's share of K.  The eight waves split every K slice and their partial
 // sums are added in fp64.
 // K goes through LDS in slices of MK_KS elements, staged as fp32 x * gamma
-// (layout [8-element block][half][column][4 x fp32]) and split into the three pieces
+// (layout [8-element block][column][8 x fp32]) and split into the three pieces
 // when a step reads them.  K is padded to whole slices: the padding's
 // activations are zero and its weight loads re-read the row's last chunk.
 // Each wave takes MK_KS / 8 elements (MK_SPS steps of 32) of every slice.  Rows
@@ -1076,11 +1076,9 @@ __device__ __forceinline__ void mfma_stage(const KParams& P, const float* src, i
 #pragma unroll
         for (int e = 0; e < 8; ++e) xv[e] = 0.f;
       }
-      // layout [8-element block][half][column][4 fp32]: a 16-lane phase of the operand reads
-      // covers 256 contiguous bytes, so no two of its lanes share a bank
-      char* xb = lds + (size_t)(c * 32 + jcol) * 16;
+      char* xb = lds + (size_t)(c * 16 + jcol) * 32;
       *(v4f*)(xb) = v4f{xv[0], xv[1], xv[2], xv[3]};
-      *(v4f*)(xb + 256) = v4f{xv[4], xv[5], xv[6], xv[7]};
+      *(v4f*)(xb + 16) = v4f{xv[4], xv[5], xv[6], xv[7]};
     }
   }
 }
@@ -1174,8 +1172,8 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
 #pragma unroll
         for (int b = 0; b < NBUF; ++b) {
           const int cblk = (w * (MK_KS / NW) + 32 * (st0 + b)) / 8 + lq;  // 8-element block of this lane
-          const char* xb = lds + (size_t)(cblk * 32 + li) * 16;
-          const v4f xa = *(const v4f*)(xb), xc = *(const v4f*)(xb + 256);
+          const char* xb = lds + (size_t)(cblk * 16 + li) * 32;
+          const v4f xa = *(const v4f*)(xb), xc = *(const v4f*)(xb + 16);
           const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xc.x, xc.y, xc.z, xc.w};
           uint32_t p0[8], p1[8], p2[8];
 #pragma unroll
