@@ -208,10 +208,13 @@ int mk_get_state(mk_ctx* ctx, int32_t* pos, int32_t* pending);
  * other calls read and write.  Errors: INVALID_ARG. */
 int mk_get_config(mk_ctx* ctx, mk_model_cfg* out);
 
-/* Canonical little-endian serialisation of the task graph (header, event
- * table, task table in topological order).  If buf is NULL or *len is too
- * small, *len receives the size needed and MK_ERR_INVALID_ARG is returned
- * when buf is non-NULL. */
+/* Canonical little-endian serialisation of the decode task graph, u32 words:
+ * header 'MKG1', version 2, n_workers, split, n_splits, n_events, n_tasks,
+ * n_slots; per event (id, fanin, first slot); per task in topological order
+ * (index, op, layer, tile, a0, a1, wait event, its fanin, wait lag, signal
+ * event, signal slot, worker, LoRA unit range la0, la1, LoRA event).  If
+ * buf is NULL or *len is too small, *len receives the size needed and
+ * MK_ERR_INVALID_ARG is returned when buf is non-NULL. */
 int mk_get_graph(mk_ctx* ctx, void* buf, size_t* len);
 
 /* Build the canonical graph bytes for cfg with n_workers workgroups without

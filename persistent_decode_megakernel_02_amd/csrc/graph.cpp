@@ -137,6 +137,8 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
 
   // LoRA: each GEMV operator of a layer spreads the A rows (units) of its adapters over its first
   // tiles, q per tile; QKV 3r rows (A_q, A_k, A_v), WO r, GU r (A_gate, A_up row pairs), DOWN r.
+  // The operator's LoRA event (fan-in: the tiles holding A rows) names the step-tagged sums the
+  // holders publish; the kernel polls those tags rather than event slots.
   const int lr = c.lora_rank;
   if (lr < 0 || lr > 64 || lr % 8) return "lora_rank must be 0 or a multiple of 8 up to 64";
 

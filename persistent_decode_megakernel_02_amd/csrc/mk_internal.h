@@ -35,8 +35,10 @@ struct TaskRec {
   uint32_t sig_ev;    // event notified (slot sig_slot)
   uint32_t sig_slot;
   // LoRA (GEMV operators of a model with adapters): the tile also computes the adapters' A rows
-  // [la0, la1) of its operator, publishes them on event lora_ev (slot = tile), and waits for all of
-  // them before its epilogue.  lora_ev is EV_NONE without adapters.
+  // [la0, la1) of its operator and publishes their sums as words tagged with the step and lora_ev;
+  // it reads all of them before its epilogue.  lora_ev, an event whose fan-in counts the tiles
+  // holding A rows, names the operator's sums (their tag); no slot of it is signalled.  EV_NONE
+  // without adapters.
   uint32_t la0, la1, lora_ev;
 };
 static_assert(sizeof(TaskRec) == 48, "TaskRec layout");
