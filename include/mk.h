@@ -221,6 +221,13 @@ int mk_get_graph(mk_ctx* ctx, void* buf, size_t* len);
  * touching any GPU (same rules as mk_create). */
 int mk_build_graph(const mk_model_cfg* cfg, int n_workers, void* buf, size_t* len);
 
+/* The same for the megakernel prefill's graph: `chunk` prompt tokens per step
+ * (virtual sequences), the decode graph's `split`, an append task (op 7) per
+ * (layer, KV-head group) between QKV and attention, no LM head, and layer 0
+ * waiting on the last layer of the previous step.  Host only.  Errors:
+ * INVALID_ARG, UNSUPPORTED. */
+int mk_build_prefill_graph(const mk_model_cfg* cfg, int n_workers, int chunk, int split, void* buf, size_t* len);
+
 /* Reset the whole context (every sequence): positions and pending tokens to
  * zero, event slots and attention partials cleared, watchdog status cleared;
  * weights, the schedule and the KV cache memory are kept (its contents become

@@ -52,7 +52,7 @@ class MkTensor(C.Structure):
 EXPORTS = ["mk_create", "mk_load_weights", "mk_prefill", "mk_prefill_noalloc", "mk_load_kv", "mk_decode", "mk_set_mode",
            "mk_set_prefill", "mk_get_state",
            "mk_get_config",
-           "mk_get_graph", "mk_build_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
+           "mk_get_graph", "mk_build_graph", "mk_build_prefill_graph", "mk_reset", "mk_last_decode_ms", "mk_set_trace", "mk_get_trace",
            "mk_read_bandwidth", "mk_copy_bandwidth", "mk_debug_poison",
            "mk_last_error", "mk_destroy"]
 
@@ -81,6 +81,7 @@ def lib():
         L.mk_get_config.argtypes = [vp, C.POINTER(MkModelCfg)]
         L.mk_get_graph.argtypes = [vp, vp, C.POINTER(sz)]
         L.mk_build_graph.argtypes = [C.POINTER(MkModelCfg), C.c_int, vp, C.POINTER(sz)]
+        L.mk_build_prefill_graph.argtypes = [C.POINTER(MkModelCfg), C.c_int, C.c_int, C.c_int, vp, C.POINTER(sz)]
         L.mk_reset.argtypes = [vp]
         L.mk_last_decode_ms.argtypes = [vp, C.POINTER(C.c_float)]
         L.mk_read_bandwidth.argtypes = [sz, C.c_int, C.POINTER(C.c_float)]
@@ -246,6 +247,14 @@ def mk_build_graph(cfg: MkModelCfg, n_workers: int) -> bytes:
     _check(lib().mk_build_graph(C.byref(cfg), n_workers, None, C.byref(n)))
     buf = C.create_string_buffer(n.value)
     _check(lib().mk_build_graph(C.byref(cfg), n_workers, buf, C.byref(n)))
+    return buf.raw[: n.value]
+
+
+def mk_build_prefill_graph(cfg: MkModelCfg, n_workers: int, chunk: int, split: int) -> bytes:
+    n = C.c_size_t(0)
+    _check(lib().mk_build_prefill_graph(C.byref(cfg), n_workers, chunk, split, None, C.byref(n)))
+    buf = C.create_string_buffer(n.value)
+    _check(lib().mk_build_prefill_graph(C.byref(cfg), n_workers, chunk, split, buf, C.byref(n)))
     return buf.raw[: n.value]
 
 

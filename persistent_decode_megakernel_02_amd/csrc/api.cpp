@@ -221,6 +221,24 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
 
 extern "C" {
 
+int mk_build_prefill_graph(const mk_model_cfg* cfg, int n_workers, int chunk, int split, void* buf, size_t* len) {
+  if (!cfg || !len) return fail(nullptr, MK_ERR_INVALID_ARG, "null argument");
+  std::string why = validate(*cfg);
+  if (!why.empty()) return fail(nullptr, MK_ERR_INVALID_ARG, why);
+  Graph g;
+  why = build_prefill_graph(*cfg, n_workers, chunk, split, &g);
+  if (!why.empty()) return fail(nullptr, MK_ERR_UNSUPPORTED, why);
+  std::vector<uint8_t> bytes = serialize_graph(*cfg, g);
+  const size_t need = bytes.size();
+  if (!buf || *len < need) {
+    *len = need;
+    return buf ? fail(nullptr, MK_ERR_INVALID_ARG, "buffer too small") : MK_OK;
+  }
+  std::memcpy(buf, bytes.data(), need);
+  *len = need;
+  return MK_OK;
+}
+
 int mk_build_graph(const mk_model_cfg* cfg, int n_workers, void* buf, size_t* len) {
   if (!cfg || !len) return fail(nullptr, MK_ERR_INVALID_ARG, "null argument");
   std::string why = validate(*cfg);

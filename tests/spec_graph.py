@@ -38,13 +38,19 @@ Rules (one decode step; the persistent kernel repeats it every step):
     in layer-major order QKV, WO, GU, DOWN, with fan-in ceil(nA / q) (the holders).  Other tasks:
     la0 = la1 = 0, lora_ev = none.
   * Canonical bytes, version 2: each task row ends with la0, la1, lora_ev.
+  * Prefill graph (chunk > 0): B = chunk virtual sequences, the given split, the plain tiling and
+    placement; after each layer's QKV tasks one append task per KV-head group g (op 7, tile g,
+    a0 = g, on the worker of the group's first QKV tile) waits QKV(l, g) and signals its own event
+    (fan-in 1), numbered after the LM event and the LoRA events, layer-major; attention tasks wait
+    on it instead of QKV(l, g); never "distributed"; no LM tasks (the LM event stays in the table);
+    layer 0 waits X(L-1) of the previous step (lag 1).
 """
 from __future__ import annotations
 
 import struct
 from dataclasses import dataclass
 
-OP_QKV, OP_ATTN, OP_WO, OP_GU, OP_DOWN, OP_LM = 1, 2, 3, 4, 5, 6
+OP_QKV, OP_ATTN, OP_WO, OP_GU, OP_DOWN, OP_LM, OP_APPEND = 1, 2, 3, 4, 5, 6, 7
 EV_NONE = 0xFFFFFFFF
 
 
@@ -66,8 +72,10 @@ class Task:
 
 
 def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0, wo_tiles=0, gu_tiles=0,
-               down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0, lora_rank=0):
+               down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0, lora_rank=0, chunk=0):
     G = Hq // Hkv
+    if chunk:
+        B = chunk
     if split > 0:
         S = split
     else:  # splits of a full cache fill the workers once; 32 <= S <= Smax = 5 * 4096 / D (8 * 4096 / D when G = 1)
@@ -90,7 +98,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
     def place(k, i):
         return (i + k * rot) % workers
     per_layer = Hkv + 4
-    dist = NS * B * Hkv <= workers
+    dist = not chunk and NS * B * Hkv <= workers
 
     def ev(layer, k):
         return layer * per_layer + k
@@ -110,6 +118,10 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
             for op in (OP_QKV, OP_WO, OP_GU, OP_DOWN):
                 fanin.append(-(-n_arows[op] // q[op]))
 
+    ev_app0 = ev_lm + 1 + (4 * L if lora_rank else 0)
+    if chunk:
+        fanin += [1] * (L * Hkv)
+
     def lora_fields(op, layer, tile):
         if not lora_rank or op not in kidx:
             return {}
@@ -122,17 +134,25 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
 
     tasks: list[Task] = []
     for layer in range(L):
-        in_ev, lag = (ev_lm, 1) if layer == 0 else (ev(layer - 1, Hkv + 3), 0)
+        if layer == 0:
+            in_ev, lag = (ev(L - 1, Hkv + 3) if chunk else ev_lm), 1
+        else:
+            in_ev, lag = ev(layer - 1, Hkv + 3), 0
         for g in range(Hkv):
             for i in range(TG):
                 t = g * TG + i
                 tasks.append(Task(OP_QKV, layer, t, g * RG + lo(i, RG, TG), g * RG + lo(i + 1, RG, TG),
                                   in_ev, lag, ev(layer, g), i, place(0, t), **lora_fields(OP_QKV, layer, t)))
+        if chunk:
+            for g in range(Hkv):
+                tasks.append(Task(OP_APPEND, layer, g, g, 0, ev(layer, g), 0, ev_app0 + layer * Hkv + g, 0,
+                                  place(0, g * TG)))
         k = 0
         for s in range(NS):
             for b in range(B):
                 for g in range(Hkv):
-                    tasks.append(Task(OP_ATTN, layer, k, b * Hkv + g, s, ev(layer, g), 0, ev(layer, Hkv),
+                    wait = ev_app0 + layer * Hkv + g if chunk else ev(layer, g)
+                    tasks.append(Task(OP_ATTN, layer, k, b * Hkv + g, s, wait, 0, ev(layer, Hkv),
                                       k if dist else b * Hkv + g, (k + aoff) % workers))
                     k += 1
         for k, (op, R, T, wait, sig) in enumerate(((OP_WO, H, n_wo, Hkv, Hkv + 1), (OP_GU, F, n_gu, Hkv + 1, Hkv + 2),
@@ -140,7 +160,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
             for i in range(T):
                 tasks.append(Task(op, layer, i, lo(i, R, T), lo(i + 1, R, T), ev(layer, wait), 0, ev(layer, sig), i,
                                   place(k, i), **lora_fields(op, layer, i)))
-    for i in range(n_lm):
+    for i in range(0 if chunk else n_lm):
         tasks.append(Task(OP_LM, 0, i, lo(i, V, n_lm), lo(i + 1, V, n_lm), ev(L - 1, Hkv + 3), 0, ev_lm, i,
                           place(4, i)))
     return {"split": S, "n_splits": NS, "fanin": fanin, "tasks": tasks}

@@ -63,6 +63,32 @@ def test_lora_graph_bytes_equal_spec(shape, B, max_seq, workers, split, sched):
     assert all(t[14] == 0xFFFFFFFF for t in g["tasks"] if t[1] in (OP_ATTN, OP_LM))
 
 
+# the megakernel prefill's graph: chunk virtual sequences, the decode graph's split, append tasks
+PREFILL_CASES = [
+    (TINY, 1, 71, 256, 4), (TINY, 2, 40, 37, 4), (replace(TINY, lora_rank=16), 1, 71, 8, 4),
+    (LLAMA8B, 1, 550, 256, 16), (LLAMA8B, 4, 1088, 256, 16), (CHAMELEON7B, 1, 4224, 256, 16),
+]
+
+
+@pytest.mark.parametrize("shape,B,max_seq,workers,chunk", PREFILL_CASES)
+def test_prefill_graph_bytes_equal_spec(shape, B, max_seq, workers, chunk):
+    cfg = cfg_of(shape, B, max_seq, 0)
+    split = struct.unpack("<8I", mk.mk_build_graph(cfg, workers)[:32])[3]  # the decode graph's
+    got = mk.mk_build_prefill_graph(cfg, workers, chunk, split)
+    dims = [getattr(shape, a) for a in SPEC_ARGS]
+    spec = canonical_bytes(spec_graph(*dims, B, max_seq, workers, split, lora_rank=shape.lora_rank, chunk=chunk),
+                           workers)
+    assert got == spec
+    g = parse(got)
+    assert g["split"] == split
+    ops = [t[1] for t in g["tasks"]]
+    assert OP_LM not in ops and ops.count(7) == shape.n_layers * shape.n_kv_heads
+    # per layer: QKV, then the appends, then attention
+    for layer in range(shape.n_layers):
+        idx = {op: [t[0] for t in g["tasks"] if t[1] == op and t[2] == layer] for op in (OP_QKV, 7, OP_ATTN)}
+        assert max(idx[OP_QKV]) < min(idx[7]) and max(idx[7]) < min(idx[OP_ATTN])
+
+
 def test_lora_rank_is_validated():
     for r in (4, 12, 72, -8):
         with pytest.raises(mk.MkError):
