@@ -92,6 +92,12 @@ typedef struct mk_model_cfg {
                          gate/up 2, down 3; LM head 4) runs on worker
                          (i + k * rotate) mod workers                        */
   int32_t attn_offset; /* attention task k runs on worker (k + attn_offset) mod workers */
+  int32_t wo_ksplit, down_ksplit; /* batch >= 8: the O- and down-projection tiles come in
+                         groups of ksplit tasks sharing a row range, each taking a part of K;
+                         the last adds the others' partial sums in order.  0: the plain rule
+                         (batch >= 8: the larger of 4 and 2 that is at most K / 2048 rounded up
+                         and divides the tile count; else none); 1: none; else 2, 4 or 8,
+                         dividing the tile count, at most K / 2048 rounded up */
   /* LoRA (Mirage article, "Case 2: LoRA + Linear"): rank r of an adapter
    * on every projection of every layer (q, k, v, o, gate, up, down), each
    * y = W x + B (A x) computed as one fused GEMV over the concatenation
@@ -209,10 +215,11 @@ int mk_get_state(mk_ctx* ctx, int32_t* pos, int32_t* pending);
 int mk_get_config(mk_ctx* ctx, mk_model_cfg* out);
 
 /* Canonical little-endian serialisation of the decode task graph, u32 words:
- * header 'MKG1', version 2, n_workers, split, n_splits, n_events, n_tasks,
+ * header 'MKG1', version 3, n_workers, split, n_splits, n_events, n_tasks,
  * n_slots; per event (id, fanin, first slot); per task in topological order
  * (index, op, layer, tile, a0, a1, wait event, its fanin, wait lag, signal
- * event, signal slot, worker, LoRA unit range la0, la1, LoRA event).  If
+ * event, signal slot, worker, LoRA unit range la0, la1, LoRA event, split-K
+ * part kp and part count kn; a part below the last signals no event).  If
  * buf is NULL or *len is too small, *len receives the size needed and
  * MK_ERR_INVALID_ARG is returned when buf is non-NULL. */
 int mk_get_graph(mk_ctx* ctx, void* buf, size_t* len);

@@ -89,6 +89,9 @@ struct mk_ctx {
   LmPart* lm_part = nullptr;
   TV* lora_u = nullptr;  // [4][B][3 r] adapter A x of the current GEMV operator (LoRA), step-tagged
   size_t n_lora_u = 0;
+  TV* kpart = nullptr;  // [2][max split - 1][H][16][2] split-K partial row sums, step-tagged
+  size_t n_kpart = 0;
+  int kpart_max = 1;
   int32_t* pending = nullptr;
   int32_t* force = nullptr;
   size_t force_cap = 0;
@@ -420,6 +423,9 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if ((rc = dalloc(c, (void**)&c->lm_part, (size_t)B * c->g.n_lm * sizeof(LmPart)))) return bail(rc);
   c->n_lora_u = (size_t)4 * B * 3 * r;
   if (r && (rc = dalloc(c, (void**)&c->lora_u, c->n_lora_u * sizeof(TV)))) return bail(rc);
+  c->kpart_max = std::max(c->g.wo_ksplit, c->g.down_ksplit);
+  c->n_kpart = (size_t)2 * (c->kpart_max - 1) * H * 16 * 2;
+  if (c->n_kpart && (rc = dalloc(c, (void**)&c->kpart, c->n_kpart * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->pending, (size_t)B * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->flags, (size_t)c->g.n_slots * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->status, 64))) return bail(rc);
@@ -507,6 +513,7 @@ int mk_reset(mk_ctx* c) {
   HIPCHK(c, hipMemsetAsync(c->part_ml, 0, c->n_part_ml * sizeof(TV), c->stream));
   HIPCHK(c, hipMemsetAsync(c->part_acc, 0, c->n_part_acc * sizeof(TV), c->stream));
   if (c->lora_u) HIPCHK(c, hipMemsetAsync(c->lora_u, 0, c->n_lora_u * sizeof(TV), c->stream));
+  if (c->kpart) HIPCHK(c, hipMemsetAsync(c->kpart, 0, c->n_kpart * sizeof(TV), c->stream));
   HIPCHK(c, hipMemsetAsync(c->status, 0, 64, c->stream));
   HIPCHK(c, hipMemsetAsync(c->pending, 0, (size_t)c->cfg.batch * 4, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
@@ -634,6 +641,8 @@ static KParams make_params(mk_ctx* c) {
   P.lm_part = c->lm_part;
   P.lora_u = c->lora_u;
   P.lora_r = cfg.lora_rank;
+  P.kpart = c->kpart;
+  P.kpart_max = c->kpart_max;
   P.pending = c->pending;
   P.flags = c->flags;
   P.events = c->d_events;
@@ -664,9 +673,11 @@ static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
       P.op_count = (int)g.op_ranges[r].count;
       P.op_range = (int)r;
       // cooperative where tasks of one launch wait on each other: attention mergers poll the other
-      // splits' partials, and with LoRA every GEMV tile waits for its operator's adapter rows
+      // splits' partials, with LoRA every GEMV tile waits for its operator's adapter rows, and the
+      // last K part of a split row tile polls the other parts' sums
       const uint32_t op = g.tasks[g.op_ranges[r].first].op;
-      const bool coop = op == OP_ATTN || (c->cfg.lora_rank > 0 && op != OP_LM);
+      const bool coop = op == OP_ATTN || (c->cfg.lora_rank > 0 && op != OP_LM) ||
+                        (op == OP_WO && g.wo_ksplit > 1) || (op == OP_DOWN && g.down_ksplit > 1);
       HIPCHK(c, launch(coop ? 3 : 1, P, c->stream));
     }
   }
@@ -937,6 +948,7 @@ int mk_debug_poison(mk_ctx* c) {
   HIPCHK(c, hipMemsetAsync(c->part_ml, 0xff, c->n_part_ml * sizeof(TV), c->stream));
   HIPCHK(c, hipMemsetAsync(c->part_acc, 0xff, c->n_part_acc * sizeof(TV), c->stream));
   if (c->lora_u) HIPCHK(c, hipMemsetAsync(c->lora_u, 0xff, c->n_lora_u * sizeof(TV), c->stream));
+  if (c->kpart) HIPCHK(c, hipMemsetAsync(c->kpart, 0xff, c->n_kpart * sizeof(TV), c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
   return MK_OK;
 }

@@ -76,6 +76,8 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
     sc.lm_tiles = c.lm_tiles;
     sc.rotate = c.rotate;
     sc.attn_offset = c.attn_offset;
+    sc.wo_ksplit = c.wo_ksplit;
+    sc.down_ksplit = c.down_ksplit;
   } else if (c.schedule == MK_SCHEDULE_FROZEN) {
     sc = frozen_schedule(c, n_workers);
   } else {
@@ -89,7 +91,7 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
   }
   const int B = chunk > 0 ? chunk : c.batch;
   if (sc.qkv_tiles < 0 || sc.wo_tiles < 0 || sc.gu_tiles < 0 || sc.down_tiles < 0 || sc.lm_tiles < 0 || sc.rotate < 0 ||
-      sc.attn_offset < 0)
+      sc.attn_offset < 0 || sc.wo_ksplit < 0 || sc.down_ksplit < 0)
     return "schedule fields must be >= 0";
   if (sc.wo_tiles > n_workers || sc.gu_tiles > n_workers || sc.down_tiles > n_workers || sc.lm_tiles > n_workers)
     return "at most one tile per worker for each GEMV operator";
@@ -124,6 +126,31 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
   g.n_down = tiles(sc.down_tiles, c.hidden);
   g.n_lm = tiles(sc.lm_tiles, c.vocab);
   if ((int64_t)g.n_qkv > n_workers) return "QKV tiles (per group times n_kv_heads) exceed the workers";
+  // split-K of the O- and down-projection (matrix-core GEMV, K in slices of 2048): the operator's
+  // tiles form row tiles of ksplit consecutive tasks, part p taking slices [p nsl / ks, (p+1) nsl / ks)
+  // 0 takes the plain rule: with the matrix-core GEMV (batch >= 8, decode graph) the larger of 4
+  // and 2 that is at most the operator's K slices and divides its tile count, else none.  Every
+  // tile otherwise stages the whole activation; split, a tile stages only its part of K.
+  const int kslices[2] = {(c.n_q_heads * D + 2047) / 2048, (c.ffn + 2047) / 2048};
+  auto plain_ks = [&](int want, int ksl, int tiles) {
+    if (want > 0) return want;
+    if (c.batch < 8 || chunk > 0) return 1;
+    for (int k : {4, 2})
+      if (k <= ksl && tiles % k == 0) return k;
+    return 1;
+  };
+  g.wo_ksplit = plain_ks(sc.wo_ksplit, kslices[0], g.n_wo);
+  g.down_ksplit = plain_ks(sc.down_ksplit, kslices[1], g.n_down);
+  {
+    const int ks[2] = {g.wo_ksplit, g.down_ksplit}, nt[2] = {g.n_wo, g.n_down};
+    for (int k = 0; k < 2; ++k) {
+      if (ks[k] == 1) continue;
+      if (c.batch < 8 || chunk > 0) return "split-K needs the matrix-core GEMV (batch >= 8, decode graph)";
+      if (ks[k] != 2 && ks[k] != 4 && ks[k] != 8) return "split-K must be 1, 2, 4 or 8";
+      if (nt[k] % ks[k]) return "split-K must divide the operator's tile count";
+      if (ks[k] > kslices[k]) return "split-K larger than the operator's K slices";
+    }
+  }
   g.rotate = sc.rotate % n_workers;
   g.attn_offset = sc.attn_offset % n_workers;
   // worker of tile i of the k-th GEMV operator of a layer, and of attention task k
@@ -168,9 +195,9 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
     for (int gg = 0; gg < Hkv; ++gg) g.events[ev_qkv(l, gg)].fanin = TG;
     g.events[ev_att(l)].fanin = dist ? g.n_splits * B * Hkv : B * Hkv;
     for (int gg = 0; gg < Hkv && chunk > 0; ++gg) g.events[ev_app(l, gg)].fanin = 1;
-    g.events[ev_o(l)].fanin = g.n_wo;
+    g.events[ev_o(l)].fanin = g.n_wo / g.wo_ksplit;
     g.events[ev_a(l)].fanin = g.n_gu;
-    g.events[ev_x(l)].fanin = g.n_down;
+    g.events[ev_x(l)].fanin = g.n_down / g.down_ksplit;
   }
   g.events[ev_lm].fanin = g.n_lm;
   for (int l = 0; l < c.n_layers && lr > 0; ++l)
@@ -193,6 +220,8 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
       t.la1 = (uint32_t)std::min<int64_t>((int64_t)(tile + 1) * per_tile[k], n_arows[k]);
       t.lora_ev = ev_lora(layer, k);
     }
+    t.kp = 0;
+    t.kn = 1;
     t.op = op;
     t.layer = (uint32_t)layer;
     t.tile = tile;
@@ -235,9 +264,18 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
                ev_att(l), dist ? idx : (uint32_t)(b * Hkv + gg), place_att(idx));
     range_end(f);
     f = range_begin();
-    for (int i = 0; i < g.n_wo; ++i)
-      push(OP_WO, l, i, tile_lo(i, c.hidden, g.n_wo), tile_lo(i + 1, c.hidden, g.n_wo), ev_att(l), 0, ev_o(l), i,
-           place(1, i));
+    // a split row tile: tasks r ks .. r ks + ks - 1; only its last part signals (slot r)
+    auto split_tiles = [&](uint32_t op, int l_, int n, int ks, int rows, uint32_t wait, uint32_t sig, int k) {
+      const int nr = n / ks;
+      for (int i = 0; i < n; ++i) {
+        const int r = i / ks, p = i - r * ks;
+        push(op, l_, i, tile_lo(r, rows, nr), tile_lo(r + 1, rows, nr), wait, 0, p == ks - 1 ? sig : EV_NONE,
+             p == ks - 1 ? (uint32_t)r : 0u, place(k, i));
+        g.tasks.back().kp = (uint32_t)p;
+        g.tasks.back().kn = (uint32_t)ks;
+      }
+    };
+    split_tiles(OP_WO, l, g.n_wo, g.wo_ksplit, c.hidden, ev_att(l), ev_o(l), 1);
     range_end(f);
     f = range_begin();
     for (int i = 0; i < g.n_gu; ++i)
@@ -245,9 +283,7 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
            place(2, i));
     range_end(f);
     f = range_begin();
-    for (int i = 0; i < g.n_down; ++i)
-      push(OP_DOWN, l, i, tile_lo(i, c.hidden, g.n_down), tile_lo(i + 1, c.hidden, g.n_down), ev_a(l), 0, ev_x(l), i,
-           place(3, i));
+    split_tiles(OP_DOWN, l, g.n_down, g.down_ksplit, c.hidden, ev_a(l), ev_x(l), 3);
     range_end(f);
   }
   if (chunk == 0) {  // the prefill graph has no LM head
@@ -297,15 +333,15 @@ std::string build_prefill_graph(const mk_model_cfg& c, int n_workers, int chunk,
 }
 
 // Canonical bytes: little-endian u32 words.
-//   header: 'MKG1', version 2, n_workers, split, n_splits, n_events, n_tasks, n_slots
+//   header: 'MKG1', version 3, n_workers, split, n_splits, n_events, n_tasks, n_slots
 //   events: id, fanin, slot0
 //   tasks (topological order): topo, op, layer, tile, a0, a1, wait_ev, wait_fanin, wait_lag,
-//                              sig_ev, sig_slot, worker, la0, la1, lora_ev
+//                              sig_ev, sig_slot, worker, la0, la1, lora_ev, kp, kn
 std::vector<uint8_t> serialize_graph(const mk_model_cfg& c, const Graph& g) {
   (void)c;
   std::vector<uint32_t> w;
   w.push_back(0x31474B4Du);
-  w.push_back(2);
+  w.push_back(3);
   w.push_back((uint32_t)g.n_workers);
   w.push_back((uint32_t)g.split);
   w.push_back((uint32_t)g.n_splits);
@@ -334,6 +370,8 @@ std::vector<uint8_t> serialize_graph(const mk_model_cfg& c, const Graph& g) {
     w.push_back(t.la0);
     w.push_back(t.la1);
     w.push_back(t.lora_ev);
+    w.push_back(t.kp);
+    w.push_back(t.kn);
   }
   std::vector<uint8_t> bytes(w.size() * 4);
   for (size_t i = 0; i < w.size(); ++i) {

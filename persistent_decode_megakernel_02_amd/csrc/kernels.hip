@@ -483,6 +483,12 @@ __device__ __forceinline__ uint64_t ld_tv(const TV* p) {
   return __hip_atomic_load((const GAS uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool tv_ok(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+// an fp64 value as two tagged words: p[0] low half, p[1] high half
+__device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
+  st_tv(p, (uint32_t)__double2loint(v), tag);
+  st_tv(p + 1, (uint32_t)__double2hiint(v), tag);
+}
+__device__ __forceinline__ double tvd_val(uint64_t lo, uint64_t hi) { return __hiloint2double((int)(uint32_t)hi, (int)(uint32_t)lo); }
 
 // ---------------------------------------------------------------------------
 // GEMV task: rows [a0, a1) of one weight matrix against B activation vectors.
@@ -1098,7 +1104,10 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
   const bool embed_src = (op == OP_QKV && l == 0);
   const int u0 = (int)t.a0, nu = (int)t.a1 - (int)t.a0;
   const int R = nu * RU, T = (R + 15) >> 4;
-  const int nsl = (K + MK_KS - 1) / MK_KS;
+  // split-K (O- and down-projection): part kp of kn takes the K slices [sl0, sl0 + nsl)
+  const int kp = (int)t.kp, kn = (int)t.kn, nsl_all = (K + MK_KS - 1) / MK_KS;
+  const int sl0 = kp * nsl_all / kn;
+  const int nsl = (kp + 1) * nsl_all / kn - sl0;
   const int npass = (T + MT - 1) / MT;
   const int gsteps = npass * nsl * MK_SPS;  // this wave's steps, over every pass and slice
 
@@ -1107,7 +1116,7 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
     if (g >= gsteps) return;
     const int pass = g / (nsl * MK_SPS), r = g - pass * nsl * MK_SPS;
     const int sl = r / MK_SPS, st = r - sl * MK_SPS;
-    const int kk = min(sl * MK_KS + w * (MK_KS / NW) + 32 * st + 8 * lq, K - 8);
+    const int kk = min((sl0 + sl) * MK_KS + w * (MK_KS / NW) + 32 * st + 8 * lq, K - 8);
 #pragma unroll
     for (int tt = 0; tt < NTB; ++tt) {
       const int row = min((min(pass * MT + tt, T - 1)) * 16 + li, R - 1);
@@ -1158,7 +1167,7 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
 #pragma unroll
     for (int tt = 0; tt < NTB; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int sl = 0; sl < nsl; ++sl) {
-      const int k0 = sl * MK_KS;
+      const int k0 = (sl0 + sl) * MK_KS;
       __syncthreads();  // the previous slice (or pass) is no longer read
       const bool sumsq = norm && pass == 0;
       if (op == OP_WO) mfma_stage<NB>(P, P.o, P.QD, false, nullptr, m, k0, K, false, lds, ss);
@@ -1217,6 +1226,59 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
       double v = 0.0;
       for (int ww = 0; ww < NW; ++ww) v += (double)part[((size_t)ww * MT + tt) * 256 + ri * 16 + b];
       red[rr * NB + b] = v;
+    }
+    if (kn > 1) {
+      // split-K: a part below the last publishes its row sums (fp64, as two words tagged with the
+      // step and the operator's event); the last part adds the others' in order of part, its own
+      // last, polling a word not yet published.  Only the last part runs the epilogue.
+      const int opi = op == OP_WO ? 0 : 1;
+      const uint32_t ev_op = (uint32_t)(l * (P.Hkv + 4) + P.Hkv + (op == OP_WO ? 1 : 3));
+      const uint32_t ktag = (P.epoch + (uint32_t)s) * P.ntag + ev_op + 1u;
+      TV* kb = P.kpart + (size_t)opi * (P.kpart_max - 1) * P.H * 16 * 2;
+      const int prow0 = u0 + tp0 * 16;
+      __syncthreads();  // red complete
+      if (kp < kn - 1) {
+        for (int i = tid; i < rows * NB; i += NT) {
+          const int rr = i / NB, b = i - rr * NB;
+          st_tvd(kb + (((size_t)kp * P.H + prow0 + rr) * 16 + b) * 2, red[rr * NB + b], ktag);
+        }
+        continue;  // next pass
+      }
+      bool ok = true;
+      for (int i = tid; i < rows * NB; i += NT) {
+        const int rr = i / NB, b = i - rr * NB;
+        double v = 0.0;
+        for (int q = 0; q < kn - 1 && ok; ++q) {
+          const TV* src = kb + (((size_t)q * P.H + prow0 + rr) * 16 + b) * 2;
+          uint64_t lo = ld_tv(src), hi = ld_tv(src + 1);
+          for (uint32_t polls = 0; !(tv_ok(lo, ktag) && tv_ok(hi, ktag));) {
+            if (++polls >= P.watchdog || ldc_u(P.status + ST_ABORT)) {
+              ok = false;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            lo = ld_tv(src);
+            hi = ld_tv(src + 1);
+          }
+          v += tvd_val(lo, hi);
+        }
+        red[rr * NB + b] = v + red[rr * NB + b];
+      }
+      if (tid == 0) m->flag = 1;
+      __syncthreads();
+      if (!ok) {
+        uint32_t zero = 0u;
+        if (__hip_atomic_compare_exchange_strong((GAS uint32_t*)(P.status + ST_CODE), &zero, ERR_WATCHDOG,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          stc_u(P.status + ST_CU, blockIdx.x);
+          stc_u(P.status + ST_TASK, t.tile);
+          stc_u(P.status + ST_EVENT, ev_op);
+        }
+        stc_u(P.status + ST_ABORT, 1u);
+        m->flag = 0;
+      }
+      __syncthreads();
+      if (!m->flag) return false;
     }
     // ---- epilogue for this pass's rows (the RMSNorm scale per sequence, formed once, in LDS)
     if (tid < NB) {
@@ -1281,7 +1343,12 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
       stc_i(&lp->idx, m->lmi[tid]);
     }
   }
-  signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+  if (t.sig_ev != EV_NONE) {
+    signal_event(P, t.sig_ev, t.sig_slot, P.epoch + (uint32_t)s + 1u);
+  } else {  // a split-K part below the last: its tagged sums are complete once stored
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   return true;
 }
 
@@ -1330,12 +1397,6 @@ __device__ __forceinline__ uint64_t ld_tv_b(__amdgpu_buffer_rsrc_t r, uint32_t v
   const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 16 /* sc1 */);
   return ((uint64_t)v.y << 32) | v.x;
 }
-// an fp64 value as two tagged words: p[0] low half, p[1] high half
-__device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
-  st_tv(p, (uint32_t)__double2loint(v), tag);
-  st_tv(p + 1, (uint32_t)__double2hiint(v), tag);
-}
-__device__ __forceinline__ double tvd_val(uint64_t lo, uint64_t hi) { return __hiloint2double((int)(uint32_t)hi, (int)(uint32_t)lo); }
 
 // NL: K/V 16-byte loads per thread (the split covers at most NL * PPB positions)
 // QR: compiled with the reuse of rotated queries (left out where registers are scarce)

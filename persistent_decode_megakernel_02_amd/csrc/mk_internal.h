@@ -40,8 +40,13 @@ struct TaskRec {
   // holding A rows, names the operator's sums (their tag); no slot of it is signalled.  EV_NONE
   // without adapters.
   uint32_t la0, la1, lora_ev;
+  // split-K (O- and down-projection at batch >= 8): part kp of kn of the operator's K slices for
+  // the tile's rows; parts below kn - 1 publish step-tagged partial row sums, part kn - 1 adds
+  // them in order of kp and signals.  kn = 1: the whole K.
+  uint32_t kp, kn;
+  uint32_t pad[2];
 };
-static_assert(sizeof(TaskRec) == 48, "TaskRec layout");
+static_assert(sizeof(TaskRec) == 64, "TaskRec layout");
 
 struct EventRec {
   uint32_t fanin;  // number of producer slots
@@ -135,6 +140,8 @@ struct KParams {
   TV* part_acc;     // [B][Hkv][NS][G][D][2] split unnormalised P.V (fp64 as two tagged words)
   LmPart* lm_part;    // [B][n_lm]
   TV* lora_u;         // [4 operators][B][3 r]: the adapters' A x of the current GEMV operator (fp32, step-tagged)
+  TV* kpart;          // [2 operators (WO, DOWN)][max split - 1][H][16][2]: split-K partial row sums (fp64, step-tagged)
+  int32_t kpart_max;  // largest split of the graph (1: none)
   // tokens
   int32_t* pending;           // [B]
   int32_t* out_tokens;        // [n_steps][B] or null

@@ -50,7 +50,11 @@ def candidates(shape, batch, workers, plain_split):
     smax = (8 if G == 1 else 5) * 4096 // shape.head_dim
     splits = [s for s in splits if s <= smax]
     frac = lambda fs: sorted({max(1, int(workers * f)) for f in fs}, reverse=True)  # noqa: E731
+    # split-K of WO / DOWN (matrix-core GEMV, batch >= 8): 2, 4, 8 parts up to the K slices of 2048
+    ks = lambda k: [1] + [p for p in (2, 4, 8) if batch >= 8 and p <= -(-k // 2048)]  # noqa: E731
     return {
+        "wo_ksplit": ks(shape.n_q_heads * shape.head_dim),
+        "down_ksplit": ks(shape.ffn),
         "split": splits,
         "rotate": [0, 1, 2, 4, 8, 16, 32, 64, 128],
         "attn_offset": [0, 16, 64, 128, 192],
@@ -114,16 +118,18 @@ class Bench:
             if self.ref is None:
                 self.ref = {}
                 self.first = out
-            ref = self.ref.get(split)
-            if ref is not None:  # same split: tiling and placement must not change a single bit
+            # tiling and placement change no bit; the attention split and split-K regroup sums
+            key = (split, max(1, sched.get("wo_ksplit", 0)), max(1, sched.get("down_ksplit", 0)))
+            ref = self.ref.get(key)
+            if ref is not None:  # same sums: tiling and placement must not change a single bit
                 if not (torch.equal(out[0], ref[0]) and torch.equal(out[1].view(torch.int32), ref[1].view(torch.int32))):
                     raise RuntimeError(f"schedule {sched} split {split}: results differ from the same split's")
-            else:  # another split adds the attention partials in other groups: same tokens, close logits
+            else:  # other groupings of the same sums: same tokens, close logits
                 d = (out[1] - self.first[1]).abs().max().item()
                 if not torch.equal(out[0], self.first[0]) or d > 1e-3:
                     log(f"split {split}: tokens differ or max |d logit| {d} > 1e-3 (a near-tie): not a candidate")
                     times = [math.inf]
-                self.ref[split] = out
+                self.ref[key] = out
             phases = self._phases(eng) if trace else None
             graph = mk.mk_get_graph(eng.ctx)
         finally:
@@ -174,7 +180,7 @@ def parse_graph(raw: bytes):
     base = 8 + 3 * nev
     op, layer, worker = [], [], []
     for i in range(nt):
-        r = w[base + 15 * i: base + 15 * (i + 1)]
+        r = w[base + 17 * i: base + 17 * (i + 1)]
         op.append(r[1])
         layer.append(r[2])
         worker.append(r[11])
@@ -196,6 +202,8 @@ def plain_split(shape, batch, max_seq, workers):
 
 def search(args):
     import torch
+
+    from . import binding as mk
 
     b = Bench(args.workload, args.steps, args.warmup, args.reps)
     w = b.w
@@ -220,7 +228,11 @@ def search(args):
                 cfg[field] = v
                 if any(e["cfg"] == cfg for e in evals):
                     continue
-                t, times, _, _ = b.run(cfg["split"], sched_of(cfg))
+                try:
+                    t, times, _, _ = b.run(cfg["split"], sched_of(cfg))
+                except mk.MkError as e:  # e.g. a split-K that does not divide the tile count
+                    log(f"sweep {sweep} {field}={v}: rejected ({e})")
+                    continue
                 evals.append({"cfg": cfg, "ms": t, "times": times})
                 log(f"sweep {sweep} {field}={v}: {t:.4f} ms/token")
                 if t < t_best * (1.0 - noise):
@@ -310,10 +322,11 @@ def freeze(paths):
         rows.append((kept, f"    // {r['workload']}: plain {r['plain']['ms']:.4f} ms/token, winner "
                            f"{r['winner']['ms']:.4f}; paired gains {gain}" + ("" if kept else " (not kept)")))
         if kept:
-            rows.append((True, "    {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, {%d, %d, %d, %d, %d, %d, %d, %d}}," % (
-                s["n_layers"], s["hidden"], s["n_q_heads"], s["n_kv_heads"], s["head_dim"], s["ffn"], s["vocab"],
-                r["batch"], r["workers"], lo, hi, win["split"], win["qkv_tiles"], win["wo_tiles"], win["gu_tiles"],
-                win["down_tiles"], win["lm_tiles"], win["rotate"], win["attn_offset"])))
+            rows.append((True, "    {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d}},"
+                         % (s["n_layers"], s["hidden"], s["n_q_heads"], s["n_kv_heads"], s["head_dim"], s["ffn"],
+                            s["vocab"], r["batch"], r["workers"], lo, hi, win["split"], win["qkv_tiles"],
+                            win["wo_tiles"], win["gu_tiles"], win["down_tiles"], win["lm_tiles"], win["rotate"],
+                            win["attn_offset"], win.get("wo_ksplit", 0), win.get("down_ksplit", 0))))
     body = "\n".join(line for _, line in rows)
     text = f"""// schedule_table.inc -- schedules frozen by the offline search (schedule_search.py), one entry
 // per (shape, batch, workers, max_seq range).  An entry overrides the plain rules of graph.cpp
@@ -326,7 +339,7 @@ struct FrozenSchedule {{
 }};
 static const FrozenSchedule kFrozenSchedules[] = {{
     // L, H, Hq, Hkv, D, F, V, B, workers, max_seq range,
-    //   {{split, qkv, wo, gu, down, lm tiles, rotate, attn_offset}}
+    //   {{split, qkv, wo, gu, down, lm tiles, rotate, attn_offset, wo_ksplit, down_ksplit}}
 {body}
     {{0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, {{}}}},  // end marker, matches nothing (empty max_seq range)
 }};

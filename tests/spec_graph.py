@@ -37,7 +37,14 @@ Rules (one decode step; the persistent kernel repeats it every step):
     [min(i q, nA), min((i+1) q, nA)).  One event per (layer, operator), appended after the LM event
     in layer-major order QKV, WO, GU, DOWN, with fan-in ceil(nA / q) (the holders).  Other tasks:
     la0 = la1 = 0, lora_ev = none.
-  * Canonical bytes, version 2: each task row ends with la0, la1, lora_ev.
+  * Split-K (batch >= 8 decode graphs): ks = wo_ksplit (down_ksplit), 0 taking the plain rule: the
+    first of 4, 2 that is at most ceil(K / 2048) and divides T, else 1 (always 1 below batch 8 and in
+    the prefill graph).  With ks > 1 the T tasks of WO (DOWN)
+    form T / ks row tiles of ks consecutive tasks; task i is part p = i mod ks of row tile r = i // ks,
+    covering units [floor(r R / (T / ks)), floor((r+1) R / (T / ks))); only the last part (p = ks - 1)
+    signals, slot r, so the event's fan-in is T / ks; the other parts signal none (slot 0).  Valid:
+    ks in {1, 2, 4, 8}, ks | T, ks <= ceil(K / 2048) (K = Hq D for WO, F for DOWN).
+  * Canonical bytes, version 3: each task row ends with la0, la1, lora_ev, kp, kn.
   * Prefill graph (chunk > 0): B = chunk virtual sequences, the given split, the plain tiling and
     placement; after each layer's QKV tasks one append task per KV-head group g (op 7, tile g,
     a0 = g, on the worker of the group's first QKV tile) waits QKV(l, g) and signals its own event
@@ -69,10 +76,13 @@ class Task:
     la0: int = 0
     la1: int = 0
     lora_ev: int = EV_NONE
+    kp: int = 0
+    kn: int = 1
 
 
 def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0, wo_tiles=0, gu_tiles=0,
-               down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0, lora_rank=0, chunk=0):
+               down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0, lora_rank=0, chunk=0, wo_ksplit=0,
+               down_ksplit=0):
     G = Hq // Hkv
     if chunk:
         B = chunk
@@ -94,6 +104,14 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
     n_wo, n_gu = min(wo_tiles or workers, H), min(gu_tiles or workers, F)
     n_down, n_lm = min(down_tiles or workers, H), min(lm_tiles or workers, V)
     rot, aoff = rotate % workers, attn_offset % workers
+    ksplit = {OP_WO: wo_ksplit, OP_GU: 1, OP_DOWN: down_ksplit}
+    for op, T, K in ((OP_WO, n_wo, Hq * D), (OP_DOWN, n_down, F)):
+        nsl = -(-K // 2048)
+        if ksplit[op] == 0:  # the plain rule
+            ksplit[op] = next((k for k in (4, 2) if B >= 8 and not chunk and k <= nsl and T % k == 0), 1)
+        ks = ksplit[op]
+        if ks > 1 and (B < 8 or chunk or ks not in (2, 4, 8) or T % ks or ks > nsl):
+            raise ValueError("invalid split-K")
 
     def place(k, i):
         return (i + k * rot) % workers
@@ -106,7 +124,8 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
     ev_lm = L * per_layer
     fanin = []
     for _ in range(L):
-        fanin += [TG] * Hkv + [NS * B * Hkv if dist else B * Hkv, n_wo, n_gu, n_down]
+        fanin += [TG] * Hkv + [NS * B * Hkv if dist else B * Hkv, n_wo // ksplit[OP_WO], n_gu,
+                               n_down // ksplit[OP_DOWN]]
     fanin.append(n_lm)
     # LoRA A-row events, after the LM event
     n_arows = {OP_QKV: 3 * lora_rank, OP_WO: lora_rank, OP_GU: lora_rank, OP_DOWN: lora_rank}
@@ -157,9 +176,13 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
                     k += 1
         for k, (op, R, T, wait, sig) in enumerate(((OP_WO, H, n_wo, Hkv, Hkv + 1), (OP_GU, F, n_gu, Hkv + 1, Hkv + 2),
                                                    (OP_DOWN, H, n_down, Hkv + 2, Hkv + 3)), start=1):
+            ks = ksplit[op]
             for i in range(T):
-                tasks.append(Task(op, layer, i, lo(i, R, T), lo(i + 1, R, T), ev(layer, wait), 0, ev(layer, sig), i,
-                                  place(k, i), **lora_fields(op, layer, i)))
+                r, p = divmod(i, ks)
+                last = p == ks - 1
+                tasks.append(Task(op, layer, i, lo(r, R, T // ks), lo(r + 1, R, T // ks), ev(layer, wait), 0,
+                                  ev(layer, sig) if last else EV_NONE, r if last else 0, place(k, i),
+                                  kp=p, kn=ks, **lora_fields(op, layer, i)))
     for i in range(0 if chunk else n_lm):
         tasks.append(Task(OP_LM, 0, i, lo(i, V, n_lm), lo(i + 1, V, n_lm), ev(L - 1, Hkv + 3), 0, ev_lm, i,
                           place(4, i)))
@@ -172,11 +195,11 @@ def canonical_bytes(g, workers) -> bytes:
     for f in fanin:
         slot0.append(acc)
         acc += f
-    words = [0x31474B4D, 2, workers, g["split"], g["n_splits"], len(fanin), len(tasks), acc]
+    words = [0x31474B4D, 3, workers, g["split"], g["n_splits"], len(fanin), len(tasks), acc]
     for i, f in enumerate(fanin):
         words += [i, f, slot0[i]]
     for i, t in enumerate(tasks):
         wf = 0 if t.wait_ev == EV_NONE else fanin[t.wait_ev]
         words += [i, t.op, t.layer, t.tile, t.a0, t.a1, t.wait_ev, wf, t.wait_lag, t.sig_ev, t.sig_slot, t.worker,
-                  t.la0, t.la1, t.lora_ev]
+                  t.la0, t.la1, t.lora_ev, t.kp, t.kn]
     return struct.pack(f"<{len(words)}I", *words)

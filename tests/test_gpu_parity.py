@@ -172,6 +172,43 @@ def test_k_sliced_batches_match_oracle(batch, prompt, steps):
     check_against_oracle(WIDE, w, s, toks, logits, steps, f"wide-b{batch}", n_threads=16)
 
 
+# split-K of the O- and down-projection at batch >= 8: Hq D = 4096 gives WO two K slices of 2048,
+# F = 7168 gives DOWN four (the last ragged); WIDE's F = 5632 splits its three slices as 1 + 2
+WIDE_K = ModelShape(n_layers=2, hidden=1024, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=7168, vocab=3000,
+                    rope_theta=500000.0)
+SPLIT_K = [
+    (WIDE_K, 8, 9, 24, dict(wo_ksplit=2, down_ksplit=4)),
+    (WIDE, 16, 5, 20, dict(down_tiles=200, down_ksplit=2, rotate=7)),
+]
+
+
+@pytest.mark.parametrize("shape,batch,prompt,steps,sched", SPLIT_K)
+def test_split_k_matches_oracle(shape, batch, prompt, steps, sched):
+    say(f"split-K batch={batch} hidden={shape.hidden} ffn={shape.ffn} {sched}")
+    w, s, (toks, logits) = run_prompt_case(shape, batch, prompt, steps, schedule=sched)
+    check_against_oracle(shape, w, s, toks, logits, steps, f"split-K b{batch}", n_threads=16)
+
+
+def test_split_k_per_op_and_resumed_decode_are_bit_identical():
+    say("split-K: megakernel vs per-operator launches vs decode in three calls, batch=8")
+    sched = dict(wo_ksplit=2, down_ksplit=4)
+    weights = synth.make_weights(WIDE_K, seed=5, device="cuda")
+    seqs = synth.make_sequences(WIDE_K, 8, 7, 0, seed=5)
+    res = []
+    for mode, chunks in ((mk.MK_MODE_MEGAKERNEL, [12]), (mk.MK_MODE_PER_OP, [12]), (mk.MK_MODE_MEGAKERNEL, [1, 4, 7])):
+        eng = mk.Engine(WIDE_K, batch=8, max_seq=6 + 12, mode=mode, schedule=sched)
+        eng.load_weights(weights)
+        eng.prefill(seqs["prompts"].numpy())
+        out = [eng.decode(n) for n in chunks]
+        torch.cuda.synchronize()
+        res.append((np.concatenate([t.cpu().numpy() for t, _ in out]),
+                    np.concatenate([lg.cpu().numpy() for _, lg in out])))
+        eng.close()
+    for t, lg in res[1:]:
+        assert np.array_equal(t, res[0][0])
+        assert np.array_equal(lg.view(np.uint32), res[0][1].view(np.uint32))
+
+
 @pytest.mark.parametrize("batch,shape", [(1, TINY), (4, TINY), (16, WIDE)])
 def test_argmax_ties_go_to_the_lowest_index(batch, shape):
     # Two LM-head rows made identical and dominant: their logits are equal and the largest, so the

@@ -132,7 +132,7 @@ def parse(raw: bytes):
     magic, ver, workers, split, ns, nev, nt, nslots = w[:8]
     ev = [w[8 + 3 * i: 11 + 3 * i] for i in range(nev)]
     base = 8 + 3 * nev
-    tasks = [w[base + 15 * i: base + 15 * (i + 1)] for i in range(nt)]
+    tasks = [w[base + 17 * i: base + 17 * (i + 1)] for i in range(nt)]
     return dict(magic=magic, ver=ver, workers=workers, split=split, ns=ns, events=ev, tasks=tasks, nslots=nslots)
 
 
@@ -148,7 +148,7 @@ def test_builder_bytes_equal_spec(shape, B, max_seq, workers, split):
 @pytest.mark.parametrize("shape,B,max_seq,workers,split", CASES)
 def test_graph_invariants(shape, B, max_seq, workers, split):
     g = parse(mk.mk_build_graph(cfg_of(shape, B, max_seq, split), workers))
-    assert g["magic"] == 0x31474B4D and g["ver"] == 2
+    assert g["magic"] == 0x31474B4D and g["ver"] == 3
     tasks, events = g["tasks"], g["events"]
     # topological indices are consecutive; slots partition the flag array
     assert [t[0] for t in tasks] == list(range(len(tasks)))
@@ -180,12 +180,13 @@ def test_graph_invariants(shape, B, max_seq, workers, split):
         else:
             assert t[1] == OP_QKV and t[2] == 0
         assert t[7] == events[t[6]][1]
-    # each GEMV operator's tiles partition its output units (one writer per output row)
+    # each GEMV operator's tiles partition its output units (one writer per output row: with split-K
+    # the last part of each row tile)
     H, F, V = shape.hidden, shape.ffn, shape.vocab
     RG = (shape.n_q_heads // shape.n_kv_heads + 2) * shape.head_dim
     for layer in range(shape.n_layers):
         for op, R in ((OP_QKV, shape.n_kv_heads * RG), (OP_WO, H), (OP_GU, F), (OP_DOWN, H)):
-            rng = sorted((t[4], t[5]) for t in tasks if t[1] == op and t[2] == layer)
+            rng = sorted((t[4], t[5]) for t in tasks if t[1] == op and t[2] == layer and t[15] == t[16] - 1)
             assert rng[0][0] == 0 and rng[-1][1] == R
             assert all(a[1] == b[0] for a, b in zip(rng, rng[1:])) and all(a < b for a, b in rng)
     rng = sorted((t[4], t[5]) for t in tasks if t[1] == OP_LM)
@@ -222,6 +223,9 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None, early=None, violati
     per_layer = Hkv + 4
     dist = g["ns"] * B * Hkv <= workers
     lists = [[t for t in tasks if t[11] == w] for w in range(workers)]
+    L = shape.n_layers
+    kdone = {}                     # split-K (op, row tile, part) -> uses published (use u = step * L + layer)
+    kread = {}                     # split-K (op, row tile) -> uses the last part has reduced
     flags = {}                     # (event, slot) -> steps signalled
     done_split = {}                # (step, layer, bg) -> active splits that stored their partial
     stored = [False] * workers     # a merging split has stored and waits for its head's others
@@ -245,6 +249,26 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None, early=None, violati
         n_act = n_active(step)
         return t[5] == n_act - 1 or (dist and n_act > 8)
 
+    def parts_ready(t, step):  # the last K part of a row tile reduces once the others have published
+        kp, kn = t[15], t[16]
+        if kn == 1 or kp < kn - 1:
+            return True
+        u = step * L + t[2]
+        return all(kdone.get((t[1], t[3] // kn, p), 0) >= u + 1 for p in range(kn - 1))
+
+    def finish(t, step):
+        completed[t[0]] = step + 1
+        kp, kn = t[15], t[16]
+        if kn == 1:
+            return
+        key, u = (t[1], t[3] // kn), step * L + t[2]
+        if kp < kn - 1:  # publishing overwrites the previous use's partials: it must have been reduced
+            if violations is not None and kread.get(key, 0) < u:
+                violations.append((t[0], "kpart", step))
+            kdone[key + (kp,)] = u + 1
+        else:
+            kread[key] = u + 1
+
     while True:
         ready = []
         for w in range(workers):
@@ -259,7 +283,8 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None, early=None, violati
                     ready.append(w)
             else:
                 target = step + 1 - t[8]
-                if target <= 0 or all(flags.get((t[6], sl), 0) >= target for sl in slots(t[6], step - t[8])):
+                if (target <= 0 or all(flags.get((t[6], sl), 0) >= target for sl in slots(t[6], step - t[8]))) \
+                        and parts_ready(t, step):
                     ready.append(w)
         if not ready:
             return all(pos[w] >= total[w] for w in range(workers))
@@ -268,7 +293,7 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None, early=None, violati
         t = lists[w][i]
         if released[w]:  # the early-release task completes now
             released[w] = False
-            completed[t[0]] = step + 1
+            finish(t, step)
             pos[w] += 1
             continue
         if violations is not None and t[6] != 0xFFFFFFFF and not stored[w] and not (
@@ -279,7 +304,7 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None, early=None, violati
                     src = signaller.get((t[6], sl))
                     if src is not None and completed.get(src, 0) < target:
                         violations.append((t[0], src, step))
-        signal = True
+        signal = t[9] != 0xFFFFFFFF  # a split-K part below the last signals nothing
         if t[1] == OP_ATTN:
             if t[5] >= n_active(step):
                 signal = False
@@ -295,7 +320,7 @@ def simulate(g, shape, B, steps, start_pos, seed, drop=None, early=None, violati
         if early is not None and t[0] == early:  # signal now, complete on the worker's next move
             released[w] = True
         else:
-            completed[t[0]] = step + 1
+            finish(t, step)
             pos[w] += 1
         if signal and not (drop is not None and t[0] == drop):
             assert flags.get((t[9], t[10]), 0) <= step, "slot signalled twice in a step"
@@ -363,3 +388,100 @@ def test_builder_rejects_unsupported_shapes(bad):
     del base
     with pytest.raises(mk.MkError):
         mk.mk_build_graph(cfg_of(shape, B, 64, split), 256)
+
+
+# split-K of the O- and down-projection (batch >= 8): K >= 4096 for WO (Hq D) and DOWN (F)
+KSHAPE = ModelShape(2, 128, 32, 8, 128, 8192, 100)
+KSPLIT_CASES = [
+    (KSHAPE, 8, 40, 24, 16, dict(wo_ksplit=2, down_ksplit=4)),
+    (KSHAPE, 16, 40, 37, 8, dict(wo_tiles=36, down_tiles=32, wo_ksplit=2, down_ksplit=4, rotate=5)),
+    (LLAMA8B, 8, 1088, 256, 0, dict(wo_ksplit=2, down_ksplit=4)),
+    (LLAMA8B, 16, 1088, 256, 0, dict(down_tiles=192, down_ksplit=2, rotate=3)),
+]
+
+
+def plain_ks(B, K, T):
+    """Written out from the rule: at batch >= 8, the first of 4, 2 within K's slices of 2048 that divides T."""
+    if B < 8:
+        return 1
+    for k in (4, 2):
+        if k * 2048 < K + 2048 and T % k == 0:
+            return k
+    return 1
+
+
+def test_split_k_plain_rule():
+    ks = lambda g, op: {t[16] for t in g["tasks"] if t[1] == op}  # noqa: E731
+    for B, wo, down in ((1, 1, 1), (4, 1, 1), (8, 2, 4), (16, 2, 4)):
+        g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, B, 1088, 0), 256))
+        assert ks(g, OP_WO) == {wo} and ks(g, OP_DOWN) == {down}
+    # 1 turns it off; tile counts that 4 does not divide take 2, or none
+    g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, 8, 1088, 0, dict(wo_ksplit=1, down_ksplit=1)), 256))
+    assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {1}
+    g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, 8, 1088, 0, dict(wo_tiles=255, down_tiles=250)), 256))
+    assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {2}
+    # the prefill graph never splits
+    g = parse(mk.mk_build_prefill_graph(cfg_of(LLAMA8B, 8, 1088, 0), 256, 16, 64))
+    assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {1}
+
+
+@pytest.mark.parametrize("shape,B,max_seq,workers,split,sched", KSPLIT_CASES)
+def test_split_k_graph_bytes_equal_spec(shape, B, max_seq, workers, split, sched):
+    got = mk.mk_build_graph(cfg_of(shape, B, max_seq, split, sched), workers)
+    assert got == spec_bytes(shape, B, max_seq, workers, split, **sched)
+    g = parse(got)
+    # a part count not given takes the plain rule
+    wo_ks = sched.get("wo_ksplit") or plain_ks(B, shape.n_q_heads * shape.head_dim, sched.get("wo_tiles") or workers)
+    down_ks = sched.get("down_ksplit") or plain_ks(B, shape.ffn, sched.get("down_tiles") or workers)
+    for op, ks in ((OP_WO, wo_ks), (OP_DOWN, down_ks)):
+        for layer in range(shape.n_layers):
+            ts = [t for t in g["tasks"] if t[1] == op and t[2] == layer]
+            assert [(t[15], t[16]) for t in ts] == [(i % ks, ks) for i in range(len(ts))]
+            # the parts of a row tile share its rows; the row tiles cover the output once
+            rows = [(t[4], t[5]) for t in ts[ks - 1::ks]]
+            assert all(ts[i][4:6] == ts[i - i % ks + ks - 1][4:6] for i in range(len(ts)))
+            assert rows[0][0] == 0 and rows[-1][1] == shape.hidden
+            assert all(a[1] == b[0] for a, b in zip(rows, rows[1:]))
+            # only last parts signal, one slot per row tile
+            sig = [t for t in ts if t[9] != 0xFFFFFFFF]
+            assert sig == ts[ks - 1::ks] and [t[10] for t in sig] == list(range(len(sig)))
+            assert g["events"][sig[0][9]][1] == len(sig)
+
+
+@pytest.mark.parametrize("bad", [
+    (KSHAPE, 4, dict(wo_ksplit=2)),                       # batch below 8: no matrix-core GEMV
+    (KSHAPE, 8, dict(down_ksplit=3)),                     # not 2, 4 or 8
+    (KSHAPE, 8, dict(wo_ksplit=4)),                       # more parts than WO's two K slices
+    (KSHAPE, 8, dict(down_tiles=30, down_ksplit=4)),      # does not divide the tile count
+    (LLAMA8B, 8, dict(down_ksplit=8)),                    # 14336 has 7 K slices
+    (KSHAPE, 8, dict(wo_ksplit=-2)),
+])
+def test_split_k_is_validated(bad):
+    shape, B, sched = bad
+    with pytest.raises(mk.MkError):
+        mk.mk_build_graph(cfg_of(shape, B, 40, 0, sched), 24)
+
+
+@pytest.mark.parametrize("case,seed", [(0, 0), (0, 1), (1, 2), (1, 3)])
+def test_split_k_protocol_completes_without_stale_partials(case, seed):
+    shape, B, max_seq, workers, split, sched = KSPLIT_CASES[case]
+    g = parse(mk.mk_build_graph(cfg_of(shape, B, max_seq, split, sched), workers))
+    bad = []
+    assert simulate(g, shape, B, steps=3, start_pos=5, seed=seed, violations=bad)
+    assert bad == []
+
+
+def test_split_k_simulation_catches_a_reordered_list():
+    # control for the simulator: the four parts of one down-projection row tile moved onto one worker
+    # in reverse order put the reducing part ahead of parts it polls for, which must deadlock
+    shape, B, max_seq, workers, split, sched = KSPLIT_CASES[0]
+    g = parse(mk.mk_build_graph(cfg_of(shape, B, max_seq, split, dict(sched, down_tiles=4)), workers))
+    assert simulate(g, shape, B, steps=2, start_pos=5, seed=0)
+    idx = [i for i, t in enumerate(g["tasks"]) if t[1] == OP_DOWN and t[2] == 0]
+    assert len(idx) == 4
+    w0 = g["tasks"][idx[0]][11]
+    moved = [g["tasks"][i][:11] + (w0,) + g["tasks"][i][12:] for i in reversed(idx)]
+    tasks = list(g["tasks"])
+    for i, t in zip(idx, moved):
+        tasks[i] = t
+    assert not simulate(dict(g, tasks=tasks), shape, B, steps=2, start_pos=5, seed=0)
