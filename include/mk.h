@@ -96,8 +96,10 @@ typedef struct mk_model_cfg {
                          groups of ksplit tasks sharing a row range, each taking a part of K;
                          the last adds the others' partial sums in order.  0: the plain rule
                          (batch >= 8: the larger of 4 and 2 that is at most K / 2048 rounded up
-                         and divides the tile count; else none); 1: none; else 2, 4 or 8,
-                         dividing the tile count, at most K / 2048 rounded up */
+                         and divides the tile count; batch 2 and 4: the fewest of 1, 2, 4, 8
+                         parts whose fp64 staging of every sequence fits 128 KB, the next that
+                         divides the tile count; batch 1, LoRA: none); 1: none; else 2, 4 or 8,
+                         dividing the tile count (batch >= 8: at most K / 2048 rounded up) */
   /* LoRA (Mirage article, "Case 2: LoRA + Linear"): rank r of an adapter
    * on every projection of every layer (q, k, v, o, gate, up, down), each
    * y = W x + B (A x) computed as one fused GEMV over the concatenation

@@ -171,9 +171,11 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
   auto maxrows = [](int R, int T) { return (R + T - 1) / T; };
   // with LoRA a tile also sums up to ceil(A rows / tiles) adapter rows (row pairs at gate/up)
   const int lr = cfg.lora_rank;
-  const int worst = std::max({maxrows(cfg.hidden, g.n_wo) + maxrows(lr, g.n_wo),
+  // (a split-K row tile of the O- or down-projection holds ksplit tiles' rows)
+  const int worst = std::max({maxrows(cfg.hidden, g.n_wo / g.wo_ksplit) + maxrows(lr, g.n_wo),
                               (maxrows(cfg.ffn, g.n_gu) + maxrows(lr, g.n_gu)) * 2,
-                              maxrows(cfg.hidden, g.n_down) + maxrows(lr, g.n_down), maxrows(cfg.vocab, g.n_lm),
+                              maxrows(cfg.hidden, g.n_down / g.down_ksplit) + maxrows(lr, g.n_down),
+                              maxrows(cfg.vocab, g.n_lm),
                               (G + 2) * D / g.qkv_tiles_per_group + 1 + maxrows(3 * lr, g.n_qkv)});
   LdsPlan L;
   L.mk_ks = 0;
@@ -199,7 +201,8 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
     L.red_off = L.misc_off - L.red_doubles * 8;
     L.xs_doubles = L.red_off / 8;
     // streaming engine: [region 0][region 1][residual x 2][row sums x 2][misc]
-    const int resid = std::max(maxrows(cfg.hidden, g.n_wo), maxrows(cfg.hidden, g.n_down)) * B;
+    const int resid =
+        std::max(maxrows(cfg.hidden, g.n_wo / g.wo_ksplit), maxrows(cfg.hidden, g.n_down / g.down_ksplit)) * B;
     L.sg_red_cap = (worst * B + 1) / 2 * 2;
     L.sg_red = (L.misc_off - 2 * L.sg_red_cap * 8) & ~15;
     L.sg_xold_cap = (resid + 3) / 4 * 4;

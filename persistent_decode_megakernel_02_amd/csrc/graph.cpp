@@ -128,27 +128,41 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
   if ((int64_t)g.n_qkv > n_workers) return "QKV tiles (per group times n_kv_heads) exceed the workers";
   // split-K of the O- and down-projection (matrix-core GEMV, K in slices of 2048): the operator's
   // tiles form row tiles of ksplit consecutive tasks, part p taking slices [p nsl / ks, (p+1) nsl / ks)
-  // 0 takes the plain rule: with the matrix-core GEMV (batch >= 8, decode graph) the larger of 4
-  // and 2 that is at most the operator's K slices and divides its tile count, else none.  Every
-  // tile otherwise stages the whole activation; split, a tile stages only its part of K.
-  const int kslices[2] = {(c.n_q_heads * D + 2047) / 2048, (c.ffn + 2047) / 2048};
-  auto plain_ks = [&](int want, int ksl, int tiles) {
+  // Every tile stages the whole activation of its operator; split, a tile stages only its part of
+  // K.  0 takes the plain rule (decode graph, no adapters):
+  //  * batch >= 8 (matrix-core GEMV, K in slices of 2048): the larger of 4 and 2 that is at most
+  //    the operator's K slices and divides its tile count;
+  //  * batch 2 to 4 (fp64 GEMV): the fewest parts (1, 2, 4 or 8) whose K part, staged in fp64 for
+  //    every sequence, takes at most 128 KB, so that a part stages once; the next of 2, 4, 8 that
+  //    divides the tile count if that one does not (none if no such part divides it);
+  //  * batch 1: none (not built: one sequence's activations fit one slice).
+  const int kdim[2] = {c.n_q_heads * D, c.ffn};
+  const int kslices[2] = {(kdim[0] + 2047) / 2048, (kdim[1] + 2047) / 2048};
+  const bool kable = chunk == 0 && c.lora_rank == 0 && c.batch >= 2;
+  auto plain_ks = [&](int want, int k, int tiles) {
     if (want > 0) return want;
-    if (c.batch < 8 || chunk > 0) return 1;
-    for (int k : {4, 2})
-      if (k <= ksl && tiles % k == 0) return k;
+    if (!kable) return 1;
+    if (c.batch >= 8) {
+      for (int p : {4, 2})
+        if (p <= kslices[k] && tiles % p == 0) return p;
+      return 1;
+    }
+    int p = 1;
+    while (p < 8 && (int64_t)((kdim[k] + p - 1) / p) * c.batch * 8 > 131072) p *= 2;
+    for (; p <= 8; p *= 2)
+      if (tiles % p == 0) return p;
     return 1;
   };
-  g.wo_ksplit = plain_ks(sc.wo_ksplit, kslices[0], g.n_wo);
-  g.down_ksplit = plain_ks(sc.down_ksplit, kslices[1], g.n_down);
+  g.wo_ksplit = plain_ks(sc.wo_ksplit, 0, g.n_wo);
+  g.down_ksplit = plain_ks(sc.down_ksplit, 1, g.n_down);
   {
     const int ks[2] = {g.wo_ksplit, g.down_ksplit}, nt[2] = {g.n_wo, g.n_down};
     for (int k = 0; k < 2; ++k) {
       if (ks[k] == 1) continue;
-      if (c.batch < 8 || chunk > 0) return "split-K needs the matrix-core GEMV (batch >= 8, decode graph)";
+      if (!kable) return "split-K is for the decode graph of two or more sequences without adapters";
       if (ks[k] != 2 && ks[k] != 4 && ks[k] != 8) return "split-K must be 1, 2, 4 or 8";
       if (nt[k] % ks[k]) return "split-K must divide the operator's tile count";
-      if (ks[k] > kslices[k]) return "split-K larger than the operator's K slices";
+      if (c.batch >= 8 && ks[k] > kslices[k]) return "split-K larger than the operator's K slices";
     }
   }
   g.rotate = sc.rotate % n_workers;

@@ -542,9 +542,13 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   const uint32_t utag = (P.epoch + (uint32_t)s) * P.ntag + t.lora_ev + 1u;
   const int my_units = nut > w ? (nut - w + NW - 1) / NW : 0;
   const int my_rows = my_units * RU;
-  const int kc = min(K, (P.xs_doubles / NB) / 512 * 512);
+  // split-K (O- and down-projection): part kp of kn takes K elements [k_lo, k_hi), in whole
+  // 8-element chunks; the row sums of the others go through kpart to the last part
+  const int kp = (int)t.kp, kn = (int)t.kn;
+  const int k_lo = kp * (K >> 3) / kn * 8, k_hi = (kp + 1) * (K >> 3) / kn * 8;
+  const int kc = min(k_hi - k_lo, (P.xs_doubles / NB) / 512 * 512);
   const int ps = kc >> 2;  // one plane: elements (2p, 2p+1) of every 8-element chunk, kc/8 pairs
-  const int nsl = (K + kc - 1) / kc;
+  const int nsl = (k_hi - k_lo + kc - 1) / kc;
 
   auto rowptr = [&](int r) -> const uint16_t* {
     const int ui = RU == 2 ? (r >> 1) : r;
@@ -563,8 +567,8 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   int ir = 0, ig = 0, cr = 0, cgi = 0;
   int k0 = 0, nch8 = 0, GPR = 1;
   auto slice_setup = [&](int sl) {
-    k0 = sl * kc;
-    const int ks = min(kc, K - k0);
+    k0 = k_lo + sl * kc;
+    const int ks = min(kc, k_hi - k0);
     nch8 = ks / 8;
     const int nch = (nch8 + 63) / 64;
     GPR = (nch + CGE - 1) / CGE;
@@ -728,7 +732,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   // after the wait, so the epilogue does not wait a round trip for it.
   const bool resid = op == OP_WO || op == OP_DOWN;
   float xpre = 0.f;
-  if (resid && tid < nu * NB) {
+  if (resid && kp == kn - 1 && tid < nu * NB) {
     const int ul = tid / NB, b = tid - ul * NB;
     xpre = ldc(P.x + (size_t)b * P.H + u0 + ul);
   }
@@ -743,7 +747,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     }
     // ---- stage activations of this slice into LDS (x * gamma, exact in fp64); sum of squares on slice 0
     {
-      const int ks = min(kc, K - k0);
+      const int ks = min(kc, k_hi - k0);
       double ss[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) ss[b] = 0.0;
@@ -842,6 +846,63 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
       if (g + DEPTH + d < total) consume(buf[d]);
   }
   __syncthreads();
+
+  // ---- split-K: a part below the last publishes its row sums (fp64, two words tagged with the
+  // step and the operator's event) and is done; the last part adds the others' in order of part,
+  // its own last, polling a word not yet published (no adapters here: wbase is 0).  Not compiled
+  // for one sequence, whose activations always fit one slice (with it, the compiler keeps a copy
+  // of the parameter block in scratch memory).
+  if constexpr (NB >= 2) {
+    if (kn > 1) {
+      const uint32_t ev_op = (uint32_t)(l * (P.Hkv + 4) + P.Hkv + (op == OP_WO ? 1 : 3));
+      const uint32_t ktag = (P.epoch + (uint32_t)s) * P.ntag + ev_op + 1u;
+      TV* kb = P.kpart + (size_t)(op == OP_WO ? 0 : 1) * (P.kpart_max - 1) * P.H * 16 * 2;
+      if (kp < kn - 1) {
+        for (int i = tid; i < nu * NB; i += NT) {
+          const int ul = i / NB, b = i - ul * NB;
+          st_tvd(kb + (((size_t)kp * P.H + u0 + ul) * 16 + b) * 2, red[ul * NB + b], ktag);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        return true;
+      }
+      bool ok = true;
+      for (int i = tid; i < nu * NB; i += NT) {
+        const int ul = i / NB, b = i - ul * NB;
+        double v = 0.0;
+        for (int q = 0; q < kn - 1 && ok; ++q) {
+          const TV* src = kb + (((size_t)q * P.H + u0 + ul) * 16 + b) * 2;
+          uint64_t lo = ld_tv(src), hi = ld_tv(src + 1);
+          for (uint32_t polls = 0; !(tv_ok(lo, ktag) && tv_ok(hi, ktag));) {
+            if (++polls >= P.watchdog || ldc_u(P.status + ST_ABORT)) {
+              ok = false;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            lo = ld_tv(src);
+            hi = ld_tv(src + 1);
+          }
+          v += tvd_val(lo, hi);
+        }
+        red[ul * NB + b] = v + red[ul * NB + b];
+      }
+      if (tid == 0) m->flag = 1;
+      __syncthreads();
+      if (!ok) {
+        uint32_t zero = 0u;
+        if (__hip_atomic_compare_exchange_strong((GAS uint32_t*)(P.status + ST_CODE), &zero, ERR_WATCHDOG,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          stc_u(P.status + ST_CU, blockIdx.x);
+          stc_u(P.status + ST_TASK, t.tile);
+          stc_u(P.status + ST_EVENT, ev_op);
+        }
+        stc_u(P.status + ST_ABORT, 1u);
+        m->flag = 0;
+      }
+      __syncthreads();
+      if (!m->flag) return false;
+    }
+  }
 
   // ---- RMSNorm scale r = 1/sqrt(mean(x^2) + eps) in fp64, applied after the dot products
   double rs[NB];

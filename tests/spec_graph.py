@@ -37,13 +37,16 @@ Rules (one decode step; the persistent kernel repeats it every step):
     [min(i q, nA), min((i+1) q, nA)).  One event per (layer, operator), appended after the LM event
     in layer-major order QKV, WO, GU, DOWN, with fan-in ceil(nA / q) (the holders).  Other tasks:
     la0 = la1 = 0, lora_ev = none.
-  * Split-K (batch >= 8 decode graphs): ks = wo_ksplit (down_ksplit), 0 taking the plain rule: the
-    first of 4, 2 that is at most ceil(K / 2048) and divides T, else 1 (always 1 below batch 8 and in
-    the prefill graph).  With ks > 1 the T tasks of WO (DOWN)
+  * Split-K (decode graphs of batch >= 2 without LoRA): ks = wo_ksplit (down_ksplit), 0 taking the plain rule.
+    Batch >= 8: the first of 4, 2 that is at most ceil(K / 2048) and divides T, else 1.  Batch < 8:
+    need = the first of 1, 2, 4 with ceil(K / p) * B * 8 <= 131072 (else 8), then the first of
+    1, 2, 4, 8 at least need that divides T, else 1.  Always 1 in the prefill graph, with LoRA and at
+    batch 1.
+    With ks > 1 the T tasks of WO (DOWN)
     form T / ks row tiles of ks consecutive tasks; task i is part p = i mod ks of row tile r = i // ks,
     covering units [floor(r R / (T / ks)), floor((r+1) R / (T / ks))); only the last part (p = ks - 1)
     signals, slot r, so the event's fan-in is T / ks; the other parts signal none (slot 0).  Valid:
-    ks in {1, 2, 4, 8}, ks | T, ks <= ceil(K / 2048) (K = Hq D for WO, F for DOWN).
+    ks in {1, 2, 4, 8}, ks | T, at batch >= 8 ks <= ceil(K / 2048) (K = Hq D for WO, F for DOWN).
   * Canonical bytes, version 3: each task row ends with la0, la1, lora_ev, kp, kn.
   * Prefill graph (chunk > 0): B = chunk virtual sequences, the given split, the plain tiling and
     placement; after each layer's QKV tasks one append task per KV-head group g (op 7, tile g,
@@ -105,12 +108,19 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
     n_down, n_lm = min(down_tiles or workers, H), min(lm_tiles or workers, V)
     rot, aoff = rotate % workers, attn_offset % workers
     ksplit = {OP_WO: wo_ksplit, OP_GU: 1, OP_DOWN: down_ksplit}
+    splittable = not chunk and not lora_rank and B >= 2
     for op, T, K in ((OP_WO, n_wo, Hq * D), (OP_DOWN, n_down, F)):
         nsl = -(-K // 2048)
         if ksplit[op] == 0:  # the plain rule
-            ksplit[op] = next((k for k in (4, 2) if B >= 8 and not chunk and k <= nsl and T % k == 0), 1)
+            if not splittable:
+                ksplit[op] = 1
+            elif B >= 8:
+                ksplit[op] = next((k for k in (4, 2) if k <= nsl and T % k == 0), 1)
+            else:  # fewest parts whose fp64 staging of B sequences takes at most 128 KB
+                need = next((p for p in (1, 2, 4) if -(-K // p) * B * 8 <= 131072), 8)
+                ksplit[op] = next((p for p in (1, 2, 4, 8) if p >= need and T % p == 0), 1)
         ks = ksplit[op]
-        if ks > 1 and (B < 8 or chunk or ks not in (2, 4, 8) or T % ks or ks > nsl):
+        if ks > 1 and (not splittable or ks not in (2, 4, 8) or T % ks or (B >= 8 and ks > nsl)):
             raise ValueError("invalid split-K")
 
     def place(k, i):

@@ -179,6 +179,10 @@ WIDE_K = ModelShape(n_layers=2, hidden=1024, n_q_heads=32, n_kv_heads=8, head_di
 SPLIT_K = [
     (WIDE_K, 8, 9, 24, dict(wo_ksplit=2, down_ksplit=4)),
     (WIDE, 16, 5, 20, dict(down_tiles=200, down_ksplit=2, rotate=7)),
+    # the fp64 GEMV (batch <= 4): parts of whole 8-element chunks; at batch 4 the plain rule splits
+    # WIDE's down-projection in two (5632 fp64 activations of 4 sequences exceed 128 KB)
+    (WIDE, 4, 9, 16, {}),
+    (WIDE_K, 2, 9, 16, dict(wo_ksplit=2, down_ksplit=8, down_tiles=200)),
 ]
 
 
@@ -189,14 +193,15 @@ def test_split_k_matches_oracle(shape, batch, prompt, steps, sched):
     check_against_oracle(shape, w, s, toks, logits, steps, f"split-K b{batch}", n_threads=16)
 
 
-def test_split_k_per_op_and_resumed_decode_are_bit_identical():
-    say("split-K: megakernel vs per-operator launches vs decode in three calls, batch=8")
+@pytest.mark.parametrize("batch", [8, 4])
+def test_split_k_per_op_and_resumed_decode_are_bit_identical(batch):
+    say(f"split-K: megakernel vs per-operator launches vs decode in three calls, batch={batch}")
     sched = dict(wo_ksplit=2, down_ksplit=4)
     weights = synth.make_weights(WIDE_K, seed=5, device="cuda")
-    seqs = synth.make_sequences(WIDE_K, 8, 7, 0, seed=5)
+    seqs = synth.make_sequences(WIDE_K, batch, 7, 0, seed=5)
     res = []
     for mode, chunks in ((mk.MK_MODE_MEGAKERNEL, [12]), (mk.MK_MODE_PER_OP, [12]), (mk.MK_MODE_MEGAKERNEL, [1, 4, 7])):
-        eng = mk.Engine(WIDE_K, batch=8, max_seq=6 + 12, mode=mode, schedule=sched)
+        eng = mk.Engine(WIDE_K, batch=batch, max_seq=6 + 12, mode=mode, schedule=sched)
         eng.load_weights(weights)
         eng.prefill(seqs["prompts"].numpy())
         out = [eng.decode(n) for n in chunks]

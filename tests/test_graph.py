@@ -397,22 +397,35 @@ KSPLIT_CASES = [
     (KSHAPE, 16, 40, 37, 8, dict(wo_tiles=36, down_tiles=32, wo_ksplit=2, down_ksplit=4, rotate=5)),
     (LLAMA8B, 8, 1088, 256, 0, dict(wo_ksplit=2, down_ksplit=4)),
     (LLAMA8B, 16, 1088, 256, 0, dict(down_tiles=192, down_ksplit=2, rotate=3)),
+    (KSHAPE, 2, 40, 24, 16, dict(wo_ksplit=2, down_ksplit=8, rotate=1)),   # fp64 GEMV path
+    (LLAMA8B, 4, 1088, 256, 0, {}),                                         # plain rule: DOWN in 4
+    (LLAMA8B, 4, 1088, 100, 0, dict(down_tiles=98)),                        # 4 does not divide 98: none
 ]
 
 
 def plain_ks(B, K, T):
-    """Written out from the rule: at batch >= 8, the first of 4, 2 within K's slices of 2048 that divides T."""
-    if B < 8:
+    """Written out from the rule: at batch >= 8, the first of 4, 2 within K's slices of 2048 that
+    divides T; below, the first of 1, 2, 4, 8 dividing T from the fewest parts whose fp64 staging of
+    B sequences fits 128 KB."""
+    if B == 1:
         return 1
-    for k in (4, 2):
-        if k * 2048 < K + 2048 and T % k == 0:
+    if B >= 8:
+        for k in (4, 2):
+            if k * 2048 < K + 2048 and T % k == 0:
+                return k
+        return 1
+    need = 1
+    while need < 8 and (K + need - 1) // need * B * 8 > 128 * 1024:
+        need *= 2
+    for k in (1, 2, 4, 8):
+        if k >= need and T % k == 0:
             return k
     return 1
 
 
 def test_split_k_plain_rule():
     ks = lambda g, op: {t[16] for t in g["tasks"] if t[1] == op}  # noqa: E731
-    for B, wo, down in ((1, 1, 1), (4, 1, 1), (8, 2, 4), (16, 2, 4)):
+    for B, wo, down in ((1, 1, 1), (2, 1, 2), (4, 1, 4), (8, 2, 4), (16, 2, 4)):
         g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, B, 1088, 0), 256))
         assert ks(g, OP_WO) == {wo} and ks(g, OP_DOWN) == {down}
     # 1 turns it off; tile counts that 4 does not divide take 2, or none
@@ -449,7 +462,8 @@ def test_split_k_graph_bytes_equal_spec(shape, B, max_seq, workers, split, sched
 
 
 @pytest.mark.parametrize("bad", [
-    (KSHAPE, 4, dict(wo_ksplit=2)),                       # batch below 8: no matrix-core GEMV
+    (replace(KSHAPE, lora_rank=8), 4, dict(wo_ksplit=2)),  # not with adapters
+    (KSHAPE, 1, dict(down_ksplit=2)),                     # not for one sequence
     (KSHAPE, 8, dict(down_ksplit=3)),                     # not 2, 4 or 8
     (KSHAPE, 8, dict(wo_ksplit=4)),                       # more parts than WO's two K slices
     (KSHAPE, 8, dict(down_tiles=30, down_ksplit=4)),      # does not divide the tile count
@@ -462,7 +476,7 @@ def test_split_k_is_validated(bad):
         mk.mk_build_graph(cfg_of(shape, B, 40, 0, sched), 24)
 
 
-@pytest.mark.parametrize("case,seed", [(0, 0), (0, 1), (1, 2), (1, 3)])
+@pytest.mark.parametrize("case,seed", [(0, 0), (0, 1), (1, 2), (1, 3), (4, 4), (4, 5)])
 def test_split_k_protocol_completes_without_stale_partials(case, seed):
     shape, B, max_seq, workers, split, sched = KSPLIT_CASES[case]
     g = parse(mk.mk_build_graph(cfg_of(shape, B, max_seq, split, sched), workers))
