@@ -100,6 +100,10 @@ typedef struct mk_model_cfg {
                          parts whose fp64 staging of every sequence fits 128 KB, the next that
                          divides the tile count; batch 1, LoRA: none); 1: none; else 2, 4 or 8,
                          dividing the tile count (batch >= 8: at most K / 2048 rounded up) */
+  int32_t qkv_ksplit; /* batch >= 8 only: the same for the QKV tiles of each KV-head group (the
+                         parts also pass on their sums of squares for the RMSNorm scale).  0 or
+                         1: none (the plain rule; a split measured slower); else 2, 4 or 8,
+                         dividing the tiles per group, at most hidden / 2048 rounded up */
   /* LoRA (Mirage article, "Case 2: LoRA + Linear"): rank r of an adapter
    * on every projection of every layer (q, k, v, o, gate, up, down), each
    * y = W x + B (A x) computed as one fused GEMV over the concatenation

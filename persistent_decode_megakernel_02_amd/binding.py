@@ -27,7 +27,7 @@ MK_PREFILL_MEGAKERNEL = 1
 MK_SCHEDULE_FROZEN = 0
 MK_SCHEDULE_GIVEN = 1
 SCHEDULE_FIELDS = ("qkv_tiles", "wo_tiles", "gu_tiles", "down_tiles", "lm_tiles", "rotate", "attn_offset",
-                   "wo_ksplit", "down_ksplit")
+                   "wo_ksplit", "down_ksplit", "qkv_ksplit")
 
 
 class MkError(RuntimeError):
@@ -44,6 +44,7 @@ class MkModelCfg(C.Structure):
                 ("stream", C.c_void_p), ("schedule", C.c_int32), ("qkv_tiles", C.c_int32), ("wo_tiles", C.c_int32),
                 ("gu_tiles", C.c_int32), ("down_tiles", C.c_int32), ("lm_tiles", C.c_int32), ("rotate", C.c_int32),
                 ("attn_offset", C.c_int32), ("wo_ksplit", C.c_int32), ("down_ksplit", C.c_int32),
+                ("qkv_ksplit", C.c_int32),
                 ("lora_rank", C.c_int32), ("prefill", C.c_int32)]
 
 

@@ -89,7 +89,7 @@ struct mk_ctx {
   LmPart* lm_part = nullptr;
   TV* lora_u = nullptr;  // [4][B][3 r] adapter A x of the current GEMV operator (LoRA), step-tagged
   size_t n_lora_u = 0;
-  TV* kpart = nullptr;  // [2][max split - 1][H][16][2] split-K partial row sums, step-tagged
+  TV* kpart = nullptr;  // split-K partial row sums (and QKV sums of squares), step-tagged
   size_t n_kpart = 0;
   int kpart_max = 1;
   int32_t* pending = nullptr;
@@ -176,7 +176,7 @@ static int plan_lds(const mk_model_cfg& cfg, const Graph& g, LdsPlan* out, std::
                               (maxrows(cfg.ffn, g.n_gu) + maxrows(lr, g.n_gu)) * 2,
                               maxrows(cfg.hidden, g.n_down / g.down_ksplit) + maxrows(lr, g.n_down),
                               maxrows(cfg.vocab, g.n_lm),
-                              (G + 2) * D / g.qkv_tiles_per_group + 1 + maxrows(3 * lr, g.n_qkv)});
+                              (G + 2) * D / (g.qkv_tiles_per_group / g.qkv_ksplit) + 1 + maxrows(3 * lr, g.n_qkv)});
   LdsPlan L;
   L.mk_ks = 0;
   if (B >= 8) {
@@ -426,8 +426,9 @@ int mk_create(const mk_model_cfg* cfg_in, mk_ctx** out) {
   if ((rc = dalloc(c, (void**)&c->lm_part, (size_t)B * c->g.n_lm * sizeof(LmPart)))) return bail(rc);
   c->n_lora_u = (size_t)4 * B * 3 * r;
   if (r && (rc = dalloc(c, (void**)&c->lora_u, c->n_lora_u * sizeof(TV)))) return bail(rc);
-  c->kpart_max = std::max(c->g.wo_ksplit, c->g.down_ksplit);
-  c->n_kpart = (size_t)2 * (c->kpart_max - 1) * H * 16 * 2;
+  // [WO: H + 1 rows][DN: H + 1][QKV: QKVR + 1] per part below the last, 16 sequences, two words
+  c->kpart_max = std::max({c->g.wo_ksplit, c->g.down_ksplit, c->g.qkv_ksplit});
+  c->n_kpart = (size_t)(c->kpart_max - 1) * (2 * ((size_t)H + 1) + (size_t)QKVR + 1) * 16 * 2;
   if (c->n_kpart && (rc = dalloc(c, (void**)&c->kpart, c->n_kpart * sizeof(TV)))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->pending, (size_t)B * 4))) return bail(rc);
   if ((rc = dalloc(c, (void**)&c->flags, (size_t)c->g.n_slots * 4))) return bail(rc);
@@ -680,7 +681,8 @@ static int run_per_op_steps(mk_ctx* c, KParams P, int n_steps, bool with_lm) {
       // last K part of a split row tile polls the other parts' sums
       const uint32_t op = g.tasks[g.op_ranges[r].first].op;
       const bool coop = op == OP_ATTN || (c->cfg.lora_rank > 0 && op != OP_LM) ||
-                        (op == OP_WO && g.wo_ksplit > 1) || (op == OP_DOWN && g.down_ksplit > 1);
+                        (op == OP_WO && g.wo_ksplit > 1) || (op == OP_DOWN && g.down_ksplit > 1) ||
+                        (op == OP_QKV && g.qkv_ksplit > 1);
       HIPCHK(c, launch(coop ? 3 : 1, P, c->stream));
     }
   }

@@ -78,6 +78,7 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
     sc.attn_offset = c.attn_offset;
     sc.wo_ksplit = c.wo_ksplit;
     sc.down_ksplit = c.down_ksplit;
+    sc.qkv_ksplit = c.qkv_ksplit;
   } else if (c.schedule == MK_SCHEDULE_FROZEN) {
     sc = frozen_schedule(c, n_workers);
   } else {
@@ -91,7 +92,7 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
   }
   const int B = chunk > 0 ? chunk : c.batch;
   if (sc.qkv_tiles < 0 || sc.wo_tiles < 0 || sc.gu_tiles < 0 || sc.down_tiles < 0 || sc.lm_tiles < 0 || sc.rotate < 0 ||
-      sc.attn_offset < 0 || sc.wo_ksplit < 0 || sc.down_ksplit < 0)
+      sc.attn_offset < 0 || sc.wo_ksplit < 0 || sc.down_ksplit < 0 || sc.qkv_ksplit < 0)
     return "schedule fields must be >= 0";
   if (sc.wo_tiles > n_workers || sc.gu_tiles > n_workers || sc.down_tiles > n_workers || sc.lm_tiles > n_workers)
     return "at most one tile per worker for each GEMV operator";
@@ -155,6 +156,21 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
   };
   g.wo_ksplit = plain_ks(sc.wo_ksplit, 0, g.n_wo);
   g.down_ksplit = plain_ks(sc.down_ksplit, 1, g.n_down);
+  // QKV (matrix-core GEMV only): the parts of a row tile stay inside one KV-head group; the
+  // parts also pass on their sums of squares, for the RMSNorm scale that the last part applies.
+  // The plain rule leaves it unsplit: split in two it measured slower on the 8B shape at batch 8
+  // and 16 (its row tiles are short, and the partial exchange sits right before attention).
+  {
+    const int ksq = (c.hidden + 2047) / 2048;
+    const int q = sc.qkv_ksplit == 0 ? 1 : sc.qkv_ksplit;
+    if (q != 1) {
+      if (!kable || c.batch < 8) return "QKV split-K needs the matrix-core GEMV (batch >= 8, decode graph)";
+      if (q != 2 && q != 4 && q != 8) return "split-K must be 1, 2, 4 or 8";
+      if (TG % q) return "QKV split-K must divide the QKV tiles per KV-head group";
+      if (q > ksq) return "split-K larger than the operator's K slices";
+    }
+    g.qkv_ksplit = q;
+  }
   {
     const int ks[2] = {g.wo_ksplit, g.down_ksplit}, nt[2] = {g.n_wo, g.n_down};
     for (int k = 0; k < 2; ++k) {
@@ -206,7 +222,7 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
   auto ev_app = [&](int l, int gg) { return ev_app0 + (uint32_t)(l * Hkv + gg); };
   g.events.resize(ev_app0 + (chunk > 0 ? Hkv * c.n_layers : 0));
   for (int l = 0; l < c.n_layers; ++l) {
-    for (int gg = 0; gg < Hkv; ++gg) g.events[ev_qkv(l, gg)].fanin = TG;
+    for (int gg = 0; gg < Hkv; ++gg) g.events[ev_qkv(l, gg)].fanin = TG / g.qkv_ksplit;
     g.events[ev_att(l)].fanin = dist ? g.n_splits * B * Hkv : B * Hkv;
     for (int gg = 0; gg < Hkv && chunk > 0; ++gg) g.events[ev_app(l, gg)].fanin = 1;
     g.events[ev_o(l)].fanin = g.n_wo / g.wo_ksplit;
@@ -256,11 +272,17 @@ static std::string build_graph_impl(const mk_model_cfg& c, int n_workers, int ch
     const uint32_t in_ev = l == 0 ? (chunk > 0 ? ev_x(c.n_layers - 1) : ev_lm) : ev_x(l - 1);
     const uint32_t in_lag = l == 0 ? 1u : 0u;
     uint32_t f = range_begin();
+    const int qks = g.qkv_ksplit, nrq = TG / qks;
     for (int gg = 0; gg < Hkv; ++gg)
       for (int i = 0; i < TG; ++i) {
+        // split: row tile r = i / qks of the group, part p = i mod qks; only the last part signals
+        const int r = i / qks, p = i - r * qks;
         uint32_t tile = (uint32_t)(gg * TG + i);
-        uint32_t r0 = (uint32_t)(gg * RG) + tile_lo(i, RG, TG), r1 = (uint32_t)(gg * RG) + tile_lo(i + 1, RG, TG);
-        push(OP_QKV, l, tile, r0, r1, in_ev, in_lag, ev_qkv(l, gg), (uint32_t)i, place(0, tile));
+        uint32_t r0 = (uint32_t)(gg * RG) + tile_lo(r, RG, nrq), r1 = (uint32_t)(gg * RG) + tile_lo(r + 1, RG, nrq);
+        push(OP_QKV, l, tile, r0, r1, in_ev, in_lag, p == qks - 1 ? ev_qkv(l, gg) : EV_NONE,
+             p == qks - 1 ? (uint32_t)r : 0u, place(0, tile));
+        g.tasks.back().kp = (uint32_t)p;
+        g.tasks.back().kn = (uint32_t)qks;
       }
     range_end(f);
     if (chunk > 0) {  // prefill: one append task per KV-head group, on the worker of the group's first QKV tile

@@ -25,6 +25,7 @@ struct Graph {
   std::vector<uint32_t> range_start;
   int rotate = 0, attn_offset = 0;  // placement (see build_graph)
   int wo_ksplit = 1, down_ksplit = 1;  // K parts of the O- and down-projection tiles
+  int qkv_ksplit = 1;                  // K parts of the QKV tiles (within a KV-head group)
 };
 
 // The schedule choices of one graph: what the offline search varies (tile counts per operator,
@@ -36,7 +37,8 @@ struct Schedule {
   int wo_tiles = 0, gu_tiles = 0, down_tiles = 0, lm_tiles = 0;
   int rotate = 0;      // GEMV operator k of a layer (QKV 0, WO 1, GU 2, DOWN 3; LM 4): tile i on worker i + k rotate
   int attn_offset = 0; // attention task k on worker k + attn_offset
-  int wo_ksplit = 0, down_ksplit = 0;  // K parts per row tile of WO / DOWN (batch >= 8; 0: plain rule, 1: none)
+  int wo_ksplit = 0, down_ksplit = 0;  // K parts per row tile of WO / DOWN (batch >= 2; 0: plain rule, 1: none)
+  int qkv_ksplit = 0;                  // ... of the QKV tiles of a KV-head group (batch >= 8)
 };
 
 // The search's winner for cfg's shape and batch at n_workers (all fields 0 where it has none).

@@ -57,6 +57,7 @@ struct Misc {
   double ml[8][2];      // attention (max, sum) per head
   int32_t flag;
   double rsd[16];       // matrix-core GEMV: RMSNorm scale per sequence
+  double kss[16];       // split-K QKV, last part: the other parts' sums of squares per sequence
   float lmv[16];        // matrix-core LM head: running (max, index) per sequence
   int32_t lmi[16];
   uint32_t cev, ctgt;   // the last (event, target) this worker's wait saw complete
@@ -490,6 +491,16 @@ __device__ __forceinline__ void st_tvd(TV* p, double v, uint32_t tag) {
 }
 __device__ __forceinline__ double tvd_val(uint64_t lo, uint64_t hi) { return __hiloint2double((int)(uint32_t)hi, (int)(uint32_t)lo); }
 
+// split-K partial sums: [operator region][part < kpart_max - 1][row][16 sequences], each an fp64 as
+// two tagged words; regions WO (H + 1 rows), DN (H + 1), QKV (QKVR + 1); a region's last row holds
+// a part's sums of squares (QKV).  (Sizes chosen arithmetically, not by selecting field addresses.)
+__device__ __forceinline__ TV* kpart_row(const KParams& P, int op, int part, int row) {
+  const size_t km = (size_t)(P.kpart_max - 1), rh = (size_t)P.H + 1, rq = (size_t)P.QKVR + 1;
+  const size_t off = (size_t)(op == OP_DOWN) * km * rh + (size_t)(op == OP_QKV) * 2 * km * rh;
+  const size_t rows = (size_t)(op == OP_QKV) * rq + (size_t)(op != OP_QKV) * rh;
+  return P.kpart + (off + (size_t)part * rows + (size_t)row) * 32;
+}
+
 // ---------------------------------------------------------------------------
 // GEMV task: rows [a0, a1) of one weight matrix against B activation vectors.
 // Numerics: the staged activation x_k * gamma_k and every product with a bf16
@@ -854,13 +865,11 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   // of the parameter block in scratch memory).
   if constexpr (NB >= 2) {
     if (kn > 1) {
-      const uint32_t ev_op = (uint32_t)(l * (P.Hkv + 4) + P.Hkv + (op == OP_WO ? 1 : 3));
-      const uint32_t ktag = (P.epoch + (uint32_t)s) * P.ntag + ev_op + 1u;
-      TV* kb = P.kpart + (size_t)(op == OP_WO ? 0 : 1) * (P.kpart_max - 1) * P.H * 16 * 2;
+      const uint32_t ktag = (P.epoch + (uint32_t)s) * P.ntag + t.wait_ev + 1u;
       if (kp < kn - 1) {
         for (int i = tid; i < nu * NB; i += NT) {
           const int ul = i / NB, b = i - ul * NB;
-          st_tvd(kb + (((size_t)kp * P.H + u0 + ul) * 16 + b) * 2, red[ul * NB + b], ktag);
+          st_tvd(kpart_row(P, op, kp, u0 + ul) + b * 2, red[ul * NB + b], ktag);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -871,7 +880,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
         const int ul = i / NB, b = i - ul * NB;
         double v = 0.0;
         for (int q = 0; q < kn - 1 && ok; ++q) {
-          const TV* src = kb + (((size_t)q * P.H + u0 + ul) * 16 + b) * 2;
+          const TV* src = kpart_row(P, op, q, u0 + ul) + b * 2;
           uint64_t lo = ld_tv(src), hi = ld_tv(src + 1);
           for (uint32_t polls = 0; !(tv_ok(lo, ktag) && tv_ok(hi, ktag));) {
             if (++polls >= P.watchdog || ldc_u(P.status + ST_ABORT)) {
@@ -894,7 +903,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
                                                  __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
           stc_u(P.status + ST_CU, blockIdx.x);
           stc_u(P.status + ST_TASK, t.tile);
-          stc_u(P.status + ST_EVENT, ev_op);
+          stc_u(P.status + ST_EVENT, t.sig_ev);
         }
         stc_u(P.status + ST_ABORT, 1u);
         m->flag = 0;
@@ -1290,27 +1299,32 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
     }
     if (kn > 1) {
       // split-K: a part below the last publishes its row sums (fp64, as two words tagged with the
-      // step and the operator's event); the last part adds the others' in order of part, its own
-      // last, polling a word not yet published.  Only the last part runs the epilogue.
-      const int opi = op == OP_WO ? 0 : 1;
-      const uint32_t ev_op = (uint32_t)(l * (P.Hkv + 4) + P.Hkv + (op == OP_WO ? 1 : 3));
-      const uint32_t ktag = (P.epoch + (uint32_t)s) * P.ntag + ev_op + 1u;
-      TV* kb = P.kpart + (size_t)opi * (P.kpart_max - 1) * P.H * 16 * 2;
-      const int prow0 = u0 + tp0 * 16;
-      __syncthreads();  // red complete
+      // step and the operator's input event, which differs per layer) and, at QKV, its sums of
+      // squares; the last part adds the others' in order of part, its own last, polling a word
+      // not yet published.  Only the last part runs the epilogue.
+      const uint32_t ktag = (P.epoch + (uint32_t)s) * P.ntag + t.wait_ev + 1u;
+      const int prow0 = u0 * RU + tp0 * 16;
+      const int srow = (op == OP_QKV) * P.QKVR + (op != OP_QKV) * P.H;  // the sums-of-squares row
+      const bool pss = norm && pass == 0;
+      __builtin_amdgcn_s_waitcnt(0);  // this task's earlier stores (layer 0: its share of x) are done
+      __syncthreads();                // red complete
       if (kp < kn - 1) {
         for (int i = tid; i < rows * NB; i += NT) {
           const int rr = i / NB, b = i - rr * NB;
-          st_tvd(kb + (((size_t)kp * P.H + prow0 + rr) * 16 + b) * 2, red[rr * NB + b], ktag);
+          st_tvd(kpart_row(P, op, kp, prow0 + rr) + b * 2, red[rr * NB + b], ktag);
+        }
+        if (pss && tid < NB) {
+          double tot = 0.0;
+          for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][tid];
+          st_tvd(kpart_row(P, op, kp, srow) + tid * 2, tot, ktag);
         }
         continue;  // next pass
       }
       bool ok = true;
-      for (int i = tid; i < rows * NB; i += NT) {
-        const int rr = i / NB, b = i - rr * NB;
+      auto poll_sum = [&](int row, int b) -> double {
         double v = 0.0;
         for (int q = 0; q < kn - 1 && ok; ++q) {
-          const TV* src = kb + (((size_t)q * P.H + prow0 + rr) * 16 + b) * 2;
+          const TV* src = kpart_row(P, op, q, row) + b * 2;
           uint64_t lo = ld_tv(src), hi = ld_tv(src + 1);
           for (uint32_t polls = 0; !(tv_ok(lo, ktag) && tv_ok(hi, ktag));) {
             if (++polls >= P.watchdog || ldc_u(P.status + ST_ABORT)) {
@@ -1323,8 +1337,13 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
           }
           v += tvd_val(lo, hi);
         }
-        red[rr * NB + b] = v + red[rr * NB + b];
+        return v;
+      };
+      for (int i = tid; i < rows * NB; i += NT) {
+        const int rr = i / NB, b = i - rr * NB;
+        red[rr * NB + b] = poll_sum(prow0 + rr, b) + red[rr * NB + b];
       }
+      if (pss && tid < NB) m->kss[tid] = poll_sum(srow, tid);
       if (tid == 0) m->flag = 1;
       __syncthreads();
       if (!ok) {
@@ -1333,7 +1352,7 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
                                                  __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
           stc_u(P.status + ST_CU, blockIdx.x);
           stc_u(P.status + ST_TASK, t.tile);
-          stc_u(P.status + ST_EVENT, ev_op);
+          stc_u(P.status + ST_EVENT, t.sig_ev);
         }
         stc_u(P.status + ST_ABORT, 1u);
         m->flag = 0;
@@ -1343,7 +1362,7 @@ __device__ __forceinline__ bool gemv_mfma(const KParams& P, const TaskRec& t, in
     }
     // ---- epilogue for this pass's rows (the RMSNorm scale per sequence, formed once, in LDS)
     if (tid < NB) {
-      double tot = 0.0;
+      double tot = (kn > 1 && norm) ? m->kss[tid] : 0.0;  // split: the other parts' first, in order
       for (int ww = 0; ww < NW; ++ww) tot += m->wred[ww][tid];
       m->rsd[tid] = norm ? 1.0 / sqrt(tot / (double)K + (double)P.eps) : 1.0;
     }

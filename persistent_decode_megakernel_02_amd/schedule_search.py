@@ -55,6 +55,7 @@ def candidates(shape, batch, workers, plain_split):
     return {
         "wo_ksplit": ks(shape.n_q_heads * shape.head_dim),
         "down_ksplit": ks(shape.ffn),
+        "qkv_ksplit": ks(shape.hidden),
         "split": splits,
         "rotate": [0, 1, 2, 4, 8, 16, 32, 64, 128],
         "attn_offset": [0, 16, 64, 128, 192],
@@ -118,8 +119,10 @@ class Bench:
             if self.ref is None:
                 self.ref = {}
                 self.first = out
-            # tiling and placement change no bit; the attention split and split-K regroup sums
-            key = (split, max(1, sched.get("wo_ksplit", 0)), max(1, sched.get("down_ksplit", 0)))
+            # tiling and placement change no bit; the attention split and split-K regroup sums (the
+            # part counts as built, read back from the graph: 0 in a field takes the plain rule)
+            graph = mk.mk_get_graph(eng.ctx)
+            key = (split, graph_ksplits(graph))
             ref = self.ref.get(key)
             if ref is not None:  # same sums: tiling and placement must not change a single bit
                 if not (torch.equal(out[0], ref[0]) and torch.equal(out[1].view(torch.int32), ref[1].view(torch.int32))):
@@ -131,7 +134,6 @@ class Bench:
                     times = [math.inf]
                 self.ref[key] = out
             phases = self._phases(eng) if trace else None
-            graph = mk.mk_get_graph(eng.ctx)
         finally:
             eng.close()
         return statistics.median(times), times, phases, graph
@@ -188,6 +190,20 @@ def parse_graph(raw: bytes):
     for i in range(nt):
         lists[worker[i]].append(i)
     return {"op": op, "layer": layer, "lists": lists, "L": max(layer) + 1}
+
+
+def graph_ksplits(raw: bytes):
+    """Split-K part count of each operator (QKV, WO, DN) in a serialised graph."""
+    import struct
+
+    w = struct.unpack(f"<{len(raw) // 4}I", raw)
+    nev, nt = w[5], w[6]
+    base = 8 + 3 * nev
+    ks = {}
+    for i in range(nt):
+        r = w[base + 17 * i: base + 17 * (i + 1)]
+        ks[r[1]] = max(ks.get(r[1], 1), r[16])
+    return tuple(ks.get(op, 1) for op in (1, 3, 5))
 
 
 def plain_split(shape, batch, max_seq, workers):
@@ -322,11 +338,12 @@ def freeze(paths):
         rows.append((kept, f"    // {r['workload']}: plain {r['plain']['ms']:.4f} ms/token, winner "
                            f"{r['winner']['ms']:.4f}; paired gains {gain}" + ("" if kept else " (not kept)")))
         if kept:
-            rows.append((True, "    {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d}},"
+            rows.append((True, "    {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d}},"
                          % (s["n_layers"], s["hidden"], s["n_q_heads"], s["n_kv_heads"], s["head_dim"], s["ffn"],
                             s["vocab"], r["batch"], r["workers"], lo, hi, win["split"], win["qkv_tiles"],
                             win["wo_tiles"], win["gu_tiles"], win["down_tiles"], win["lm_tiles"], win["rotate"],
-                            win["attn_offset"], win.get("wo_ksplit", 0), win.get("down_ksplit", 0))))
+                            win["attn_offset"], win.get("wo_ksplit", 0), win.get("down_ksplit", 0),
+                            win.get("qkv_ksplit", 0))))
     body = "\n".join(line for _, line in rows)
     text = f"""// schedule_table.inc -- schedules frozen by the offline search (schedule_search.py), one entry
 // per (shape, batch, workers, max_seq range).  An entry overrides the plain rules of graph.cpp
@@ -339,7 +356,7 @@ struct FrozenSchedule {{
 }};
 static const FrozenSchedule kFrozenSchedules[] = {{
     // L, H, Hq, Hkv, D, F, V, B, workers, max_seq range,
-    //   {{split, qkv, wo, gu, down, lm tiles, rotate, attn_offset, wo_ksplit, down_ksplit}}
+    //   {{split, qkv, wo, gu, down, lm tiles, rotate, attn_offset, wo_ksplit, down_ksplit, qkv_ksplit}}
 {body}
     {{0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, {{}}}},  // end marker, matches nothing (empty max_seq range)
 }};

@@ -42,6 +42,9 @@ Rules (one decode step; the persistent kernel repeats it every step):
     need = the first of 1, 2, 4 with ceil(K / p) * B * 8 <= 131072 (else 8), then the first of
     1, 2, 4, 8 at least need that divides T, else 1.  Always 1 in the prefill graph, with LoRA and at
     batch 1.
+    QKV (qkv_ksplit, batch >= 8 only): 0 means none; a given 2, 4 or 8 must be at most ceil(H / 2048)
+    and divide TG; the parts of a row tile lie inside one KV-head group (row tile r = i // ks of the
+    group's TG tiles covers the group's rows [floor(r RG / (TG / ks)), ...)), fan-in TG / ks.
     With ks > 1 the T tasks of WO (DOWN)
     form T / ks row tiles of ks consecutive tasks; task i is part p = i mod ks of row tile r = i // ks,
     covering units [floor(r R / (T / ks)), floor((r+1) R / (T / ks))); only the last part (p = ks - 1)
@@ -85,7 +88,7 @@ class Task:
 
 def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0, wo_tiles=0, gu_tiles=0,
                down_tiles=0, lm_tiles=0, rotate=0, attn_offset=0, lora_rank=0, chunk=0, wo_ksplit=0,
-               down_ksplit=0):
+               down_ksplit=0, qkv_ksplit=0):
     G = Hq // Hkv
     if chunk:
         B = chunk
@@ -122,6 +125,11 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
         ks = ksplit[op]
         if ks > 1 and (not splittable or ks not in (2, 4, 8) or T % ks or (B >= 8 and ks > nsl)):
             raise ValueError("invalid split-K")
+    # QKV (batch >= 8): parts of a row tile within one KV-head group
+    nslq = -(-H // 2048)
+    qks = qkv_ksplit or 1  # the plain rule leaves QKV unsplit
+    if qks > 1 and (not splittable or B < 8 or qks not in (2, 4, 8) or TG % qks or qks > nslq):
+        raise ValueError("invalid QKV split-K")
 
     def place(k, i):
         return (i + k * rot) % workers
@@ -134,7 +142,7 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
     ev_lm = L * per_layer
     fanin = []
     for _ in range(L):
-        fanin += [TG] * Hkv + [NS * B * Hkv if dist else B * Hkv, n_wo // ksplit[OP_WO], n_gu,
+        fanin += [TG // qks] * Hkv + [NS * B * Hkv if dist else B * Hkv, n_wo // ksplit[OP_WO], n_gu,
                                n_down // ksplit[OP_DOWN]]
     fanin.append(n_lm)
     # LoRA A-row events, after the LM event
@@ -170,8 +178,11 @@ def spec_graph(L, H, Hq, Hkv, D, F, V, B, max_seq, workers, split=0, qkv_tiles=0
         for g in range(Hkv):
             for i in range(TG):
                 t = g * TG + i
-                tasks.append(Task(OP_QKV, layer, t, g * RG + lo(i, RG, TG), g * RG + lo(i + 1, RG, TG),
-                                  in_ev, lag, ev(layer, g), i, place(0, t), **lora_fields(OP_QKV, layer, t)))
+                r, p = divmod(i, qks)
+                last = p == qks - 1
+                tasks.append(Task(OP_QKV, layer, t, g * RG + lo(r, RG, TG // qks), g * RG + lo(r + 1, RG, TG // qks),
+                                  in_ev, lag, ev(layer, g) if last else EV_NONE, r if last else 0, place(0, t),
+                                  kp=p, kn=qks, **lora_fields(OP_QKV, layer, t)))
         if chunk:
             for g in range(Hkv):
                 tasks.append(Task(OP_APPEND, layer, g, g, 0, ev(layer, g), 0, ev_app0 + layer * Hkv + g, 0,

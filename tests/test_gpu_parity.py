@@ -176,7 +176,12 @@ def test_k_sliced_batches_match_oracle(batch, prompt, steps):
 # F = 7168 gives DOWN four (the last ragged); WIDE's F = 5632 splits its three slices as 1 + 2
 WIDE_K = ModelShape(n_layers=2, hidden=1024, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=7168, vocab=3000,
                     rope_theta=500000.0)
+# hidden 4096: the QKV tiles split too (the parts pass on their sums of squares for the RMSNorm)
+WIDE_Q = ModelShape(n_layers=2, hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=4608, vocab=3000,
+                    rope_theta=500000.0)
 SPLIT_K = [
+    (WIDE_Q, 8, 5, 16, dict(qkv_ksplit=2)),
+    (WIDE_Q, 16, 3, 12, dict(qkv_tiles=16, qkv_ksplit=2, wo_ksplit=1, rotate=3)),
     (WIDE_K, 8, 9, 24, dict(wo_ksplit=2, down_ksplit=4)),
     (WIDE, 16, 5, 20, dict(down_tiles=200, down_ksplit=2, rotate=7)),
     # the fp64 GEMV (batch <= 4): parts of whole 8-element chunks; at batch 4 the plain rule splits
@@ -193,15 +198,17 @@ def test_split_k_matches_oracle(shape, batch, prompt, steps, sched):
     check_against_oracle(shape, w, s, toks, logits, steps, f"split-K b{batch}", n_threads=16)
 
 
-@pytest.mark.parametrize("batch", [8, 4])
-def test_split_k_per_op_and_resumed_decode_are_bit_identical(batch):
-    say(f"split-K: megakernel vs per-operator launches vs decode in three calls, batch={batch}")
-    sched = dict(wo_ksplit=2, down_ksplit=4)
-    weights = synth.make_weights(WIDE_K, seed=5, device="cuda")
-    seqs = synth.make_sequences(WIDE_K, batch, 7, 0, seed=5)
+@pytest.mark.parametrize("shape,batch,sched", [(WIDE_K, 8, dict(wo_ksplit=2, down_ksplit=4)),
+                                                (WIDE_K, 4, dict(wo_ksplit=2, down_ksplit=4)),
+                                                (WIDE_Q, 8, dict(qkv_ksplit=2))])
+def test_split_k_per_op_and_resumed_decode_are_bit_identical(shape, batch, sched):
+    say(f"split-K: megakernel vs per-operator launches vs decode in three calls, batch={batch} "
+        f"hidden={shape.hidden} {sched}")
+    weights = synth.make_weights(shape, seed=5, device="cuda")
+    seqs = synth.make_sequences(shape, batch, 7, 0, seed=5)
     res = []
     for mode, chunks in ((mk.MK_MODE_MEGAKERNEL, [12]), (mk.MK_MODE_PER_OP, [12]), (mk.MK_MODE_MEGAKERNEL, [1, 4, 7])):
-        eng = mk.Engine(WIDE_K, batch=batch, max_seq=6 + 12, mode=mode, schedule=sched)
+        eng = mk.Engine(shape, batch=batch, max_seq=6 + 12, mode=mode, schedule=sched)
         eng.load_weights(weights)
         eng.prefill(seqs["prompts"].numpy())
         out = [eng.decode(n) for n in chunks]

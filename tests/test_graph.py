@@ -392,11 +392,14 @@ def test_builder_rejects_unsupported_shapes(bad):
 
 # split-K of the O- and down-projection (batch >= 8): K >= 4096 for WO (Hq D) and DOWN (F)
 KSHAPE = ModelShape(2, 128, 32, 8, 128, 8192, 100)
+KSHAPE_Q = ModelShape(2, 4096, 32, 8, 128, 4096, 100)  # hidden 4096: QKV has two K slices
 KSPLIT_CASES = [
     (KSHAPE, 8, 40, 24, 16, dict(wo_ksplit=2, down_ksplit=4)),
     (KSHAPE, 16, 40, 37, 8, dict(wo_tiles=36, down_tiles=32, wo_ksplit=2, down_ksplit=4, rotate=5)),
     (LLAMA8B, 8, 1088, 256, 0, dict(wo_ksplit=2, down_ksplit=4)),
     (LLAMA8B, 16, 1088, 256, 0, dict(down_tiles=192, down_ksplit=2, rotate=3)),
+    (KSHAPE_Q, 8, 40, 32, 16, dict(qkv_ksplit=2, wo_ksplit=2, down_ksplit=2)),
+    (KSHAPE_Q, 16, 40, 37, 8, dict(qkv_tiles=3, qkv_ksplit=1, down_tiles=36, down_ksplit=2)),
     (KSHAPE, 2, 40, 24, 16, dict(wo_ksplit=2, down_ksplit=8, rotate=1)),   # fp64 GEMV path
     (LLAMA8B, 4, 1088, 256, 0, {}),                                         # plain rule: DOWN in 4
     (LLAMA8B, 4, 1088, 100, 0, dict(down_tiles=98)),                        # 4 does not divide 98: none
@@ -425,17 +428,20 @@ def plain_ks(B, K, T):
 
 def test_split_k_plain_rule():
     ks = lambda g, op: {t[16] for t in g["tasks"] if t[1] == op}  # noqa: E731
-    for B, wo, down in ((1, 1, 1), (2, 1, 2), (4, 1, 4), (8, 2, 4), (16, 2, 4)):
+    for B, wo, down, qkv in ((1, 1, 1, 1), (2, 1, 2, 1), (4, 1, 4, 1), (8, 2, 4, 1), (16, 2, 4, 1)):
         g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, B, 1088, 0), 256))
-        assert ks(g, OP_WO) == {wo} and ks(g, OP_DOWN) == {down}
+        assert ks(g, OP_WO) == {wo} and ks(g, OP_DOWN) == {down} and ks(g, OP_QKV) == {qkv}
     # 1 turns it off; tile counts that 4 does not divide take 2, or none
-    g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, 8, 1088, 0, dict(wo_ksplit=1, down_ksplit=1)), 256))
-    assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {1}
+    g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, 8, 1088, 0, dict(wo_ksplit=1, down_ksplit=1, qkv_ksplit=1)), 256))
+    assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {1} and ks(g, OP_QKV) == {1}
     g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, 8, 1088, 0, dict(wo_tiles=255, down_tiles=250)), 256))
     assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {2}
+    # QKV splits only when asked
+    g = parse(mk.mk_build_graph(cfg_of(LLAMA8B, 16, 1088, 0, dict(qkv_tiles=6, qkv_ksplit=2)), 256))
+    assert ks(g, OP_QKV) == {2}
     # the prefill graph never splits
     g = parse(mk.mk_build_prefill_graph(cfg_of(LLAMA8B, 8, 1088, 0), 256, 16, 64))
-    assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {1}
+    assert ks(g, OP_WO) == {1} and ks(g, OP_DOWN) == {1} and ks(g, OP_QKV) == {1}
 
 
 @pytest.mark.parametrize("shape,B,max_seq,workers,split,sched", KSPLIT_CASES)
@@ -446,6 +452,19 @@ def test_split_k_graph_bytes_equal_spec(shape, B, max_seq, workers, split, sched
     # a part count not given takes the plain rule
     wo_ks = sched.get("wo_ksplit") or plain_ks(B, shape.n_q_heads * shape.head_dim, sched.get("wo_tiles") or workers)
     down_ks = sched.get("down_ksplit") or plain_ks(B, shape.ffn, sched.get("down_tiles") or workers)
+    # QKV: row tiles of ks parts inside each KV-head group (plain rule: 2 with hidden's two K slices)
+    tg = len([t for t in g["tasks"] if t[1] == OP_QKV and t[2] == 0]) // shape.n_kv_heads
+    qks = sched.get("qkv_ksplit") or 1
+    rg = (shape.n_q_heads // shape.n_kv_heads + 2) * shape.head_dim
+    for layer in range(shape.n_layers):
+        for grp in range(shape.n_kv_heads):
+            ts = [t for t in g["tasks"] if t[1] == OP_QKV and t[2] == layer and t[3] // tg == grp]
+            assert [(t[15], t[16]) for t in ts] == [(i % qks, qks) for i in range(tg)]
+            assert all(ts[i][4:6] == ts[i - i % qks + qks - 1][4:6] for i in range(tg))
+            rows = [(t[4], t[5]) for t in ts[qks - 1::qks]]
+            assert rows[0][0] == grp * rg and rows[-1][1] == (grp + 1) * rg
+            sig = [t for t in ts if t[9] != 0xFFFFFFFF]
+            assert sig == ts[qks - 1::qks] and [t[10] for t in sig] == list(range(tg // qks))
     for op, ks in ((OP_WO, wo_ks), (OP_DOWN, down_ks)):
         for layer in range(shape.n_layers):
             ts = [t for t in g["tasks"] if t[1] == op and t[2] == layer]
@@ -464,6 +483,9 @@ def test_split_k_graph_bytes_equal_spec(shape, B, max_seq, workers, split, sched
 @pytest.mark.parametrize("bad", [
     (replace(KSHAPE, lora_rank=8), 4, dict(wo_ksplit=2)),  # not with adapters
     (KSHAPE, 1, dict(down_ksplit=2)),                     # not for one sequence
+    (LLAMA8B, 4, dict(qkv_ksplit=2)),                     # QKV: matrix-core GEMV only
+    (LLAMA8B, 8, dict(qkv_ksplit=4)),                     # more parts than hidden's two K slices
+    (LLAMA8B, 8, dict(qkv_tiles=5, qkv_ksplit=2)),        # does not divide the tiles per group
     (KSHAPE, 8, dict(down_ksplit=3)),                     # not 2, 4 or 8
     (KSHAPE, 8, dict(wo_ksplit=4)),                       # more parts than WO's two K slices
     (KSHAPE, 8, dict(down_tiles=30, down_ksplit=4)),      # does not divide the tile count
@@ -476,7 +498,7 @@ def test_split_k_is_validated(bad):
         mk.mk_build_graph(cfg_of(shape, B, 40, 0, sched), 24)
 
 
-@pytest.mark.parametrize("case,seed", [(0, 0), (0, 1), (1, 2), (1, 3), (4, 4), (4, 5)])
+@pytest.mark.parametrize("case,seed", [(0, 0), (0, 1), (1, 2), (1, 3), (6, 4), (6, 5), (4, 6), (4, 7)])
 def test_split_k_protocol_completes_without_stale_partials(case, seed):
     shape, B, max_seq, workers, split, sched = KSPLIT_CASES[case]
     g = parse(mk.mk_build_graph(cfg_of(shape, B, max_seq, split, sched), workers))
