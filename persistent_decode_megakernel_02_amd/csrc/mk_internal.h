@@ -140,7 +140,7 @@ struct KParams {
   TV* part_acc;     // [B][Hkv][NS][G][D][2] split unnormalised P.V (fp64 as two tagged words)
   LmPart* lm_part;    // [B][n_lm]
   TV* lora_u;         // [4 operators][B][3 r]: the adapters' A x of the current GEMV operator (fp32, step-tagged)
-  TV* kpart;          // [2 operators (WO, DOWN)][max split - 1][H][16][2]: split-K partial row sums (fp64, step-tagged)
+  TV* kpart;          // [WO, DN, QKV][max split - 1][rows + 1][16][2]: split-K partial row sums (fp64, step-tagged)
   int32_t kpart_max;  // largest split of the graph (1: none)
   // tokens
   int32_t* pending;           // [B]
