@@ -67,11 +67,14 @@ def build(verbose: bool = False, extra=(), jobs: int = 0, out: str = LIB) -> str
 
 
 # Compile-time alternatives that the offline measurements compare with the built default:
-# the GEMV pipeline depth (groups of 4 KB in flight per wave) and the counter form of events.
+# the GEMV pipeline depth and group size (DEPTH groups of CG 16-byte chunks per lane in flight per
+# wave) and the counter form of events.
 VARIANTS = {
     "depth1": ["-DMK_GEMV_DEPTH=1"],
     "depth3": ["-DMK_GEMV_DEPTH=3"],
     "counter_events": ["-DMK_EVENT_COUNTER=1"],
+    "cg2": ["-DMK_GEMV_CG=2"],
+    "cg2d4": ["-DMK_GEMV_CG=2", "-DMK_GEMV_DEPTH=4"],
 }
 VARIANT_DIR = os.path.join(HERE, "variants")
 

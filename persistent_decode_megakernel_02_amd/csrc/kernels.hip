@@ -29,7 +29,10 @@ namespace mk {
 
 constexpr int NT = 512;  // threads per worker
 constexpr int NW = NT / 64;
-constexpr int CG = 4;      // 16-byte weight chunks per lane per pipeline group
+#ifndef MK_GEMV_CG
+#define MK_GEMV_CG 4
+#endif
+constexpr int CG = MK_GEMV_CG;  // 16-byte weight chunks per lane per pipeline group
 #ifndef MK_GEMV_DEPTH
 #define MK_GEMV_DEPTH 2
 #endif
@@ -348,7 +351,7 @@ __device__ __forceinline__ bool wait_event(const KParams& P, uint32_t ev, uint32
   const int tid = ltid();
   if (tid < 64) {
     const int lane = tid;
-    const EventRec e = ldg(P.events + ev);
+    const EventRec e = ldk(P.events + ev);
     const uint32_t* f = P.flags + e.slot0;
     uint32_t fanin = e.fanin;
     uint32_t want = target;
@@ -430,7 +433,7 @@ __device__ __forceinline__ void signal_event(const KParams& P, uint32_t ev, uint
     if constexpr (kEventCounter)
       __hip_atomic_fetch_add((GAS uint32_t*)(P.flags + ev), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
-      stc_u(P.flags + ldg(P.events + ev).slot0 + slot, val);
+      stc_u(P.flags + ldk(P.events + ev).slot0 + slot, val);
   }
 }
 
@@ -517,7 +520,7 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
   double* xs = (double*)lds;
   double* red = (double*)(lds + P.red_off);
   Misc* m = (Misc*)(lds + P.misc_off);
-  const LayerW LW = ldg(P.layers + (op == OP_LM ? 0 : l));
+  const LayerW LW = ldk(P.layers + (op == OP_LM ? 0 : l));
 
   const uint16_t* W0;
   const uint16_t* W1 = nullptr;
@@ -1437,7 +1440,7 @@ template <int NB>
 __device__ __forceinline__ bool task_gemv_mfma(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                                uint64_t* tr) {
   const int op = (int)t.op, l = (int)t.layer;
-  const LayerW LW = ldg(P.layers + (op == OP_LM ? 0 : l));
+  const LayerW LW = ldk(P.layers + (op == OP_LM ? 0 : l));
   const uint16_t* W0;
   const uint16_t* W1 = nullptr;
   const uint16_t* gamma = nullptr;
@@ -1550,7 +1553,7 @@ __device__ __forceinline__ bool task_attn(const KParams& P, const TaskRec& t, in
     rc = ldg(P.rope_cos + (size_t)pos * half + rk);
     rsn = ldg(P.rope_sin + (size_t)pos * half + rk);
     if (P.qk_norm) {
-      const LayerW LW = ldg(P.layers + l);
+      const LayerW LW = ldk(P.layers + l);
       const uint16_t* gm = rh < G ? LW.q_norm : LW.k_norm;
       g0 = (double)bf1(ldg(gm + rk));
       g1 = (double)bf1(ldg(gm + rk + half));
@@ -1958,7 +1961,7 @@ __device__ __forceinline__ bool task_append(const KParams& P, const TaskRec& t, 
   if (mega && !wait_event(P, t.wait_ev, P.epoch + (uint32_t)s + 1u, t.tile, m, tr)) return false;
   uint16_t* kst = (uint16_t*)lds;  // [C][D] rotated keys, bf16
   uint16_t* vst = kst + C * D;     // [C][D] values, bf16
-  const LayerW LW = ldg(P.layers + l);
+  const LayerW LW = ldk(P.layers + l);
   for (int b = w; b < C; b += NW) {
     const int pos = P.pos0 + s * C + b;
     if (pos >= P.pos_end) continue;
@@ -2027,7 +2030,7 @@ __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int
 template <int NB, bool LO>
 __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   char* lds = g_lds;
-  const uint32_t off = ldg(P.list_off + blockIdx.x), n = ldg(P.list_len + blockIdx.x);
+  const uint32_t off = ldk(P.list_off + blockIdx.x), n = ldk(P.list_len + blockIdx.x);
   if (threadIdx.x == 0) {
     Misc* m = (Misc*)(lds + P.misc_off);
     m->cev = EV_NONE;
@@ -2041,7 +2044,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
     int s = 0;
     uint32_t i = 0;
     while (s < P.n_steps && n > 0) {
-      const TaskRec t = ldg(P.tasks + seg_index(L, i));
+      const TaskRec t = ldk(P.tasks + seg_index(L, i));
       if (t.op == OP_ATTN) {
         uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + i) * 4 : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
@@ -2055,7 +2058,7 @@ __global__ __launch_bounds__(NT, 1) void mk_persistent(KParams P) {
   } else {
     for (int s = 0; s < P.n_steps; ++s) {
       for (uint32_t i = 0; i < n; ++i) {
-        const TaskRec t = ldg(P.tasks + ldg(P.cu_tasks + off + i));
+        const TaskRec t = ldk(P.tasks + ldk(P.cu_tasks + off + i));
         uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + i) * 4 : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = wall_clock64();
         if (!run_task<NB, LO>(P, t, s, true, lds, tr)) return;
@@ -2089,10 +2092,10 @@ __global__ __launch_bounds__(NT, 1) void mk_per_op(KParams P) {
   // a worker's tasks of this operator instance are a contiguous stretch of its list (the lists
   // are in topological order), located by the host: no scan of the operator's other tasks
   const uint32_t w = blockIdx.x, nw = (uint32_t)P.n_workers, r = (uint32_t)P.op_range;
-  const uint32_t j1 = ldg(P.range_start + (r + 1u) * nw + w), off = ldg(P.list_off + w);
-  for (uint32_t j = ldg(P.range_start + r * nw + w); j < j1; ++j) {
-    const int i = (int)ldg(P.cu_tasks + off + j);
-    const TaskRec t = ldg(P.tasks + i);
+  const uint32_t j1 = ldk(P.range_start + (r + 1u) * nw + w), off = ldk(P.list_off + w);
+  for (uint32_t j = ldk(P.range_start + r * nw + w); j < j1; ++j) {
+    const int i = (int)ldk(P.cu_tasks + off + j);
+    const TaskRec t = ldk(P.tasks + i);
     if constexpr (NB <= 4 && kStreamEngine) {
       if (t.op != OP_ATTN) {  // a segment of one task
         const SegList L{nullptr, (uint32_t)i, 1u, 1, P.step};
