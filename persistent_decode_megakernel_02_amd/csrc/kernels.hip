@@ -512,7 +512,7 @@ __device__ __forceinline__ TV* kpart_row(const KParams& P, int op, int part, int
 // ---------------------------------------------------------------------------
 // LO: compiled with the LoRA adapters (a separate instantiation, so that the plain GEMV keeps its
 // registers)
-template <int NB, bool LO>
+template <int NB, bool LO, int RPG = 1>
 __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, int s, bool mega, char* lds,
                                           uint64_t* tr) {
   const int op = (int)t.op, l = (int)t.layer;
@@ -572,10 +572,10 @@ __device__ __forceinline__ bool task_gemv(const KParams& P, const TaskRec& t, in
     else return base + (size_t)(u0 + U) * K;
   };
 
-  // pipeline state for one slice.  With four or more sequences the activations
-  // read from LDS for a chunk serve RPG rows (a group holds CG / RPG chunks of each
-  // of RPG rows): at one row per read the reads would outrun LDS bandwidth.
-  constexpr int RPG = NB >= 4 ? 2 : 1, CGE = CG / RPG;
+  // pipeline state for one slice.  With four sequences the activations read from LDS for a
+  // chunk serve RPG rows (a group holds CG / RPG chunks of each of RPG rows): at one row per
+  // read the reads would outrun LDS bandwidth.  RPG is chosen per operator (run_task).
+  constexpr int CGE = CG / RPG;
   const int my_groups = (my_rows + RPG - 1) / RPG;  // row groups (a last odd row is paired with itself)
   uint4 buf[DEPTH][CG];
   int ir = 0, ig = 0, cr = 0, cgi = 0;
@@ -2023,7 +2023,12 @@ __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int
     }
   }
   if constexpr (NB >= 8) return task_gemv_mfma<NB>(P, t, s, mega, lds, tr);
-  else return task_gemv<NB, LO>(P, t, s, mega, lds, tr);
+  else if constexpr (NB < 4) return task_gemv<NB, LO, 1>(P, t, s, mega, lds, tr);
+  // four sequences: each staged-activation read serves four rows where a wave's rows come in
+  // fours or the pairing wastes as much (down projection, QKV, LM head), two elsewhere (a wave
+  // holds two O-projection rows; fourteen gate/up rows would leave two slots of sixteen idle)
+  else if (t.op == OP_WO || t.op == OP_GU) return task_gemv<NB, LO, 2>(P, t, s, mega, lds, tr);
+  else return task_gemv<NB, LO, 4>(P, t, s, mega, lds, tr);
 }
 
 // The megakernel: one launch runs n_steps decode steps of the whole model.
