@@ -29,6 +29,13 @@ namespace mk {
 
 constexpr int NT = 512;  // threads per worker
 constexpr int NW = NT / 64;
+#ifndef MK_RPG1
+#define MK_RPG1 2
+#endif
+// rows per staged-activation read at one sequence at the O-projection, gate/up and down projection,
+// whose waves hold an even number of rows (QKV's three rows per wave would pay for a duplicate;
+// the LM head measured slower with two)
+constexpr int kRpg1 = MK_RPG1;
 #ifndef MK_GEMV_CG
 #define MK_GEMV_CG 4
 #endif
@@ -2023,7 +2030,10 @@ __device__ __forceinline__ bool run_task(const KParams& P, const TaskRec& t, int
     }
   }
   if constexpr (NB >= 8) return task_gemv_mfma<NB>(P, t, s, mega, lds, tr);
-  else if constexpr (NB < 4) return task_gemv<NB, LO, 1>(P, t, s, mega, lds, tr);
+  else if constexpr (NB == 1 && kRpg1 > 1) {
+    if (t.op == OP_WO || t.op == OP_GU || t.op == OP_DOWN) return task_gemv<NB, LO, kRpg1>(P, t, s, mega, lds, tr);
+    return task_gemv<NB, LO, 1>(P, t, s, mega, lds, tr);
+  } else if constexpr (NB < 4) return task_gemv<NB, LO, 1>(P, t, s, mega, lds, tr);
   // four sequences: each staged-activation read serves four rows where a wave's rows come in
   // fours or the pairing wastes as much (down projection, QKV, LM head), two elsewhere (a wave
   // holds two O-projection rows; fourteen gate/up rows would leave two slots of sixteen idle)
